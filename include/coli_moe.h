@@ -1,0 +1,204 @@
+/*
+ * coli_moe.h -- C ABI of libcoli_moe.so: one Mixture-of-Experts FFN layer
+ * with int4 (group size 64) routed experts, on AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows the per-token path the Colibri pages describe -- route,
+ * union, then expert compute -- for experts that are already resident in
+ * device memory (placement and streaming are outside this library):
+ *   [Start]  Colibri getting-started page (cti.vibequant.cc), section
+ *            "토큰당 처리 경로 (The Per-Token Path)": Route picks the experts,
+ *            Union de-duplicates experts shared by tokens of a batch, Place
+ *            changes only speed, never router decisions or precision.
+ *   [Guide]  "Colibri 完全ガイド — 25GB のメモリで 744B パラメータの大規模モデルを
+ *            動かす" (dashen-tech.com): table "コア技術のハイライト" (DeepSeek-V3
+ *            sigmoid router with shared experts; int8 and packed-int4 integer
+ *            dot kernels) and walk-through "詳細解説" step 3 (single-token
+ *            decode in f32, batched prefill on the integer kernel).
+ *   [Skill]  "Colibri" (mcpfield.com), section "コアアーキテクチャ" item 1.
+ *   [Heart]  "colibri解説｜GLM-5.2（744B MoE）を25GB RAMで動かす純Cランタイムの
+ *            実測速度" (ai-heartland.com), section "なぜ25GBで動くのか" (top-8
+ *            experts per MoE layer, ~19 MB int4 experts).
+ *   [Hysen]  "colibri: 744B MoEをストレージから推論するCエンジン"
+ *            (hysenlabs.com), sections "トークンごとの5ステップパス..." and
+ *            "エンドツーエンドの測定で地位を獲得する技術" (batched expert union;
+ *            the default policy never silently changes precision or router
+ *            semantics).
+ *
+ * Conventions for every entry point
+ *  - Memory: every tensor pointer is DEVICE memory owned by the caller; the
+ *    library never allocates or frees device memory, keeps no state between
+ *    calls and never synchronises.  Work is enqueued on `hip_stream` (a
+ *    hipStream_t; NULL = the null stream) and buffers must stay valid until
+ *    the caller synchronises that stream.  The layer descriptor itself is
+ *    host memory and may be reused or freed when the call returns.
+ *  - Layouts are row-major.  int4 codes are two's complement in [-8, 7];
+ *    byte b of a packed row holds element 2b in its low nibble and element
+ *    2b+1 in its high nibble.  Scales are IEEE fp16 bit patterns, one per
+ *    row per 64-wide group along the reduction axis.
+ *  - Alignment: every tensor pointer must be 16-byte aligned.
+ *  - Errors: argument, shape and alignment checks run on the host before any
+ *    HIP call and return a nonzero COLI_E_* code (nothing is enqueued then).
+ *    A failed launch returns COLI_E_DEVICE.  Faults inside kernels surface
+ *    at the caller's next synchronisation.  Non-finite inputs give
+ *    unspecified (but memory-safe) results.  No C++ exception crosses the ABI.
+ *  - Threading: calls are thread-safe; concurrent calls must use distinct
+ *    output and workspace buffers.
+ *  - Determinism: for a given input every result is bitwise reproducible
+ *    from run to run (no floating-point atomics), and a token's results do
+ *    not depend on the other tokens of the batch within one arithmetic
+ *    family (act_mode).
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COLI_MOE_ABI_VERSION 1
+
+enum coli_status {
+    COLI_OK = 0,
+    COLI_E_ARG = 1,         /* NULL pointer or invalid scalar argument        */
+    COLI_E_SHAPE = 2,       /* H, I, E, k, T, n_shared outside the limits     */
+    COLI_E_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned        */
+    COLI_E_WORKSPACE = 4,   /* workspace smaller than coli_moe_workspace_bytes */
+    COLI_E_DEVICE = 5,      /* a HIP call or kernel launch failed             */
+    COLI_E_UNSUPPORTED = 6  /* current device is not gfx950, or unknown mode  */
+};
+
+/* Arithmetic family of the expert matmuls ([Guide] "詳細解説" step 3; the
+ * pages' IDOT switch made an explicit argument, so batching never changes
+ * the function silently -- [Hysen] "エンドツーエンドの測定で...").        */
+enum coli_act_mode {
+    COLI_ACT_F32 = 0, /* fp32 activations x dequantised int4 weights       */
+    COLI_ACT_I8 = 1   /* int8 per-token gs64 activations x int4 weights,
+                         exact int32 group accumulators, fp32 scaling     */
+};
+
+/* Shape limits checked by every entry point. */
+#define COLI_MAX_H 8192     /* H % 64 == 0, 64 <= H <= COLI_MAX_H          */
+#define COLI_MAX_I 8192     /* I % 64 == 0, 64 <= I <= COLI_MAX_I          */
+#define COLI_MAX_E 1024     /* 1 <= E <= COLI_MAX_E                        */
+#define COLI_MAX_K 16       /* 1 <= k <= min(E, COLI_MAX_K)                */
+#define COLI_MAX_T 65536    /* 0 <= T <= COLI_MAX_T                        */
+
+/* One MoE layer resident in device memory (descriptor in host memory). */
+typedef struct coli_moe_layer {
+    int32_t H;             /* hidden size                                   */
+    int32_t I;             /* expert intermediate size                     */
+    int32_t E;             /* routed experts                                */
+    int32_t k;             /* experts selected per token                    */
+    int32_t n_shared;      /* 0 or 1 shared expert of the same shape        */
+    const float *router_w;     /* [E][H] fp32                               */
+    const float *router_bias;  /* [E] fp32, used for selection only         */
+    const uint8_t *w13;        /* [E][2I][H/2] int4; rows [0,I) gate,
+                                  rows [I,2I) up                            */
+    const uint16_t *s13;       /* [E][2I][H/64] fp16 scales                 */
+    const uint8_t *w2;         /* [E][H][I/2] int4 down projection          */
+    const uint16_t *s2;        /* [E][H][I/64] fp16 scales                  */
+    const uint8_t *sh_w13;     /* shared expert [2I][H/2]; NULL iff n_shared==0 */
+    const uint16_t *sh_s13;    /* [2I][H/64]                                */
+    const uint8_t *sh_w2;      /* [H][I/2]                                  */
+    const uint16_t *sh_s2;     /* [H][I/64]                                 */
+} coli_moe_layer;
+
+/* Bytes of device workspace needed by coli_moe_route, coli_moe_union and
+ * coli_moe_forward for this shape and arithmetic family (one buffer of this
+ * size serves all three calls on one stream; its contents are scratch).
+ * Returns 0 for an invalid shape or mode. */
+size_t coli_moe_workspace_bytes(int32_t H, int32_t I, int32_t E, int32_t k, int32_t T,
+                                int32_t act_mode);
+
+/* Route ([Skill] "コアアーキテクチャ" item 1, [Guide] "コア技術のハイライト":
+ * a DeepSeek-V3 style sigmoid router; [Heart] "なぜ25GBで動くのか": top-8).
+ * For each token t of x [T][H] fp32:
+ *   l[e]  = fp32( sum_h x[t][h] * router_w[e][h] ), accumulated in fp64,
+ *   s[e]  = fp32( 1 / (1 + exp(-l[e])) ) evaluated in fp64,
+ *   key[e] = s[e] + router_bias[e]  (fp32),
+ *   topk_ids[t][0..k) = the k largest keys, largest first, equal keys
+ *                       ordered by lower expert index,
+ *   topk_w[t][j] = s[topk_ids[t][j]] / sum_j' s[topk_ids[t][j']]  (fp32).
+ * topk_ids [T][k] int32, topk_w [T][k] fp32 are written.  T == 0 is a no-op. */
+int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *topk_ids,
+                   float *topk_w, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Union ([Start] "토큰당 처리 경로": batch-union of the experts chosen by
+ * several tokens; [Hysen] "エンドツーエンドの測定で...": batched expert union).
+ * From topk_ids [T][k] (each row holds distinct ids in [0, E)):
+ *   n_union[0]     = U, the number of distinct experts,
+ *   union_ids[u]   = the distinct experts in ascending order (u < U),
+ *   offsets[u]     = first position in slots of expert union_ids[u],
+ *                    offsets[U] = T*k,
+ *   slots[p]       = slot index t*k + j, grouped by expert in union order,
+ *                    ascending within an expert.
+ * Capacities: union_ids [min(E, T*k)], offsets [min(E, T*k) + 1],
+ * slots [T*k].  Entries past U are set to -1 (union_ids) and T*k (offsets).
+ * All results stay on the device.  Out-of-range ids give unspecified
+ * (memory-safe) results. */
+int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
+                   int32_t *offsets, int32_t *slots, int32_t *n_union, void *hip_stream);
+
+/* Forward: expert compute and combine for the routed batch
+ * ([Guide] "詳細解説" step 3; [Start] "토큰당 처리 경로").
+ * For every union expert e and each of its slots (t, j), and for the shared
+ * expert with every token (weight 1, ungated):
+ *   g, u = x[t] . W13_e^T    (gate rows, up rows)
+ *   h    = g / (1 + exp(-g)) * u                        (SwiGLU, fp32)
+ *   o    = h . W2_e^T
+ *   y[t] = sum_j topk_w[t][j] * o_(t,j) + o_shared(t)   (j ascending)
+ * act_mode COLI_ACT_F32: dot products of fp32 x / h with the dequantised
+ *   weights (code * scale), fp32 accumulation.
+ * act_mode COLI_ACT_I8: x and h quantised per token per 64-group to int8
+ *   (scale = amax / 127, q = clamp(rint(v / scale), -127, 127), amax == 0
+ *   gives scale 0), exact int32 accumulators per 64-group, output
+ *   sum_g acc * act_scale * weight_scale in fp32.
+ * Inputs are the outputs of coli_moe_route and coli_moe_union for the same
+ * x and T; y [T][H] fp32 is written.
+ * acc_dump (COLI_ACT_I8 only; NULL in production) receives, for every row r
+ * in [0, R), R = T*k + n_shared*T (r < T*k: slot r; else shared token
+ * r - T*k), in this order:
+ *   int32  acc13 [R][2I][H/64]   gate/up group accumulators,
+ *   int32  acc2  [R][H][I/64]    down group accumulators,
+ *   int8   qh    [R][I]          int8 codes of h (natural element order),
+ *   fp32   sh    [R][I/64]       their scales,
+ * each region starting at a 256-byte aligned offset; coli_moe_acc_dump_bytes
+ * gives the total size. */
+int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
+                     const int32_t *topk_ids, const float *topk_w, const int32_t *union_ids,
+                     const int32_t *offsets, const int32_t *slots, const int32_t *n_union,
+                     int32_t act_mode, float *y, void *workspace, size_t workspace_bytes,
+                     int32_t *acc_dump, void *hip_stream);
+
+/* Size in bytes of the acc_dump buffer of coli_moe_forward (0 if invalid). */
+size_t coli_moe_acc_dump_bytes(int32_t H, int32_t I, int32_t k, int32_t T, int32_t n_shared);
+
+/* Human-readable name of a status code (static string). */
+const char *coli_moe_strerror(int status);
+
+/* COLI_MOE_ABI_VERSION of the loaded library. */
+int coli_moe_abi_version(void);
+
+/* COLI_OK when the current HIP device is a gfx950, else COLI_E_UNSUPPORTED
+ * (or COLI_E_DEVICE when no device can be queried). */
+int coli_moe_device_check(void);
+
+/* ---- Glue for stacking layers (outside the MoE layer itself) ------------
+ * The pages do not describe the blocks around the MoE layer.  To run a
+ * stack of synthetic layers without overflow, a unit-gain RMS pre-norm and
+ * a residual add are provided (the reading of a GLM-style pre-norm block). */
+
+/* xhat[t][h] = x[t][h] / sqrt(mean_h(x[t][h]^2) + eps), fp32, [T][H]. */
+int coli_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
+                 void *hip_stream);
+
+/* x[i] += y[i] for i < n (fp32). */
+int coli_add_inplace(float *x, const float *y, int64_t n, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COLI_MOE_H */

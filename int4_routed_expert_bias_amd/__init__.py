@@ -1,0 +1,232 @@
+"""Python binding of libcoli_moe.so -- the int4 routed-expert MoE layer on
+MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and streams.  The functions carry
+the C ABI names (include/coli_moe.h) without the ``coli_moe_`` prefix and
+raise ``ColiError`` on a nonzero status.  If the library is not built, the
+import of ``lib()`` fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcoli_moe.so")
+
+ACT_F32, ACT_I8 = 0, 1
+COLI_OK, COLI_E_ARG, COLI_E_SHAPE, COLI_E_ALIGN, COLI_E_WORKSPACE, COLI_E_DEVICE, \
+    COLI_E_UNSUPPORTED = range(7)
+
+# every symbol declared in include/coli_moe.h
+EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
+           "coli_moe_union", "coli_moe_forward", "coli_moe_acc_dump_bytes",
+           "coli_moe_strerror", "coli_moe_device_check", "coli_rmsnorm", "coli_add_inplace")
+
+
+class ColiError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class ColiLayer(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32)] + [
+        (n, ctypes.c_void_p) for n in ("router_w", "router_bias", "w13", "s13", "w2", "s2",
+                                       "sh_w13", "sh_s13", "sh_w2", "sh_s2")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcoli_moe.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sig = {
+            "coli_moe_abi_version": ([], ctypes.c_int),
+            "coli_moe_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
+            "coli_moe_route": ([vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "coli_moe_union": ([vp, i32, i32, i32, vp, vp, vp, vp, vp], ctypes.c_int),
+            "coli_moe_forward": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp, vp],
+                                 ctypes.c_int),
+            "coli_moe_acc_dump_bytes": ([i32, i32, i32, i32, i32], sz),
+            "coli_moe_strerror": ([ctypes.c_int], ctypes.c_char_p),
+            "coli_moe_device_check": ([], ctypes.c_int),
+            "coli_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
+            "coli_add_inplace": ([vp, vp, i64, vp], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().coli_moe_strerror(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != COLI_OK:
+        raise ColiError(status, f"{what}: {strerror(status)}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def workspace_bytes(H, I, E, k, T, act_mode) -> int:
+    return lib().coli_moe_workspace_bytes(H, I, E, k, T, act_mode)
+
+
+def acc_dump_bytes(H, I, k, T, n_shared) -> int:
+    return lib().coli_moe_acc_dump_bytes(H, I, k, T, n_shared)
+
+
+def device_check() -> int:
+    return lib().coli_moe_device_check()
+
+
+def route(layer, x, T, ids, w, workspace, workspace_nbytes=None, stream=None):
+    nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    _check(lib().coli_moe_route(layer.ref, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(workspace), nb,
+                                _stream(stream)), "coli_moe_route")
+
+
+def union(ids, T, k, E, union_ids, offsets, slots, n_union, stream=None):
+    _check(lib().coli_moe_union(_ptr(ids), T, k, E, _ptr(union_ids), _ptr(offsets), _ptr(slots),
+                                _ptr(n_union), _stream(stream)), "coli_moe_union")
+
+
+def forward(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y, workspace,
+            workspace_nbytes=None, acc_dump=None, stream=None):
+    nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    _check(lib().coli_moe_forward(layer.ref, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(union_ids),
+                                  _ptr(offsets), _ptr(slots), _ptr(n_union), act_mode, _ptr(y),
+                                  _ptr(workspace), nb, _ptr(acc_dump), _stream(stream)),
+           "coli_moe_forward")
+
+
+def rmsnorm(x, xhat, T, H, eps=1e-6, stream=None):
+    _check(lib().coli_rmsnorm(_ptr(x), _ptr(xhat), T, H, eps, _stream(stream)), "coli_rmsnorm")
+
+
+def add_inplace(x, y, n, stream=None):
+    _check(lib().coli_add_inplace(_ptr(x), _ptr(y), n, _stream(stream)), "coli_add_inplace")
+
+
+class DeviceLayer:
+    """One layer's tensors in device memory plus the C descriptor.
+
+    ``arrays`` uses the synthetic-layer layout (router_w, router_b, w13, s13,
+    w2, s2 and optionally sh_*), as numpy arrays or torch tensors."""
+
+    def __init__(self, arrays: dict, k: int, n_shared: int = 1, device="cuda"):
+        import numpy as np
+        import torch
+
+        def dev(a):
+            if isinstance(a, np.ndarray):
+                if a.dtype == np.uint16:
+                    a = a.view(np.int16)
+                a = torch.from_numpy(np.ascontiguousarray(a))
+            return a.to(device, non_blocking=False).contiguous()
+
+        self.H, self.I, self.E, self.k, self.n_shared = (int(arrays["H"]), int(arrays["I"]),
+                                                        int(arrays["E"]), k, n_shared)
+        self.t = {}
+        for n in ("router_w", "router_b", "w13", "s13", "w2", "s2"):
+            self.t[n] = dev(arrays[n])
+        if n_shared:
+            for n in ("sh_w13", "sh_s13", "sh_w2", "sh_s2"):
+                self.t[n] = dev(arrays[n])
+        s = ColiLayer(self.H, self.I, self.E, k, n_shared)
+        s.router_w = _ptr(self.t["router_w"])
+        s.router_bias = _ptr(self.t["router_b"])
+        for n in ("w13", "s13", "w2", "s2"):
+            setattr(s, n, _ptr(self.t[n]))
+        if n_shared:
+            for n in ("sh_w13", "sh_s13", "sh_w2", "sh_s2"):
+                setattr(s, n, _ptr(self.t[n]))
+        self.struct = s
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+class Buffers:
+    """Device buffers of one (layer shape, T, act_mode) call sequence."""
+
+    def __init__(self, layer: DeviceLayer, T: int, act_mode: int, device="cuda", dump=False):
+        import torch
+        H, I, E, k = layer.H, layer.I, layer.E, layer.k
+        self.T, self.act_mode = T, act_mode
+        cap = max(1, min(E, T * k))
+        i32, f32 = torch.int32, torch.float32
+        self.ids = torch.empty((max(T, 1), k), dtype=i32, device=device)
+        self.w = torch.empty((max(T, 1), k), dtype=f32, device=device)
+        self.union_ids = torch.empty((cap,), dtype=i32, device=device)
+        self.offsets = torch.empty((cap + 1,), dtype=i32, device=device)
+        self.slots = torch.empty((max(1, T * k),), dtype=i32, device=device)
+        self.n_union = torch.zeros((4,), dtype=i32, device=device)
+        self.y = torch.empty((max(T, 1), H), dtype=f32, device=device)
+        nb = workspace_bytes(H, I, E, k, T, act_mode)
+        self.workspace = torch.empty((max(nb, 256),), dtype=torch.uint8, device=device)
+        self.dump = None
+        if dump:
+            db = acc_dump_bytes(H, I, k, T, layer.n_shared)
+            self.dump = torch.empty((max(db, 256),), dtype=torch.uint8, device=device)
+
+
+def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None):
+    """route -> union -> forward for x [T][H] (device fp32)."""
+    T = bufs.T
+    route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+    union(bufs.ids, T, layer.k, layer.E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union,
+          stream=stream)
+    forward(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,
+            bufs.n_union, bufs.act_mode, bufs.y, bufs.workspace, acc_dump=bufs.dump,
+            stream=stream)
+    return bufs.y
+
+
+def dump_views(dump_host, H, I, k, T, n_shared):
+    """Split a host copy (numpy uint8) of the acc_dump buffer into its
+    documented regions: acc13 [R][2I][H/64], acc2 [R][H][I/64], qh [R][I],
+    sh [R][I/64]."""
+    import numpy as np
+    R = T * k + n_shared * T
+    a256 = lambda v: (v + 255) & ~255
+    off = 0
+    n13 = R * 2 * I * (H // 64) * 4
+    acc13 = dump_host[off:off + n13].view(np.int32).reshape(R, 2 * I, H // 64)
+    off = a256(off + n13)
+    n2 = R * H * (I // 64) * 4
+    acc2 = dump_host[off:off + n2].view(np.int32).reshape(R, H, I // 64)
+    off = a256(off + n2)
+    qh = dump_host[off:off + R * I].view(np.int8).reshape(R, I)
+    off = a256(off + R * I)
+    sh = dump_host[off:off + R * (I // 64) * 4].view(np.float32).reshape(R, I // 64)
+    return dict(acc13=acc13, acc2=acc2, qh=qh, sh=sh)

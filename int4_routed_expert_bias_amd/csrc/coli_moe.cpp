@@ -1,0 +1,204 @@
+// coli_moe.cpp -- host entry points of libcoli_moe.so (C ABI declared in
+// include/coli_moe.h).  Every argument, shape and alignment check runs on
+// the host before the first HIP call; kernels are enqueued on the caller's
+// stream; nothing is allocated, freed or synchronised here.
+#include "../../include/coli_moe.h"
+
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "common.h"
+
+using namespace coli;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(int32_t H, int32_t I, int32_t E, int32_t k, int32_t T)
+{
+    if (H < 64 || H > COLI_MAX_H || H % 64) return COLI_E_SHAPE;
+    if (I < 64 || I > COLI_MAX_I || I % 64) return COLI_E_SHAPE;
+    if (E < 1 || E > COLI_MAX_E) return COLI_E_SHAPE;
+    if (k < 1 || k > COLI_MAX_K || k > E) return COLI_E_SHAPE;
+    if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    return COLI_OK;
+}
+
+int check_layer(const coli_moe_layer *L, bool need_experts)
+{
+    if (!L) return COLI_E_ARG;
+    if (L->n_shared != 0 && L->n_shared != 1) return COLI_E_SHAPE;
+    if (int st = check_dims(L->H, L->I, L->E, L->k, 0)) return st;
+    if (!L->router_w || !L->router_bias) return COLI_E_ARG;
+    if (!aligned16(L->router_w) || !aligned16(L->router_bias)) return COLI_E_ALIGN;
+    if (need_experts) {
+        if (!L->w13 || !L->s13 || !L->w2 || !L->s2) return COLI_E_ARG;
+        if (!aligned16(L->w13) || !aligned16(L->s13) || !aligned16(L->w2) || !aligned16(L->s2))
+            return COLI_E_ALIGN;
+        const bool any_sh = L->sh_w13 || L->sh_s13 || L->sh_w2 || L->sh_s2;
+        const bool all_sh = L->sh_w13 && L->sh_s13 && L->sh_w2 && L->sh_s2;
+        if (L->n_shared ? !all_sh : any_sh) return COLI_E_ARG;
+        if (L->n_shared && (!aligned16(L->sh_w13) || !aligned16(L->sh_s13) ||
+                            !aligned16(L->sh_w2) || !aligned16(L->sh_s2)))
+            return COLI_E_ALIGN;
+    }
+    return COLI_OK;
+}
+
+std::atomic<int> g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+int device_check()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return COLI_E_DEVICE;
+    if (dev < 0 || dev >= 64) return COLI_E_DEVICE;
+    int s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return COLI_E_DEVICE;
+        s = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_state[dev].store(s, std::memory_order_relaxed);
+    }
+    return s == 1 ? COLI_OK : COLI_E_UNSUPPORTED;
+}
+
+LayerDev to_dev(const coli_moe_layer *L)
+{
+    LayerDev d;
+    d.H = L->H; d.I = L->I; d.E = L->E; d.k = L->k; d.n_shared = L->n_shared;
+    d.router_w = L->router_w; d.router_bias = L->router_bias;
+    d.w13 = L->w13; d.s13 = L->s13; d.w2 = L->w2; d.s2 = L->s2;
+    d.sh_w13 = L->sh_w13; d.sh_s13 = L->sh_s13; d.sh_w2 = L->sh_w2; d.sh_s2 = L->sh_s2;
+    return d;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_E_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int coli_moe_abi_version(void) { return COLI_MOE_ABI_VERSION; }
+
+size_t coli_moe_workspace_bytes(int32_t H, int32_t I, int32_t E, int32_t k, int32_t T,
+                                int32_t act_mode)
+{
+    if (check_dims(H, I, E, k, T) != COLI_OK) return 0;
+    if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return 0;
+    return workspace_layout(H, I, E, k, T, act_mode, 1).total;
+}
+
+size_t coli_moe_acc_dump_bytes(int32_t H, int32_t I, int32_t k, int32_t T, int32_t n_shared)
+{
+    if (check_dims(H, I, k, k, T) != COLI_OK) return 0;
+    if (n_shared != 0 && n_shared != 1) return 0;
+    return dump_layout(H, I, k, T, n_shared).total;
+}
+
+const char *coli_moe_strerror(int status)
+{
+    switch (status) {
+    case COLI_OK: return "COLI_OK";
+    case COLI_E_ARG: return "COLI_E_ARG: null pointer or invalid argument";
+    case COLI_E_SHAPE: return "COLI_E_SHAPE: shape outside the supported limits";
+    case COLI_E_ALIGN: return "COLI_E_ALIGN: tensor pointer not 16-byte aligned";
+    case COLI_E_WORKSPACE: return "COLI_E_WORKSPACE: workspace too small";
+    case COLI_E_DEVICE: return "COLI_E_DEVICE: HIP call or kernel launch failed";
+    case COLI_E_UNSUPPORTED: return "COLI_E_UNSUPPORTED: device is not gfx950 or mode unknown";
+    default: return "unknown coli status";
+    }
+}
+
+int coli_moe_device_check(void) { return device_check(); }
+
+int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *topk_ids,
+                   float *topk_w, void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    if (int st = check_layer(L, false)) return st;
+    if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    if (T == 0) return COLI_OK;
+    if (!x || !topk_ids || !topk_w || !workspace) return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(workspace))
+        return COLI_E_ALIGN;
+    const Workspace lay = workspace_layout(L->H, L->I, L->E, L->k, T, COLI_ACT_F32, L->n_shared);
+    if (workspace_bytes < lay.route_end) return COLI_E_WORKSPACE;
+    if (int st = device_check()) return st;
+    RouteIO io{x, T, topk_ids, topk_w,
+               reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + lay.logits)};
+    return status_of(launch_route(to_dev(L), io, static_cast<hipStream_t>(hip_stream)));
+}
+
+int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
+                   int32_t *offsets, int32_t *slots, int32_t *n_union, void *hip_stream)
+{
+    if (E < 1 || E > COLI_MAX_E) return COLI_E_SHAPE;
+    if (k < 1 || k > COLI_MAX_K || k > E) return COLI_E_SHAPE;
+    if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    if (!n_union || !union_ids || !offsets) return COLI_E_ARG;
+    if (T > 0 && (!topk_ids || !slots)) return COLI_E_ARG;
+    if (!aligned16(union_ids) || !aligned16(offsets) || !aligned16(n_union) ||
+        (T > 0 && (!aligned16(topk_ids) || !aligned16(slots))))
+        return COLI_E_ALIGN;
+    if (int st = device_check()) return st;
+    return status_of(launch_union(topk_ids, T, k, E, union_ids, offsets, slots, n_union,
+                                  static_cast<hipStream_t>(hip_stream)));
+}
+
+int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
+                     const int32_t *topk_ids, const float *topk_w, const int32_t *union_ids,
+                     const int32_t *offsets, const int32_t *slots, const int32_t *n_union,
+                     int32_t act_mode, float *y, void *workspace, size_t workspace_bytes,
+                     int32_t *acc_dump, void *hip_stream)
+{
+    if (int st = check_layer(L, true)) return st;
+    if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return COLI_E_UNSUPPORTED;
+    if (acc_dump && act_mode != COLI_ACT_I8) return COLI_E_ARG;
+    if (T == 0) return COLI_OK;
+    if (!x || !topk_ids || !topk_w || !union_ids || !offsets || !slots || !n_union || !y ||
+        !workspace)
+        return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(union_ids) ||
+        !aligned16(offsets) || !aligned16(slots) || !aligned16(n_union) || !aligned16(y) ||
+        !aligned16(workspace) || (acc_dump && !aligned16(acc_dump)))
+        return COLI_E_ALIGN;
+    const Workspace lay = workspace_layout(L->H, L->I, L->E, L->k, T, act_mode, L->n_shared);
+    if (workspace_bytes < lay.forward_end) return COLI_E_WORKSPACE;
+    if (int st = device_check()) return st;
+    ForwardIO io{};
+    io.x = x; io.T = T; io.ids = topk_ids; io.w = topk_w;
+    io.union_ids = union_ids; io.offsets = offsets; io.slots = slots; io.n_union = n_union;
+    io.y = y; io.ws = static_cast<uint8_t *>(workspace); io.lay = lay;
+    io.acc_dump = acc_dump;
+    io.dump = dump_layout(L->H, L->I, L->k, T, L->n_shared);
+    const LayerDev d = to_dev(L);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    return status_of(act_mode == COLI_ACT_I8 ? launch_forward_i8(d, io, st)
+                                             : launch_forward_f32(d, io, st));
+}
+
+int coli_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps, void *hip_stream)
+{
+    if (T < 0 || T > COLI_MAX_T || H < 64 || H > COLI_MAX_H || H % 64) return COLI_E_SHAPE;
+    if (!(eps >= 0.0f)) return COLI_E_ARG;
+    if (T == 0) return COLI_OK;
+    if (!x || !xhat) return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(xhat)) return COLI_E_ALIGN;
+    if (int st = device_check()) return st;
+    return status_of(launch_rmsnorm(x, xhat, T, H, eps, static_cast<hipStream_t>(hip_stream)));
+}
+
+int coli_add_inplace(float *x, const float *y, int64_t n, void *hip_stream)
+{
+    if (n < 0) return COLI_E_ARG;
+    if (n == 0) return COLI_OK;
+    if (!x || !y) return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(y)) return COLI_E_ALIGN;
+    if (int st = device_check()) return st;
+    return status_of(launch_add(x, y, n, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// common.h -- internal helpers of libcoli_moe.so (device utilities, the
+// workspace layout and the launcher interface between the host entry points
+// and the kernel translation units).  Written for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace coli {
+
+constexpr int kWave = 64;
+#define COLI_MAX_K_DEV 16    // must equal COLI_MAX_K of the public header
+#define COLI_MAX_E_DEV 1024  // must equal COLI_MAX_E of the public header
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+// IEEE binary16 bit pattern -> fp32 (exact; one v_cvt_f32_f16).
+__device__ __forceinline__ float f16_to_f32(uint16_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    // fixed butterfly over lane bits 5..0: same tree for every value
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Position of element kk (within a row) in the permuted int8 activation
+// layout used by the integer kernels: inside every 8-element block the
+// order is [0,2,4,6,1,3,5,7], matching how a packed int4 dword splits into
+// its even-element and odd-element bytes.
+__device__ __forceinline__ int perm8_pos(int kk)
+{
+    int b = kk & 7;
+    return (kk & ~7) | ((b & 1) << 2) | (b >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout (offsets in bytes, each region 256-byte aligned)
+
+struct Workspace {
+    size_t logits;   // route: [T][E] f32
+    size_t route_end;
+    // forward, shared by both families
+    size_t o;        // [R][H] f32 expert outputs per slot / shared row
+    // fp32 family
+    size_t h;        // [R][I] f32 SwiGLU outputs
+    // int8 family
+    size_t qx, sx;   // [T][H] i8 (permuted), [T][H/64] f32
+    size_t qh, sh;   // [R][I] i8 (permuted), [R][I/64] f32
+    size_t tiles;    // [max_tiles] int2 (entry, first row) + [1] count
+    size_t forward_end;
+    size_t total;
+    int64_t R;       // rows: T*k + n_shared*T
+    int64_t cap;     // min(E, T*k)
+    int64_t max_tiles;
+};
+
+constexpr int kTileM = 16;  // token rows per integer-GEMM tile
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, int64_t T,
+                                  int act_mode, int64_t n_shared)
+{
+    Workspace w{};
+    w.R = T * k + n_shared * T;
+    w.cap = (T * k < E) ? T * k : E;
+    w.max_tiles = (T * k + kTileM - 1) / kTileM + w.cap + n_shared * ((T + kTileM - 1) / kTileM);
+    size_t p = 0;
+    w.logits = p; p = align256(p + (size_t)T * E * 4);
+    w.route_end = p;
+    p = 0;  // forward buffers alias the route scratch (stream-ordered)
+    w.o = p; p = align256(p + (size_t)w.R * H * 4);
+    if (act_mode == 0) {
+        w.h = p; p = align256(p + (size_t)w.R * I * 4);
+    } else {
+        w.qx = p; p = align256(p + (size_t)T * H);
+        w.sx = p; p = align256(p + (size_t)T * (H / 64) * 4);
+        w.qh = p; p = align256(p + (size_t)w.R * I);
+        w.sh = p; p = align256(p + (size_t)w.R * (I / 64) * 4);
+        w.tiles = p; p = align256(p + (size_t)(w.max_tiles + 1) * 8);
+    }
+    w.forward_end = p;
+    w.total = w.route_end > w.forward_end ? w.route_end : w.forward_end;
+    if (w.total == 0) w.total = 256;
+    return w;
+}
+
+// acc_dump regions (see coli_moe.h)
+struct DumpLayout {
+    size_t acc13, acc2, qh, sh, total;
+};
+
+inline DumpLayout dump_layout(int64_t H, int64_t I, int64_t k, int64_t T, int64_t n_shared)
+{
+    DumpLayout d{};
+    int64_t R = T * k + n_shared * T;
+    size_t p = 0;
+    d.acc13 = p; p = align256(p + (size_t)R * 2 * I * (H / 64) * 4);
+    d.acc2 = p;  p = align256(p + (size_t)R * H * (I / 64) * 4);
+    d.qh = p;    p = align256(p + (size_t)R * I);
+    d.sh = p;    p = align256(p + (size_t)R * (I / 64) * 4);
+    d.total = p;
+    return d;
+}
+
+// ---------------------------------------------------------------------------
+// launcher interface (each returns hipError_t of the launch)
+
+struct LayerDev {
+    int32_t H, I, E, k, n_shared;
+    const float *router_w, *router_bias;
+    const uint8_t *w13; const uint16_t *s13;
+    const uint8_t *w2; const uint16_t *s2;
+    const uint8_t *sh_w13; const uint16_t *sh_s13;
+    const uint8_t *sh_w2; const uint16_t *sh_s2;
+};
+
+struct RouteIO {
+    const float *x; int32_t T;
+    int32_t *ids; float *w;
+    float *logits;  // workspace
+};
+
+hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st);
+
+hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
+                        int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st);
+
+struct ForwardIO {
+    const float *x; int32_t T;
+    const int32_t *ids; const float *w;
+    const int32_t *union_ids, *offsets, *slots, *n_union;
+    float *y;
+    uint8_t *ws; Workspace lay;
+    int32_t *acc_dump; DumpLayout dump;
+};
+
+hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st);
+hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st);
+hipError_t launch_combine(const float *o, const float *w, int32_t T, int32_t k, int32_t H,
+                          int32_t n_shared, float *y, hipStream_t st);
+hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
+                          hipStream_t st);
+hipError_t launch_add(float *x, const float *y, int64_t n, hipStream_t st);
+
+}  // namespace coli

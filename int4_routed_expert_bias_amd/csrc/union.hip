@@ -1,0 +1,128 @@
+// union.hip -- batch-union of the routed experts (Colibri getting-started
+// page, section "토큰당 처리 경로": experts picked by several tokens of the
+// batch are de-duplicated and computed once).
+//
+// One workgroup of 8 waves.  Wave w owns a contiguous range of slots.
+//   1. per-wave expert histograms in LDS (integer atomics: order-free),
+//   2. a block scan gives each expert its start and its union position, and
+//      each wave its private cursor per expert (start + counts of the
+//      waves before it),
+//   3. each wave walks its range in order, 64 slots at a time; lanes holding
+//      the same expert are grouped with a ballot match loop, ranked by lane
+//      order and scattered at the wave's cursor.
+// The result is the stable order (ascending slot) and is deterministic.
+#include "common.h"
+
+namespace coli {
+
+constexpr int kUnionWaves = 8;
+constexpr int kUnionThreads = kUnionWaves * 64;
+
+__device__ void block_exclusive_scan(int32_t *a, int n, int32_t *tmp)
+{
+    // Hillis-Steele inclusive scan over n <= 2 * blockDim entries, then shift.
+    for (int i = threadIdx.x; i < n; i += blockDim.x) tmp[i] = a[i];
+    __syncthreads();
+    for (int off = 1; off < n; off <<= 1) {
+        int32_t v[2];
+        int c = 0;
+        for (int i = threadIdx.x; i < n; i += blockDim.x, ++c) v[c] = (i >= off) ? tmp[i - off] : 0;
+        __syncthreads();
+        c = 0;
+        for (int i = threadIdx.x; i < n; i += blockDim.x, ++c) tmp[i] += v[c];
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < n; i += blockDim.x) a[i] = (i == 0) ? 0 : tmp[i - 1];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__restrict__ ids,
+                                                              int n, int E, int cap,
+                                                              int32_t *__restrict__ union_ids,
+                                                              int32_t *__restrict__ offsets,
+                                                              int32_t *__restrict__ slots,
+                                                              int32_t *__restrict__ n_union)
+{
+    extern __shared__ int32_t smem[];
+    volatile int32_t *cur = smem;                       // [kUnionWaves][E]
+    int32_t *start = smem + kUnionWaves * E;            // [E]
+    int32_t *upos = start + E;                          // [E]
+    int32_t *tmp = upos + E;                            // [E]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int i = tid; i < kUnionWaves * E; i += blockDim.x) cur[i] = 0;
+    __syncthreads();
+
+    const int per = ((n + kUnionWaves - 1) / kUnionWaves + 63) & ~63;
+    const int r0 = min(n, wave * per), r1 = min(n, r0 + per);
+    for (int s = r0 + lane; s < r1; s += 64) {
+        int id = ids[s];
+        if (id >= 0 && id < E) atomicAdd((int32_t *)&cur[wave * E + id], 1);
+    }
+    __syncthreads();
+
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t c = 0;
+        for (int w = 0; w < kUnionWaves; ++w) c += cur[w * E + e];
+        start[e] = c;
+        upos[e] = c > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    // counts -> flags are recovered below from the scanned starts
+    for (int e = tid; e < E; e += blockDim.x) tmp[e] = start[e];
+    __syncthreads();
+    // keep the counts in the first row of a scratch region before scanning
+    block_exclusive_scan(start, E, smem + kUnionWaves * E + 3 * E);
+    block_exclusive_scan(upos, E, smem + kUnionWaves * E + 4 * E);
+
+    int32_t U = upos[E - 1] + (tmp[E - 1] > 0 ? 1 : 0);
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t c = tmp[e];
+        if (c > 0) {
+            union_ids[upos[e]] = e;
+            offsets[upos[e]] = start[e];
+        }
+        int32_t base = start[e];
+        for (int w = 0; w < kUnionWaves; ++w) {
+            int32_t v = cur[w * E + e];
+            cur[w * E + e] = base;
+            base += v;
+        }
+    }
+    for (int u = U + tid; u < cap; u += blockDim.x) union_ids[u] = -1;
+    for (int u = U + tid; u <= cap; u += blockDim.x) offsets[u] = n;
+    if (tid == 0) n_union[0] = U;
+    __syncthreads();
+
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int b = r0; b < r1; b += 64) {
+        int s = b + lane;
+        int id = (s < r1) ? ids[s] : -1;
+        bool valid = id >= 0 && id < E;
+        uint64_t active = __ballot(valid);
+        while (active) {
+            int leader = __ffsll((unsigned long long)active) - 1;
+            int v = __shfl(id, leader, 64);
+            uint64_t m = __ballot(valid && id == v);
+            int32_t base = cur[wave * E + v];
+            if (valid && id == v) slots[base + __popcll(m & lt_mask)] = s;
+            __builtin_amdgcn_wave_barrier();
+            if (lane == leader) cur[wave * E + v] = base + __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+            active &= ~m;
+        }
+    }
+}
+
+hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
+                        int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st)
+{
+    const int n = T * k;
+    const int cap = n < E ? n : E;
+    const size_t lds = (size_t)(kUnionWaves + 5) * E * sizeof(int32_t);
+    hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), lds, st, ids, n, E, cap,
+                       union_ids, offsets, slots, n_union);
+    return hipGetLastError();
+}
+
+}  // namespace coli

@@ -1,0 +1,144 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every symbol the public header declares, and rejects bad arguments with the
+documented status codes before any HIP call.
+
+Every call here carries at least one invalid argument, so no call reaches
+the device (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_routed_expert_bias_amd as coli
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "coli_moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(coli.LIB_PATH):
+        from int4_routed_expert_bias_amd import build as b
+        b.build()
+    return coli.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(coli_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert set(names) == set(coli.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.coli_moe_abi_version() == 1
+
+
+def test_strerror(L):
+    for s in range(7):
+        assert coli.strerror(s).startswith("COLI_")
+    assert "unknown" in coli.strerror(99)
+
+
+def test_workspace_bytes(L):
+    assert coli.workspace_bytes(6144, 2048, 256, 8, 1, 0) > 0
+    assert coli.workspace_bytes(6144, 2048, 256, 8, 4096, 1) > 0
+    assert coli.workspace_bytes(6000, 2048, 256, 8, 1, 0) == 0      # H % 64
+    assert coli.workspace_bytes(6144, 2048, 256, 9, 1, 2) == 0      # mode
+    assert coli.workspace_bytes(6144, 2048, 4, 8, 1, 0) == 0        # k > E
+    assert coli.workspace_bytes(6144, 2048, 256, 17, 1, 0) == 0     # k > 16
+    assert coli.acc_dump_bytes(256, 128, 2, 4, 1) > 0
+    assert coli.acc_dump_bytes(256, 128, 2, 4, 2) == 0
+
+
+FAKE = 0x100000  # aligned, never dereferenced
+MIS = 0x100004   # 4-byte aligned only
+
+
+def layer(**kw):
+    d = dict(H=256, I=128, E=16, k=2, n_shared=1, router_w=FAKE, router_bias=FAKE, w13=FAKE,
+             s13=FAKE, w2=FAKE, s2=FAKE, sh_w13=FAKE, sh_s13=FAKE, sh_w2=FAKE, sh_s2=FAKE)
+    d.update(kw)
+    s = coli.ColiLayer(d["H"], d["I"], d["E"], d["k"], d["n_shared"])
+    for n in ("router_w", "router_bias", "w13", "s13", "w2", "s2", "sh_w13", "sh_s13",
+              "sh_w2", "sh_s2"):
+        setattr(s, n, d[n])
+    return s
+
+
+def route(L, lay, T=4, x=FAKE, ids=FAKE, w=FAKE, ws=FAKE, nb=1 << 20):
+    return L.coli_moe_route(ctypes.byref(lay) if lay is not None else None, x, T, ids, w, ws, nb,
+                            None)
+
+
+def forward(L, lay, T=4, mode=0, y=FAKE, ws=FAKE, nb=1 << 30, dump=None, **p):
+    a = dict(x=FAKE, ids=FAKE, w=FAKE, u=FAKE, off=FAKE, sl=FAKE, nu=FAKE)
+    a.update(p)
+    return L.coli_moe_forward(ctypes.byref(lay) if lay is not None else None, a["x"], T, a["ids"],
+                              a["w"], a["u"], a["off"], a["sl"], a["nu"], mode, y, ws, nb, dump,
+                              None)
+
+
+def test_route_argument_errors(L):
+    assert route(L, None) == coli.COLI_E_ARG
+    assert route(L, layer(H=100)) == coli.COLI_E_SHAPE
+    assert route(L, layer(I=0)) == coli.COLI_E_SHAPE
+    assert route(L, layer(E=0)) == coli.COLI_E_SHAPE
+    assert route(L, layer(E=2000)) == coli.COLI_E_SHAPE
+    assert route(L, layer(k=17, E=32)) == coli.COLI_E_SHAPE
+    assert route(L, layer(k=3, E=2)) == coli.COLI_E_SHAPE
+    assert route(L, layer(n_shared=2)) == coli.COLI_E_SHAPE
+    assert route(L, layer(), T=-1) == coli.COLI_E_SHAPE
+    assert route(L, layer(), T=70000) == coli.COLI_E_SHAPE
+    assert route(L, layer(router_w=0)) == coli.COLI_E_ARG
+    assert route(L, layer(), x=0) == coli.COLI_E_ARG
+    assert route(L, layer(), ws=0) == coli.COLI_E_ARG
+    assert route(L, layer(), x=MIS) == coli.COLI_E_ALIGN
+    assert route(L, layer(router_bias=MIS)) == coli.COLI_E_ALIGN
+    assert route(L, layer(), nb=16) == coli.COLI_E_WORKSPACE
+    assert route(L, layer(), T=0) == coli.COLI_OK  # no-op, nothing enqueued
+
+
+def test_union_argument_errors(L):
+    U = L.coli_moe_union
+    assert U(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert U(FAKE, 4, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert U(FAKE, 4, 17, 1024, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert U(FAKE, -2, 2, 16, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert U(None, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_ARG
+    assert U(FAKE, 4, 2, 16, FAKE, FAKE, None, FAKE, None) == coli.COLI_E_ARG
+    assert U(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, None, None) == coli.COLI_E_ARG
+    assert U(FAKE, 4, 2, 16, MIS, FAKE, FAKE, FAKE, None) == coli.COLI_E_ALIGN
+
+
+def test_forward_argument_errors(L):
+    assert forward(L, None) == coli.COLI_E_ARG
+    assert forward(L, layer(w13=0)) == coli.COLI_E_ARG
+    assert forward(L, layer(n_shared=0)) == coli.COLI_E_ARG         # shared pointers given
+    assert forward(L, layer(sh_w2=0)) == coli.COLI_E_ARG            # shared incomplete
+    assert forward(L, layer(s2=MIS)) == coli.COLI_E_ALIGN
+    assert forward(L, layer(), mode=3) == coli.COLI_E_UNSUPPORTED
+    assert forward(L, layer(), mode=0, dump=FAKE) == coli.COLI_E_ARG
+    assert forward(L, layer(), y=0) == coli.COLI_E_ARG
+    assert forward(L, layer(), nu=0) == coli.COLI_E_ARG
+    assert forward(L, layer(), sl=MIS) == coli.COLI_E_ALIGN
+    assert forward(L, layer(), nb=1024) == coli.COLI_E_WORKSPACE
+    assert forward(L, layer(), mode=1, nb=1024) == coli.COLI_E_WORKSPACE
+    assert forward(L, layer(), T=0) == coli.COLI_OK
+
+
+def test_glue_argument_errors(L):
+    assert L.coli_rmsnorm(FAKE, FAKE, 4, 100, ctypes.c_float(1e-6), None) == coli.COLI_E_SHAPE
+    assert L.coli_rmsnorm(FAKE, FAKE, 4, 128, ctypes.c_float(-1.0), None) == coli.COLI_E_ARG
+    assert L.coli_rmsnorm(MIS, FAKE, 4, 128, ctypes.c_float(1e-6), None) == coli.COLI_E_ALIGN
+    assert L.coli_add_inplace(FAKE, None, 8, None) == coli.COLI_E_ARG
+    assert L.coli_add_inplace(FAKE, FAKE, -1, None) == coli.COLI_E_ARG
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path of a GPU-less host")
+def test_no_device_reports_device_error(L):
+    assert L.coli_moe_device_check() in (coli.COLI_E_DEVICE, coli.COLI_E_UNSUPPORTED)

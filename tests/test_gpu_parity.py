@@ -1,0 +1,241 @@
+"""GPU parity of the HIP library (through its C ABI) against the CPU oracle.
+
+Bit-exact: router selections, union lists, int32 group accumulators.
+Tolerance (max|gpu-ref| <= 1e-3 max|ref| per tensor): routing weights and
+layer outputs.  Inputs are the seeded synthetic workloads (synth module).
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+import int4_routed_expert_bias_amd as coli  # noqa: E402
+import oracle as oracle_mod  # noqa: E402
+import synth  # noqa: E402
+from gpu_util import GpuLayer, assert_close, check_route, make_layer  # noqa: E402
+
+ORC = None
+
+
+def orc():
+    global ORC
+    if ORC is None:
+        ORC = oracle_mod.default()
+    return ORC
+
+
+_LAYERS = {}
+
+
+def workload_layer(name, layer=0):
+    key = (name, layer)
+    if key not in _LAYERS:
+        w = synth.WORKLOADS[name]
+        _LAYERS[key] = GpuLayer(synth.workload_layer(w, layer=layer), w.k, w.n_shared)
+    return _LAYERS[key]
+
+
+def check_union(out, T, k, E):
+    u, off, slots, nu = orc().union(out["ids"], E)
+    assert out["n_union"] == nu, (out["n_union"], nu)
+    assert np.array_equal(out["union_ids"], u), "union_ids"
+    assert np.array_equal(out["offsets"], off), "offsets"
+    assert np.array_equal(out["slots"], slots), "slots"
+
+
+def full_check(lay: GpuLayer, x, mode, rows=None, dump=False):
+    out = lay.run(x, mode, dump=dump)
+    ids, w, _, s = orc().route(lay.orc, x)
+    near = check_route(out["ids"], out["w"], ids, w, s, lay.arrays["router_b"])
+    check_union(out, x.shape[0], lay.k, lay.E)
+    # the layer output is compared on the GPU's own routing (teacher forcing)
+    sel = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    ref = orc().forward_rows(lay.orc, x, out["ids"], out["w"], sel, mode)
+    err = assert_close(out["y"][sel], ref, f"y mode={mode}")
+    return out, near, err
+
+
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
+def test_tiny_workload(mode):
+    lay = workload_layer("tiny")
+    x = synth.workload_x("tiny")
+    full_check(lay, x, mode)
+
+
+@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
+@pytest.mark.parametrize("shape", [(512, 256, 32, 4, 37), (256, 128, 16, 2, 1),
+                                   (320, 192, 10, 3, 67), (64, 64, 5, 5, 9)])
+def test_ragged_shapes(mode, shape):
+    H, I, E, k, T = shape
+    lay = make_layer(H, I, E, k, wid=50 + H % 97)
+    x = synth.activations(H, T, wid=50, layer=1)
+    full_check(lay, x, mode)
+
+
+def test_no_shared_expert():
+    lay = make_layer(256, 128, 12, 3, wid=60, n_shared=0)
+    x = synth.activations(256, 21, wid=60)
+    for mode in (coli.ACT_F32, coli.ACT_I8):
+        full_check(lay, x, mode)
+
+
+@pytest.mark.parametrize("T", [1, 16, 37])
+def test_i8_accumulators_bit_exact(T):
+    lay = make_layer(384, 192, 12, 3, wid=61)
+    x = synth.activations(384, T, wid=61)
+    out = lay.run(x, coli.ACT_I8, dump=True)
+    d = out["dump"]
+    A, k = lay.arrays, lay.k
+    R = T * k + T
+    for r in range(R):
+        if r < T * k:
+            t, e = r // k, out["ids"][r // k, r % k]
+            w13, s13, w2, s2 = A["w13"][e], A["s13"][e], A["w2"][e], A["s2"][e]
+        else:
+            t = r - T * k
+            w13, s13, w2, s2 = A["sh_w13"], A["sh_s13"], A["sh_w2"], A["sh_s2"]
+        ref = orc().expert_i8(w13, s13, w2, s2, x[t])
+        assert np.array_equal(d["acc13"][r], ref["acc13"]), f"acc13 row {r}"
+        # down accumulators: bit-exact given the GPU's own int8 codes of h
+        assert np.array_equal(d["acc2"][r], orc().down_acc_i8(w2, d["qh"][r])), f"acc2 row {r}"
+        # the codes of h agree with the oracle's up to rounding-boundary flips
+        diff = np.abs(d["qh"][r].astype(np.int32) - ref["qh"].astype(np.int32))
+        assert diff.max() <= 1 and (diff > 0).mean() < 0.01, f"qh row {r}"
+        assert_close(d["sh"][r], ref["sh"], f"sh row {r}")
+
+
+def test_i8_accumulator_extremes():
+    """All weight codes -8, all activation codes -127: acc = 65024 per group."""
+    H, I, E, k = 256, 128, 4, 2
+    A = synth.layer_arrays(H, I, E, k, wid=62)
+    for n in ("w13", "sh_w13"):
+        A[n][:] = 0x88
+    lay = GpuLayer(A, k)
+    x = np.full((3, H), -2.5, np.float32)
+    out = lay.run(x, coli.ACT_I8, dump=True)
+    assert np.all(out["dump"]["acc13"] == 64 * 127 * 8)
+
+
+def test_decode_full_size():
+    lay = workload_layer("decode")
+    x = synth.workload_x("decode")
+    out, near, err = full_check(lay, x, coli.ACT_F32)
+    assert near == 0
+    assert out["n_union"] == 8
+
+
+def test_verify_batch_full_size():
+    lay = workload_layer("verify")
+    x = synth.workload_x("verify")
+    out, near, err = full_check(lay, x, coli.ACT_F32)
+    print("verify union size", out["n_union"])
+    # each token's output equals its single-token result, bitwise
+    for t in range(x.shape[0]):
+        single = lay.run(x[t:t + 1], coli.ACT_F32)
+        assert np.array_equal(single["ids"][0], out["ids"][t])
+        assert np.array_equal(single["y"][0].view(np.uint32), out["y"][t].view(np.uint32)), t
+
+
+def test_prefill512_sampled():
+    lay = workload_layer("prefill512")
+    x = synth.workload_x("prefill512")
+    rows = [0, 1, 255, 511]
+    out, near, err = full_check(lay, x, coli.ACT_I8, rows=rows)
+    print("prefill512 union size", out["n_union"], "near ties", near)
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (4096, 8, 256), (3000, 16, 1024), (513, 1, 7)])
+def test_union_sizes(T, k, E):
+    import torch
+    rng = np.random.default_rng(T * 31 + E)
+    p = rng.zipf(1.3, size=E * 4)
+    ids = np.stack([rng.choice(E, size=k, replace=False,
+                               p=(np.arange(E, 0, -1) ** 1.5) / (np.arange(E, 0, -1) ** 1.5).sum())
+                    for _ in range(T)]).astype(np.int32)
+    del p
+    cap = min(E, T * k)
+    d_ids = torch.from_numpy(ids).cuda()
+    u = torch.empty(cap, dtype=torch.int32, device="cuda")
+    off = torch.empty(cap + 1, dtype=torch.int32, device="cuda")
+    sl = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    nu = torch.empty(4, dtype=torch.int32, device="cuda")
+    coli.union(d_ids, T, k, E, u, off, sl, nu)
+    torch.cuda.synchronize()
+    ru, roff, rsl, rnu = orc().union(ids, E)
+    assert int(nu[0]) == rnu
+    assert np.array_equal(u.cpu().numpy(), ru)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sl.cpu().numpy(), rsl)
+
+
+@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
+def test_determinism_and_batch_invariance(mode):
+    lay = make_layer(512, 256, 16, 4, wid=63)
+    x = synth.activations(512, 24, wid=63)
+    a = lay.run(x, mode)
+    b = lay.run(x, mode)
+    for key in ("ids", "w", "y", "union_ids", "offsets", "slots"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+    # a token alone and inside the batch: identical bits
+    for t in (0, 13, 23):
+        s = lay.run(x[t:t + 1], mode)
+        assert np.array_equal(s["ids"][0], a["ids"][t])
+        assert np.array_equal(s["y"][0].view(np.uint32), a["y"][t].view(np.uint32)), (mode, t)
+    # permuting the tokens permutes the outputs
+    p = np.random.default_rng(5).permutation(24)
+    c = lay.run(x[p], mode)
+    assert np.array_equal(c["y"].view(np.uint32), a["y"][p].view(np.uint32))
+
+
+def test_relabelled_experts():
+    """Placement/labels never change a token's result (bitwise on the GPU)."""
+    A = synth.layer_arrays(256, 128, 9, 3, wid=64)
+    x = synth.activations(256, 11, wid=64)
+    perm = np.random.default_rng(9).permutation(9)
+    inv = np.argsort(perm)
+    B = dict(A)
+    for n in ("router_w", "router_b", "w13", "s13", "w2", "s2"):
+        B[n] = np.ascontiguousarray(A[n][inv])
+    for mode in (coli.ACT_F32, coli.ACT_I8):
+        a = GpuLayer(A, 3).run(x, mode)
+        b = GpuLayer(B, 3).run(x, mode)
+        assert np.array_equal(b["ids"], perm[a["ids"]])
+        assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
+
+
+def test_zero_tokens_is_noop():
+    import torch
+    lay = make_layer(128, 64, 4, 2, wid=65)
+    b = coli.Buffers(lay.dev, 0, coli.ACT_F32)
+    x = torch.empty((1, 128), device="cuda")
+    coli.run_layer(lay.dev, x, b)
+    torch.cuda.synchronize()
+
+
+def test_all_experts_selected():
+    lay = make_layer(192, 128, 6, 6, wid=66)
+    x = synth.activations(192, 5, wid=66)
+    for mode in (coli.ACT_F32, coli.ACT_I8):
+        out, _, _ = full_check(lay, x, mode)
+        assert out["n_union"] == 6
+
+
+def test_rmsnorm_and_add():
+    import torch
+    x = (np.random.default_rng(1).standard_normal((33, 640)) * 7).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    out = torch.empty_like(xd)
+    coli.rmsnorm(xd, out, 33, 640, 1e-6)
+    ref = orc().rmsnorm(x)
+    d = np.abs(out.cpu().numpy().view(np.int32).astype(np.int64) - ref.view(np.int32))
+    assert d.max() <= 1
+    y = torch.ones_like(xd)
+    coli.add_inplace(xd, y, xd.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(xd.cpu().numpy(), x + np.float32(1.0))
