@@ -121,6 +121,11 @@ __device__ __forceinline__ bool better(float ka, int ea, float kb, int eb)
     return ka > kb || (ka == kb && ea < eb);
 }
 
+__device__ __forceinline__ float sigmoid_fp64(float l)
+{
+    return (float)(1.0 / (1.0 + exp(-(double)l)));
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
@@ -129,69 +134,48 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float s[kMaxPerLane], key[kMaxPerLane];
-    uint32_t taken = 0;
+    const float *lrow = logits + (size_t)t * E;
+    float key[kMaxPerLane];
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-        int e = lane + 64 * i;
-        s[i] = 0.f;
-        key[i] = 0.f;
-        if (e < E) {
-            double l = (double)logits[(size_t)t * E + e];
-            s[i] = (float)(1.0 / (1.0 + exp(-l)));
-            key[i] = s[i] + bias[e];
-        }
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? sigmoid_fp64(lrow[e]) + bias[e] : 0.f;
     }
-    float sel_s[COLI_MAX_K_DEV];
-    int sel_e[COLI_MAX_K_DEV];
-#pragma unroll
-    for (int j = 0; j < COLI_MAX_K_DEV; ++j) {
-        sel_s[j] = 0.f;
-        sel_e[j] = 0;
-    }
-#pragma unroll
-    for (int j = 0; j < COLI_MAX_K_DEV; ++j) {
-        if (j >= k) continue;  // k is uniform across the wave
-        // lane-local best
+    uint32_t taken = 0;
+    int sel = 0;  // lane j < k keeps the j-th selected expert
+    for (int j = 0; j < k; ++j) {
+        // lane-local best among the lane's untaken experts
         float bk = 0.f;
-        int be = 0x7fffffff, bi = -1;
-        float bs = 0.f;
+        int be = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < kMaxPerLane; ++i) {
-            int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u)) {
-                if (bi < 0 || better(key[i], e, bk, be)) {
-                    bk = key[i]; be = e; bi = i; bs = s[i];
-                }
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u) && (be == 0x7fffffff || better(key[i], e, bk, be))) {
+                bk = key[i];
+                be = e;
             }
         }
-        // wave argmax (lanes without candidates carry be = INT_MAX)
-        bool have = bi >= 0;
+        // wave argmax on (key desc, expert asc); be == INT_MAX marks "none"
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
-            float ok = __shfl_xor(bk, off, 64);
-            int oe = __shfl_xor(be, off, 64);
-            float os = __shfl_xor(bs, off, 64);
-            int oh = __shfl_xor((int)have, off, 64);
-            if (oh && (!have || better(ok, oe, bk, be))) {
-                bk = ok; be = oe; bs = os; have = true;
+            const float ok = __shfl_xor(bk, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (oe != 0x7fffffff && (be == 0x7fffffff || better(ok, oe, bk, be))) {
+                bk = ok;
+                be = oe;
             }
         }
-        sel_s[j] = bs;
-        sel_e[j] = be;
+        if (lane == j) sel = be;
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
     }
-    if (lane == 0) {
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < COLI_MAX_K_DEV; ++j)
-            if (j < k) sum += sel_s[j];
-#pragma unroll
-        for (int j = 0; j < COLI_MAX_K_DEV; ++j)
-            if (j < k) {
-                ids[(size_t)t * k + j] = sel_e[j];
-                w[(size_t)t * k + j] = sel_s[j] / sum;
-            }
+    // weights: the selected scores, recomputed exactly as in the keys,
+    // normalised with an fp32 sum in selection order
+    const float sj = (lane < k) ? sigmoid_fp64(lrow[sel]) : 0.f;
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __shfl(sj, j, 64);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = sel;
+        w[(size_t)t * k + lane] = sj / sum;
     }
 }
 

@@ -239,3 +239,20 @@ def test_rmsnorm_and_add():
     coli.add_inplace(xd, y, xd.numel())
     torch.cuda.synchronize()
     assert np.array_equal(xd.cpu().numpy(), x + np.float32(1.0))
+
+
+@pytest.mark.parametrize("E,k,T", [(64, 8, 3), (65, 1, 5), (256, 8, 33), (256, 16, 9),
+                                   (1000, 7, 11), (1024, 16, 70), (2, 2, 4)])
+def test_route_expert_counts(E, k, T):
+    """Router across lane counts: several experts per lane, k up to 16, both
+    logits paths (a few tokens: row streaming; many tokens: tiled)."""
+    import torch
+    H = 128
+    A = synth.layer_arrays(H, 64, E, k, wid=67, layer=E % 7)
+    lay = GpuLayer(A, k)
+    x = synth.activations(H, T, wid=67, layer=E % 5)
+    b = coli.Buffers(lay.dev, T, coli.ACT_F32)
+    coli.route(lay.dev, torch.from_numpy(x).cuda(), T, b.ids, b.w, b.workspace)
+    torch.cuda.synchronize()
+    ids, w, _, s = orc().route(lay.orc, x)
+    check_route(b.ids[:T].cpu().numpy(), b.w[:T].cpu().numpy(), ids, w, s, A["router_b"])
