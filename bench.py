@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of the int4 routed-expert MoE layer on one MI355X.
+
+A step is one pass of the whole path -- coli_moe_route, coli_moe_union,
+coli_moe_forward -- over one batch of seeded synthetic tokens.
+
+Workloads (--workload):
+  decode         H6144 I2048 E256 top-8 + 1 shared, T=1, fp32 family
+                 (the default); steps cycle over --layers resident copies of
+                 the layer (distinct weights, like consecutive layers of a
+                 model) so each step reads its experts from HBM and not from
+                 the 256 MB Infinity Cache.
+  verify         same layer, T=4 tokens sharing a common component, fp32.
+  prefill512     same layer, T=512, Zipf(1.1) popularity, int8 family.
+  prefill4096x8  T=4096 through 8 stacked layers (RMS pre-norm, residual),
+                 int8 family; a step is the whole stack.
+  tiny           H256 I128 E16 top-2, T=4 (parity-size workload).
+
+The timed steps are captured once in a HIP graph and replayed between two
+synchronisations (wall clock).  The dominant kernel's duration comes from
+HIP events the library records on its own stream around each kernel
+(coli_moe_forward_profiled), over the same inputs.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+I8_PEAK_TOPS = 5000.0     # dense int8 MFMA
+METRIC = "MoE layer tokens/s + achieved HBM GB/s (decode) / int8 TOPS (prefill)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """HIP events through the runtime torch already loaded."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads libamdhip64.so.7 first)
+        self.L = ctypes.CDLL("libamdhip64.so.7")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def expert_bytes(H, I):
+    return 3 * I * H // 2 + 3 * I * (H // 64) * 2
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "verify", "prefill512", "prefill4096x8", "tiny"])
+    ap.add_argument("--layers", type=int, default=None, help="resident layer copies cycled (decode/verify)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU sharding "
+                                   "of the layer is a design (see the design notes), not built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_bias_amd as coli
+    import synth
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+    if coli.device_check() != coli.COLI_OK:
+        raise SystemExit("device is not gfx950: " + coli.strerror(coli.device_check()))
+
+    w = synth.WORKLOADS[args.workload]
+    H, I, E, k, T = w.H, w.I, w.E, w.k, w.T
+    mode = coli.ACT_I8 if w.act_mode == "i8" else coli.ACT_F32
+    stacked = w.layers > 1
+    defaults = {"decode": (256, 32), "verify": (128, 16), "prefill512": (20, 4),
+                "prefill4096x8": (4, 1), "tiny": (256, 32)}
+    K = args.steps if args.steps is not None else defaults[w.name][0]
+    W = args.warmup if args.warmup is not None else defaults[w.name][1]
+    if stacked:
+        NL = w.layers
+    else:
+        NL = args.layers if args.layers is not None else (8 if w.name in ("decode", "verify") else 1)
+
+    # ---- resident layers -------------------------------------------------
+    t0 = time.time()
+    layers = []
+    host0 = None
+    for l in range(NL):
+        A = synth.workload_layer(w, layer=l)
+        if l == 0:
+            host0 = A
+        layers.append(coli.DeviceLayer(A, k=k, n_shared=w.n_shared))
+        if l > 0:
+            del A
+    log(f"[bench] {NL} layer(s) resident ({NL * (w.E + 1) * expert_bytes(H, I) / 1e9:.1f} GB experts) "
+        f"in {time.time() - t0:.1f}s")
+
+    # ---- inputs and buffers ----------------------------------------------
+    nsteps_in = W + K
+    if stacked:
+        xs = [torch.from_numpy(synth.workload_x(w, layer=0)).cuda()]
+    elif w.x_kind == "overlap":
+        xs = [torch.from_numpy(synth.activations(H, T, wid=w.wid, layer=100 + s, kind="overlap")).cuda()
+              for s in range(nsteps_in)]
+    else:
+        xall = torch.from_numpy(synth.activations(H, T * nsteps_in, wid=w.wid)).cuda()
+        xs = [xall[s * T:(s + 1) * T] for s in range(nsteps_in)]
+    bufs = coli.Buffers(layers[0], T, mode)
+    if stacked:
+        resid = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        xhat = torch.empty_like(resid)
+
+    def step(s):
+        if stacked:
+            resid.copy_(xs[0])
+            for l, lay in enumerate(layers):
+                coli.rmsnorm(resid, xhat, T, H, 1e-6)
+                coli.run_layer(lay, xhat, bufs)
+                coli.add_inplace(resid, bufs.y, T * H)
+        else:
+            coli.run_layer(layers[s % NL], xs[s], bufs)
+
+    # ---- warmup ----------------------------------------------------------
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+
+    # ---- timed region ----------------------------------------------------
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(g, stream=cap_stream):
+                for s in range(K):
+                    step(W + s if not stacked else s)
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay (graph upload)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+    else:
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(K):
+            step(W + s if not stacked else s)
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+    elapsed = t_end - t_start
+    layer_passes = K * (w.layers if stacked else 1)
+    value = layer_passes * T / elapsed
+    ms_per_step = elapsed * 1e3 / K
+
+    # ---- dominant kernel: per-kernel events on the library's stream ------
+    hip = Hip()
+    names = coli.forward_kernel_names(mode)
+    nk = len(names)
+    dom = 0 if mode == coli.ACT_F32 else names.index("ggemm_gateup_kernel")
+    prof_steps = min(K, 64)
+    ev = [[hip.event() for _ in range(nk + 1)] for _ in range(prof_steps * (w.layers if stacked else 1))]
+    union_sizes = []
+    torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
+    i = 0
+    for s in range(prof_steps):
+        if stacked:
+            resid.copy_(xs[0])
+            lays = list(enumerate(layers))
+        else:
+            lays = [(0, layers[(W + s) % NL])]
+        for _, lay in lays:
+            x_in = xs[W + s] if not stacked else xhat
+            if stacked:
+                coli.rmsnorm(resid, xhat, T, H, 1e-6)
+            coli.route(lay, x_in, T, bufs.ids, bufs.w, bufs.workspace)
+            coli.union(bufs.ids, T, k, E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union)
+            coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
+                                  bufs.slots, bufs.n_union, mode, bufs.y, bufs.workspace, ev[i])
+            union_sizes.append(bufs.n_union[:1].clone())
+            if stacked:
+                coli.add_inplace(resid, bufs.y, T * H)
+            i += 1
+    torch.cuda.synchronize()
+    per_kernel = np.zeros(nk)
+    for e in ev:
+        for j in range(nk):
+            per_kernel[j] += hip.elapsed_ms(e[j], e[j + 1])
+    per_kernel /= len(ev)
+    for e in ev:
+        for x_ in e:
+            hip.destroy(x_)
+    U = np.array([int(u.item()) for u in union_sizes])
+    dur_s = per_kernel[dom] * 1e-3
+    n_exp = U.mean() + w.n_shared
+    R = T * k + w.n_shared * T
+    gateup_bytes = n_exp * (2 * I * (H // 2) + 2 * I * (H // 64) * 2)
+    if mode == coli.ACT_F32:
+        algo_bytes = gateup_bytes + T * H * 4 + R * I * 4
+    else:
+        algo_bytes = gateup_bytes + T * H + T * (H // 64) * 4 + R * I + R * (I // 64) * 4
+    algo_ops = 2.0 * R * 2 * I * H  # int8 ops (or fp32 flops) of the gate/up matmul
+    t_hbm = algo_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = algo_ops / (I8_PEAK_TOPS * 1e12) if mode == coli.ACT_I8 else 0.0
+    if t_mfma > t_hbm:
+        ach = algo_ops / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(ach / I8_PEAK_TOPS, 4), "traffic": None}
+    else:
+        ach = algo_bytes / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = names[dom]
+    roof["kernel_us"] = round(per_kernel[dom] * 1e3, 2)
+    roof["algorithmic_bytes_per_launch"] = int(algo_bytes)
+    roof["algorithmic_ops_per_launch"] = int(algo_ops)
+    kernels_us = {names[j]: round(per_kernel[j] * 1e3, 2) for j in range(nk)}
+
+    # ---- CPU baseline: the oracle on a bounded sample ---------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        olay = oracle.Layer(host0, k=k, n_shared=w.n_shared)
+        xh = synth.workload_x(w, layer=0) if (stacked or w.x_kind == "overlap") else \
+            synth.activations(H, T, wid=w.wid)
+        done, t_cpu0 = 0, time.perf_counter()
+        omode = oracle.ACT_I8 if mode == coli.ACT_I8 else oracle.ACT_F32
+        while True:
+            xt = xh[done % T:done % T + 1]
+            ids, wt, _, _ = orc.route(olay, xt)
+            orc.union(ids, E)
+            orc.forward(olay, xt, ids, wt, omode)
+            done += 1
+            if time.perf_counter() - t_cpu0 >= args.cpu_seconds or done >= 1000:
+                break
+        t_cpu = time.perf_counter() - t_cpu0
+        cpu = {"value": round(done / t_cpu, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} token(s) of the {w.name} workload through route, union and "
+                         f"forward on layer 0 ({t_cpu:.1f} s, single-threaded C oracle)"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8" if mode == coli.ACT_I8 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.note, "H": H, "I": I, "E": E, "k": k,
+                   "T": T, "n_shared": w.n_shared, "layers": NL,
+                   "act_mode": "i8" if mode == coli.ACT_I8 else "f32",
+                   "graph": use_graph, "union_size_mean": round(float(U.mean()), 2),
+                   "union_size_minmax": [int(U.min()), int(U.max())],
+                   "kernels_us": kernels_us},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,6 +173,25 @@ int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
                      int32_t act_mode, float *y, void *workspace, size_t workspace_bytes,
                      int32_t *acc_dump, void *hip_stream);
 
+/* Profiling variant of coli_moe_forward: the same work, and in addition
+ * events[i] (hipEvent_t values created by the caller) is recorded on
+ * hip_stream before the i-th kernel the call launches and events[n] after
+ * its last kernel, n = coli_moe_forward_kernel_count(act_mode).  Requires
+ * n_events >= n + 1 (else COLI_E_ARG, nothing enqueued).  For measurement
+ * only; the production path is coli_moe_forward. */
+int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
+                              const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *union_ids, const int32_t *offsets,
+                              const int32_t *slots, const int32_t *n_union, int32_t act_mode,
+                              float *y, void *workspace, size_t workspace_bytes,
+                              int32_t *acc_dump, void **events, int32_t n_events,
+                              void *hip_stream);
+
+/* Number of kernels coli_moe_forward launches for act_mode (0 if unknown),
+ * and the name of the i-th one (NULL if out of range). */
+int coli_moe_forward_kernel_count(int32_t act_mode);
+const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t i);
+
 /* Size in bytes of the acc_dump buffer of coli_moe_forward (0 if invalid). */
 size_t coli_moe_acc_dump_bytes(int32_t H, int32_t I, int32_t k, int32_t T, int32_t n_shared);
 

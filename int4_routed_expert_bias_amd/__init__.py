@@ -21,8 +21,10 @@ COLI_OK, COLI_E_ARG, COLI_E_SHAPE, COLI_E_ALIGN, COLI_E_WORKSPACE, COLI_E_DEVICE
 
 # every symbol declared in include/coli_moe.h
 EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
-           "coli_moe_union", "coli_moe_forward", "coli_moe_acc_dump_bytes",
-           "coli_moe_strerror", "coli_moe_device_check", "coli_rmsnorm", "coli_add_inplace")
+           "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
+           "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
+           "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
+           "coli_rmsnorm", "coli_add_inplace")
 
 
 class ColiError(RuntimeError):
@@ -47,6 +49,9 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        # Load torch's HIP runtime first so that the library binds to the same
+        # runtime instance (one libamdhip64.so.7 per process).
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         sig = {
@@ -56,6 +61,10 @@ def lib():
             "coli_moe_union": ([vp, i32, i32, i32, vp, vp, vp, vp, vp], ctypes.c_int),
             "coli_moe_forward": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp, vp],
                                  ctypes.c_int),
+            "coli_moe_forward_profiled": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp,
+                                           vp, i32, vp], ctypes.c_int),
+            "coli_moe_forward_kernel_count": ([i32], ctypes.c_int),
+            "coli_moe_forward_kernel_name": ([i32, i32], ctypes.c_char_p),
             "coli_moe_acc_dump_bytes": ([i32, i32, i32, i32, i32], sz),
             "coli_moe_strerror": ([ctypes.c_int], ctypes.c_char_p),
             "coli_moe_device_check": ([], ctypes.c_int),
@@ -126,6 +135,23 @@ def forward(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y
                                   _ptr(offsets), _ptr(slots), _ptr(n_union), act_mode, _ptr(y),
                                   _ptr(workspace), nb, _ptr(acc_dump), _stream(stream)),
            "coli_moe_forward")
+
+
+def forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y,
+                     workspace, events, stream=None):
+    """coli_moe_forward that records ``events`` (raw hipEvent_t handles)."""
+    nb = workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib().coli_moe_forward_profiled(layer.ref, _ptr(x), T, _ptr(ids), _ptr(w),
+                                           _ptr(union_ids), _ptr(offsets), _ptr(slots),
+                                           _ptr(n_union), act_mode, _ptr(y), _ptr(workspace), nb,
+                                           None, arr, len(events), _stream(stream)),
+           "coli_moe_forward_profiled")
+
+
+def forward_kernel_names(act_mode):
+    n = lib().coli_moe_forward_kernel_count(act_mode)
+    return [lib().coli_moe_forward_kernel_name(act_mode, i).decode() for i in range(n)]
 
 
 def rmsnorm(x, xhat, T, H, eps=1e-6, stream=None):

@@ -147,16 +147,22 @@ int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int
                                   static_cast<hipStream_t>(hip_stream)));
 }
 
-int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
-                     const int32_t *topk_ids, const float *topk_w, const int32_t *union_ids,
-                     const int32_t *offsets, const int32_t *slots, const int32_t *n_union,
-                     int32_t act_mode, float *y, void *workspace, size_t workspace_bytes,
-                     int32_t *acc_dump, void *hip_stream)
+static int forward_impl(const coli_moe_layer *L, const float *x, int32_t T,
+                        const int32_t *topk_ids, const float *topk_w, const int32_t *union_ids,
+                        const int32_t *offsets, const int32_t *slots, const int32_t *n_union,
+                        int32_t act_mode, float *y, void *workspace, size_t workspace_bytes,
+                        int32_t *acc_dump, void *hip_stream, Marks *mk)
 {
     if (int st = check_layer(L, true)) return st;
     if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
     if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return COLI_E_UNSUPPORTED;
     if (acc_dump && act_mode != COLI_ACT_I8) return COLI_E_ARG;
+    if (mk) {
+        const int need = (act_mode == COLI_ACT_I8 ? kForwardKernelsI8 : kForwardKernelsF32) + 1;
+        if (!mk->ev || mk->n < need) return COLI_E_ARG;
+        for (int i = 0; i < need; ++i)
+            if (!mk->ev[i]) return COLI_E_ARG;
+    }
     if (T == 0) return COLI_OK;
     if (!x || !topk_ids || !topk_w || !union_ids || !offsets || !slots || !n_union || !y ||
         !workspace)
@@ -176,8 +182,53 @@ int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
     io.dump = dump_layout(L->H, L->I, L->k, T, L->n_shared);
     const LayerDev d = to_dev(L);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    return status_of(act_mode == COLI_ACT_I8 ? launch_forward_i8(d, io, st)
-                                             : launch_forward_f32(d, io, st));
+    return status_of(act_mode == COLI_ACT_I8 ? launch_forward_i8(d, io, st, mk)
+                                             : launch_forward_f32(d, io, st, mk));
+}
+
+int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
+                     const int32_t *topk_ids, const float *topk_w, const int32_t *union_ids,
+                     const int32_t *offsets, const int32_t *slots, const int32_t *n_union,
+                     int32_t act_mode, float *y, void *workspace, size_t workspace_bytes,
+                     int32_t *acc_dump, void *hip_stream)
+{
+    return forward_impl(L, x, T, topk_ids, topk_w, union_ids, offsets, slots, n_union, act_mode,
+                        y, workspace, workspace_bytes, acc_dump, hip_stream, nullptr);
+}
+
+int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
+                              const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *union_ids, const int32_t *offsets,
+                              const int32_t *slots, const int32_t *n_union, int32_t act_mode,
+                              float *y, void *workspace, size_t workspace_bytes,
+                              int32_t *acc_dump, void **events, int32_t n_events,
+                              void *hip_stream)
+{
+    if (!events || n_events < 1) return COLI_E_ARG;
+    Marks mk;
+    mk.ev = events;
+    mk.n = n_events;
+    return forward_impl(L, x, T, topk_ids, topk_w, union_ids, offsets, slots, n_union, act_mode,
+                        y, workspace, workspace_bytes, acc_dump, hip_stream, &mk);
+}
+
+int coli_moe_forward_kernel_count(int32_t act_mode)
+{
+    return act_mode == COLI_ACT_F32 ? kForwardKernelsF32
+           : act_mode == COLI_ACT_I8 ? kForwardKernelsI8 : 0;
+}
+
+const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t i)
+{
+    static const char *f32[kForwardKernelsF32] = {"gemv_int4_kernel<SWIGLU>", "gemv_int4_kernel<PLAIN>",
+                                                  "combine_kernel"};
+    static const char *i8[kForwardKernelsI8] = {"quant_rows_kernel", "schedule_kernel",
+                                                "ggemm_gateup_kernel", "ggemm_down_kernel",
+                                                "combine_kernel"};
+    if (i < 0) return nullptr;
+    if (act_mode == COLI_ACT_F32 && i < kForwardKernelsF32) return f32[i];
+    if (act_mode == COLI_ACT_I8 && i < kForwardKernelsI8) return i8[i];
+    return nullptr;
 }
 
 int coli_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps, void *hip_stream)

@@ -127,6 +127,19 @@ inline DumpLayout dump_layout(int64_t H, int64_t I, int64_t k, int64_t T, int64_
 // ---------------------------------------------------------------------------
 // launcher interface (each returns hipError_t of the launch)
 
+// Optional profiling marks: records caller-created events on the stream
+// before each kernel of a call and after the last one.
+struct Marks {
+    void **ev = nullptr;
+    int n = 0;
+    int i = 0;
+    void mark(hipStream_t st)
+    {
+        if (ev && i < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+        ++i;
+    }
+};
+
 struct LayerDev {
     int32_t H, I, E, k, n_shared;
     const float *router_w, *router_bias;
@@ -156,8 +169,11 @@ struct ForwardIO {
     int32_t *acc_dump; DumpLayout dump;
 };
 
-hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st);
-hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st);
+constexpr int kForwardKernelsF32 = 3;  // gate/up GEMV, down GEMV, combine
+constexpr int kForwardKernelsI8 = 5;   // quant, schedule, gate/up GEMM, down GEMM, combine
+
+hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
+hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_combine(const float *o, const float *w, int32_t T, int32_t k, int32_t H,
                           int32_t n_shared, float *y, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,

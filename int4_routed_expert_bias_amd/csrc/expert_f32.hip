@@ -195,7 +195,7 @@ static hipError_t launch_gemv(const GemvArgs &a, int max_tokens, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st)
+hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk)
 {
     const int T = io.T;
     if (T <= 0) return hipSuccess;
@@ -210,6 +210,7 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     a.N = 2 * L.I; a.K = L.H;
     a.in = io.x; a.in_by_slot = 0;
     a.out = h; a.out_ld = L.I;
+    if (mk) mk->mark(st);
     hipError_t err = launch_gemv<true>(a, T, st);
     if (err != hipSuccess) return err;
     // down: o[row][n]
@@ -217,9 +218,13 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     a.N = L.H; a.K = L.I;
     a.in = h; a.in_by_slot = 1;
     a.out = o; a.out_ld = L.H;
+    if (mk) mk->mark(st);
     err = launch_gemv<false>(a, T, st);
     if (err != hipSuccess) return err;
-    return launch_combine(o, io.w, T, L.k, L.H, L.n_shared, io.y, st);
+    if (mk) mk->mark(st);
+    err = launch_combine(o, io.w, T, L.k, L.H, L.n_shared, io.y, st);
+    if (mk) mk->mark(st);
+    return err;
 }
 
 }  // namespace coli

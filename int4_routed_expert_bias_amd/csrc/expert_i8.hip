@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void ggemm_down_kernel(I8Args a)
     }
 }
 
-hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st)
+hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk)
 {
     const int T = io.T;
     if (T <= 0) return hipSuccess;
@@ -345,10 +345,12 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     int2 *tiles = reinterpret_cast<int2 *>(io.ws + lay.tiles);
 
     const int64_t ng = (int64_t)T * (L.H / 64);
+    if (mk) mk->mark(st);
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, st, io.x, ng,
                        L.H, qx, sx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (mk) mk->mark(st);
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, io.offsets, io.n_union,
                        (int)lay.cap, T, L.n_shared, tiles, (int)lay.max_tiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -367,6 +369,7 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc13) : nullptr;
     a.dump_qh = dump ? reinterpret_cast<int8_t *>(dump_b + io.dump.qh) : nullptr;
     a.dump_sh = dump ? reinterpret_cast<float *>(dump_b + io.dump.sh) : nullptr;
+    if (mk) mk->mark(st);
     hipLaunchKernelGGL(ggemm_gateup_kernel, dim3((L.I + 255) / 256, (unsigned)lay.max_tiles),
                        dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -376,10 +379,14 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.N = L.H; a.K = L.I;
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc2) : nullptr;
     a.dump_qh = nullptr; a.dump_sh = nullptr;
+    if (mk) mk->mark(st);
     hipLaunchKernelGGL(ggemm_down_kernel, dim3((L.H + 255) / 256, (unsigned)lay.max_tiles),
                        dim3(256), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    return launch_combine(o, io.w, T, L.k, L.H, L.n_shared, io.y, st);
+    if (mk) mk->mark(st);
+    err = launch_combine(o, io.w, T, L.k, L.H, L.n_shared, io.y, st);
+    if (mk) mk->mark(st);
+    return err;
 }
 
 }  // namespace coli

@@ -256,3 +256,40 @@ def test_route_expert_counts(E, k, T):
     torch.cuda.synchronize()
     ids, w, _, s = orc().route(lay.orc, x)
     check_route(b.ids[:T].cpu().numpy(), b.w[:T].cpu().numpy(), ids, w, s, A["router_b"])
+
+
+@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
+def test_graph_replay_matches_eager(mode):
+    """route -> union -> forward captured in a HIP graph: every replay (with
+    eager work and synchronisations in between) equals the eager result."""
+    import torch
+    lay = make_layer(512, 256, 16, 4, wid=68)
+    T = 19
+    x1 = torch.from_numpy(synth.activations(512, T, wid=68)).cuda()
+    x2 = torch.from_numpy(synth.activations(512, T, wid=68, layer=1)).cuda()
+    eager = {}
+    for name, x in (("a", x1), ("b", x2)):
+        b = coli.Buffers(lay.dev, T, mode)
+        coli.run_layer(lay.dev, x, b)
+        torch.cuda.synchronize()
+        eager[name] = (b.ids.cpu().clone(), b.y.cpu().clone())
+    xin = torch.empty_like(x1)
+    bufs = coli.Buffers(lay.dev, T, mode)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            coli.run_layer(lay.dev, xin, bufs)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        name = "a" if rep % 2 == 0 else "b"
+        xin.copy_(x1 if name == "a" else x2)
+        bufs.y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs.ids.cpu(), eager[name][0]), rep
+        assert torch.equal(bufs.y.cpu().view(torch.int32), eager[name][1].view(torch.int32)), rep
+        other = coli.Buffers(lay.dev, T, mode)     # eager work between replays
+        coli.run_layer(lay.dev, x2, other)
+        torch.cuda.synchronize()
