@@ -220,7 +220,7 @@ int coli_moe_forward_kernel_count(int32_t act_mode)
 
 const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t i)
 {
-    static const char *f32[kForwardKernelsF32] = {"gemv_int4_kernel<SWIGLU>", "gemv_int4_kernel<PLAIN>",
+    static const char *f32[kForwardKernelsF32] = {"gateup_f32_kernel", "down_f32_kernel",
                                                   "combine_kernel"};
     static const char *i8[kForwardKernelsI8] = {"quant_rows_kernel", "schedule_kernel",
                                                 "ggemm_gateup_kernel", "ggemm_down_kernel",

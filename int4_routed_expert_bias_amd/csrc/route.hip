@@ -114,68 +114,95 @@ __global__ __launch_bounds__(256) void logits_gemm_kernel(const float *__restric
 }
 
 // --- top-k: one wave per token, 4 tokens per workgroup -------------------
-constexpr int kMaxPerLane = 16;  // E <= 1024
-
-__device__ __forceinline__ bool better(float ka, int ea, float kb, int eb)
-{
-    return ka > kb || (ka == kb && ea < eb);
-}
-
+// Radix select: the k-th largest key is found bit by bit with wave ballots
+// (32 rounds, no shuffles); keys equal to it are taken in expert order; the
+// k winners are then ordered by (key desc, expert asc) through LDS.
 __device__ __forceinline__ float sigmoid_fp64(float l)
 {
     return (float)(1.0 / (1.0 + exp(-(double)l)));
 }
 
+// Monotone map of an fp32 key to uint32 (larger float -> larger integer);
+// -0 is folded into +0 first so that equal keys compare equal.
+__device__ __forceinline__ uint32_t order_bits(float z)
+{
+    const uint32_t u = __float_as_uint(z + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
                                                    float *__restrict__ w)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float *lrow = logits + (size_t)t * E;
-    float key[kMaxPerLane];
+    __shared__ uint32_t sk[4][COLI_MAX_K_DEV];
+    __shared__ int32_t se[4][COLI_MAX_K_DEV];
+    __shared__ float ss[4][COLI_MAX_K_DEV];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    const bool live = t < T;
+    const float *lrow = logits + (size_t)(live ? t : 0) * E;
+    uint32_t key[KPL];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = (e < E) ? sigmoid_fp64(lrow[e]) + bias[e] : 0.f;
+        key[i] = (live && e < E) ? order_bits(sigmoid_fp64(lrow[e]) + bias[e]) : 0u;
     }
-    uint32_t taken = 0;
-    int sel = 0;  // lane j < k keeps the j-th selected expert
-    for (int j = 0; j < k; ++j) {
-        // lane-local best among the lane's untaken experts
-        float bk = 0.f;
-        int be = 0x7fffffff;
+    // largest tau with #{key >= tau} >= k  (valid keys are >= 1)
+    uint32_t tau = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = tau | (1u << b);
+        int c = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && (be == 0x7fffffff || better(key[i], e, bk, be))) {
-                bk = key[i];
-                be = e;
-            }
-        }
-        // wave argmax on (key desc, expert asc); be == INT_MAX marks "none"
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ok = __shfl_xor(bk, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (oe != 0x7fffffff && (be == 0x7fffffff || better(ok, oe, bk, be))) {
-                bk = ok;
-                be = oe;
-            }
-        }
-        if (lane == j) sel = be;
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        for (int i = 0; i < KPL; ++i) c += __popcll(__ballot(key[i] >= cand));
+        if (c >= k) tau = cand;
     }
-    // weights: the selected scores, recomputed exactly as in the keys,
-    // normalised with an fp32 sum in selection order
-    const float sj = (lane < k) ? sigmoid_fp64(lrow[sel]) : 0.f;
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += __shfl(sj, j, 64);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = sel;
-        w[(size_t)t * k + lane] = sj / sum;
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) gt += __popcll(__ballot(key[i] > tau));
+    const int need = k - gt;  // keys equal to tau to take, lowest experts first
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const uint64_t eqm = __ballot(key[i] == tau);
+        const bool is_eq = key[i] == tau;
+        const bool sel = key[i] > tau || (is_eq && eq_before + __popcll(eqm & lt_mask) < need);
+        const uint64_t selm = __ballot(sel);
+        if (sel && live && sel_before + __popcll(selm & lt_mask) < k) {
+            const int pos = sel_before + __popcll(selm & lt_mask);
+            sk[wv][pos] = key[i];
+            se[wv][pos] = lane + 64 * i;
+        }
+        eq_before += __popcll(eqm);
+        sel_before += __popcll(selm);
+    }
+    __syncthreads();
+    // lane j < k: rank of winner j among the winners, then its weight
+    uint32_t mk = 0;
+    int me = 0, rank = 0;
+    if (live && lane < k) {
+        mk = sk[wv][lane];
+        me = se[wv][lane];
+        for (int j = 0; j < k; ++j) {
+            const uint32_t ok = sk[wv][j];
+            const int oe = se[wv][j];
+            rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    float sj = 0.f;
+    if (live && lane < k) {
+        sj = sigmoid_fp64(lrow[me]);
+        ss[wv][rank] = sj;
+    }
+    __syncthreads();
+    if (live && lane < k) {
+        float sum = 0.f;
+        for (int j = 0; j < k; ++j) sum += ss[wv][j];  // fp32, selection order
+        ids[(size_t)t * k + rank] = me;
+        w[(size_t)t * k + rank] = sj / sum;
     }
 }
 
@@ -201,9 +228,17 @@ hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st)
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, io.logits, L.router_bias,
-                       T, E, L.k, io.ids, io.w);
-    return hipGetLastError();
+    const int kpl = (E + 63) / 64;
+#define COLI_TOPK(N) \
+    if (kpl <= N) { hipLaunchKernelGGL(topk_kernel<N>, dim3((T + 3) / 4), dim3(256), 0, st, io.logits, \
+                                       L.router_bias, T, E, L.k, io.ids, io.w); return hipGetLastError(); }
+    COLI_TOPK(1)
+    COLI_TOPK(2)
+    COLI_TOPK(4)
+    COLI_TOPK(8)
+    COLI_TOPK(16)
+#undef COLI_TOPK
+    return hipErrorInvalidValue;
 }
 
 }  // namespace coli

@@ -114,11 +114,61 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__r
     }
 }
 
+// Small batches (T*k <= 64): one wave sorts the 64 keys (id << 6 | slot)
+// with a bitonic network and reads the union off the sorted order.
+__global__ __launch_bounds__(64) void union_small_kernel(const int32_t *__restrict__ ids, int n,
+                                                         int E, int cap,
+                                                         int32_t *__restrict__ union_ids,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ slots,
+                                                         int32_t *__restrict__ n_union)
+{
+    const int lane = threadIdx.x;
+    int id = (lane < n) ? ids[lane] : -1;
+    const bool valid = id >= 0 && id < E;
+    uint32_t key = valid ? ((uint32_t)id << 6 | (uint32_t)lane) : 0xFFFFFFFFu;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride >= 1; stride >>= 1) {
+            const uint32_t other = __shfl_xor(key, stride, 64);
+            const bool ascending = (lane & size) == 0 || size == 64;
+            const bool lower = (lane & stride) == 0;
+            const uint32_t lo = min(key, other), hi = max(key, other);
+            key = (lower == ascending) ? lo : hi;
+        }
+    }
+    const bool has = key != 0xFFFFFFFFu;
+    const int sid = has ? (int)(key >> 6) : -1;
+    const int prev = __shfl_up(sid, 1, 64);
+    const bool first = has && (lane == 0 || prev != sid);
+    const uint64_t fm = __ballot(first);
+    const int U = __popcll(fm);
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int upos = __popcll(fm & lt_mask);
+    if (has) slots[lane] = (int32_t)(key & 63u);
+    if (first && upos < cap) {
+        union_ids[upos] = sid;
+        offsets[upos] = lane;
+    }
+    if (lane >= U && lane < cap) union_ids[lane] = -1;
+    if (lane >= U && lane <= cap) offsets[lane] = n;
+    if (lane == 0) {
+        n_union[0] = U;
+        if (cap == 64) offsets[64] = n;
+    }
+}
+
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                         int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st)
 {
     const int n = T * k;
     const int cap = n < E ? n : E;
+    if (n <= 64) {
+        hipLaunchKernelGGL(union_small_kernel, dim3(1), dim3(64), 0, st, ids, n, E, cap, union_ids,
+                           offsets, slots, n_union);
+        return hipGetLastError();
+    }
     const size_t lds = (size_t)(kUnionWaves + 5) * E * sizeof(int32_t);
     hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), lds, st, ids, n, E, cap,
                        union_ids, offsets, slots, n_union);
