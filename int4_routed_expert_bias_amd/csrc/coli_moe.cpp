@@ -65,6 +65,26 @@ int device_check()
     return s == 1 ? COLI_OK : COLI_E_UNSUPPORTED;
 }
 
+std::atomic<int> g_dev_cus[64];  // 0 unknown, else the CU count
+
+}  // namespace
+
+int coli::device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = g_dev_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        g_dev_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+namespace {
+
 LayerDev to_dev(const coli_moe_layer *L)
 {
     LayerDev d;

@@ -155,6 +155,9 @@ struct RouteIO {
     float *logits;  // workspace
 };
 
+// Compute units of the current device (cached per device on first use).
+int device_cu_count();
+
 hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st);
 
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,

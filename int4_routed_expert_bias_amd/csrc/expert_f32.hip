@@ -4,27 +4,30 @@
 // 64-group ("colibri: 744B MoE...", section "はじめにとソースが語らないこと":
 // the gs64 build).
 //
-// The matmuls stream every union expert's packed weights once from HBM
-// (a GEMV at decode, a few tokens for a verify batch).  Design for CDNA4:
-//  - grid = (row blocks, union entries + shared expert); many small
-//    workgroups keep ~20 waves per CU with all their weight loads in flight;
-//  - a wave owns a few weight rows, loads all of its 16-byte chunks up front
-//    (lane l reads chunks l, l+64, ...: 1 KB per wave instruction) through
-//    32-bit buffer offsets, and keeps them in registers for every batch of
-//    the entry's tokens;
-//  - gate/up stages the token rows in LDS; it writes h in a chunk-transposed
-//    row layout so that the down matmul's per-lane activation reads are
-//    coalesced;
-//  - a packed dword w of 8 codes becomes the signed bytes (w << 4) & 0xF0F0F0F0
-//    (even elements) and w & 0xF0F0F0F0 (odd elements), each equal to 16 x
-//    the code; one sign-extending byte-to-float conversion per weight feeds
-//    an fp32 FMA; the 1/16 is folded into the group scale (exact);
-//  - lane partials are combined with a reduce-scatter that applies the same
-//    xor-butterfly (32, 16, 8, 4, 2, 1) to every value, so the sum of a
-//    given (token, row) does not depend on how many values a wave reduces.
+// The matmuls stream every union expert's packed weights once from HBM (a
+// GEMV at decode, a few tokens for a verify batch).  On CDNA4 the dequantise
+// and multiply work is the VALU bottleneck of this stream, so the chunk
+// arithmetic uses only full-rate vector ops:
+//  - a lane owns 16-byte chunks (32 codes) of a row, lane l chunk l + 64 p,
+//    so one wave instruction reads 1 KB of a row;
+//  - a packed dword q of 8 codes gives the biased codes n = code + 8 in
+//    [0, 15] of its even elements as the bytes of (q ^ 0x88888888) &
+//    0x0F0F0F0F and of its odd elements as the bytes of ((q >> 4) ^
+//    0x08080808) & 0x0F0F0F0F (one v_bitop3_b32 each, plus one shift);
+//  - v_cvt_f32_ubyte{0..3} turns a byte into fp32 and v_fmac_f32 accumulates
+//    it times x; the chunk sum starts at -K, K = 8 sum(x), which removes the
+//    bias: sum (code + 8) x - 8 sum x = sum code * x up to fp32 rounding
+//    (every product is exact; for integer x and power-of-two scales the
+//    whole sum is exact);
+//  - one fp16 group scale per chunk, applied with one more FMA;
+//  - lane partials are combined with permlane swaps and DPP (reduce_values),
+//    one fixed pairing sequence for every value, so the sum of a given
+//    (token, row) does not depend on how many values a wave reduces.
 // A token's arithmetic is the same whatever the batch and whichever kernel
 // variant runs it: a token alone and inside a batch give identical bits.
 #include "common.h"
+
+#include <algorithm>
 
 namespace coli {
 
@@ -43,60 +46,151 @@ struct GemvArgs {
     int T, k, cap, n_shared;
 };
 
-constexpr int kRows = 4;  // weight rows a wave computes at a time
-
-// 32 products of one 16-byte chunk (32 int4 codes) with 32 activations,
-// fp32, ascending element order.  Returns 16 x the dot product.
-__device__ __forceinline__ float chunk_dot16(const uint4 wv, const float *xv)
+// K of an activation chunk: 8 sum(v), the sum in ascending element order.
+__device__ __forceinline__ float chunk_K(const float (&v)[32])
 {
-    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-    float acc = 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sum += v[i];
+    return 8.f * sum;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &w, int d)
+{
+    return d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w;
+}
+
+__device__ __forceinline__ float byte_f32(uint32_t v, int b)
+{
+    return (float)((v >> (8 * b)) & 0xFFu);  // v_cvt_f32_ubyte{b}
+}
+
+// out[r][c] = sum_i code_i * x_i over 16-byte chunk w[r][c] of packed codes
+// and activation chunk x[c] (see the file comment): every chain starts at
+// -K[c] and adds its 32 products in ascending element order.  The NR * NC
+// chains are interleaved so that no product waits on the previous one of
+// its own chain.
+template <int NR, int NC>
+__device__ __forceinline__ void chunk_dots(const uint4 (&w)[NR][NC], const float (&x)[NC][32],
+                                           const float (&K)[NC], float (&out)[NR][NC])
+{
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) out[r][c] = -K[c];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = (wd[d] << 4) & 0xF0F0F0F0u;  // 16 x even codes
-        const uint32_t hi = wd[d] & 0xF0F0F0F0u;         // 16 x odd codes
+        uint32_t lo[NR][NC], hi[NR][NC];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            acc = fmaf((float)(int8_t)(lo >> (8 * b)), xv[8 * d + 2 * b], acc);
-            acc = fmaf((float)(int8_t)(hi >> (8 * b)), xv[8 * d + 2 * b + 1], acc);
-        }
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const uint32_t q = word_of(w[r][c], d);
+                lo[r][c] = (q ^ 0x88888888u) & 0x0F0F0F0Fu;         // even elements
+                hi[r][c] = ((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;  // odd elements
+            }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    out[r][c] = fmaf(byte_f32(lo[r][c], b), x[c][8 * d + 2 * b], out[r][c]);
+                    out[r][c] = fmaf(byte_f32(hi[r][c], b), x[c][8 * d + 2 * b + 1], out[r][c]);
+                }
     }
-    return acc;
 }
 
-// Sum of v[i] over the 64 lanes for V values (V a power of two <= 64):
-// halving exchanges over xor 32, 16, ... while more than one value is left,
-// then a plain butterfly.  Every value sees the same pairing tree.  On
-// return, lane l holds the total of value (l >> (6 - log2 V)) in v[0].
-template <int V>
-__device__ __forceinline__ float reduce_scatter(float (&v)[V], int lane)
+// ---------------------------------------------------------------------------
+// Cross-lane reduction.  reduce_values<V> sums each of V per-lane values over
+// the 64 lanes with one fixed pairing sequence: lane bit 5 (v_permlane32_swap),
+// bit 4 (v_permlane16_swap), then DPP row_ror:8 (bit 3), row_half_mirror
+// (lanes l and 7 - l), quad_perm xor 2 and xor 1.  The two swap levels also
+// halve the value count (lanes with the bit set keep the upper half of the
+// values), the DPP levels reduce the n = V / 4 (at least 1) values left in
+// every lane.  The partial sums of a value meet in the same pairs whatever
+// V is, so a (token, row) sum does not depend on how many values a wave
+// reduces.  On return v[j], j < reduced_count(V), holds the total of value
+// reduced_value(V, j, lane) in every lane.
+__device__ __forceinline__ void swap32(float &a, float &b)
 {
-    int off = 32;
-#pragma unroll
-    for (int n = V; n > 1; n >>= 1, off >>= 1) {
-        const bool upper = (lane & off) != 0;
-#pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-            const float send = upper ? v[i] : v[i + n / 2];
-            const float keep = upper ? v[i + n / 2] : v[i];
-            v[i] = keep + __shfl_xor(send, off, 64);
-        }
-    }
-#pragma unroll
-    for (; off >= 1; off >>= 1) v[0] += __shfl_xor(v[0], off, 64);
-    return v[0];
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                   false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
 }
 
-// Value index held by a lane after reduce_scatter<V>.
-template <int V>
-__device__ __forceinline__ int scatter_index(int lane)
+__device__ __forceinline__ void swap16(float &a, float &b)
 {
-    int idx = 0, off = 32;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                   false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int reduced_count(int V) { return V >= 4 ? V / 4 : 1; }
+
+template <int V>
+__device__ __forceinline__ int reduced_value(int j, int lane)
+{
+    const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
+    if (V >= 4) return j + (V / 4) * (b4 + 2 * b5);
+    if (V == 2) return b5;
+    return 0;
+}
+
+template <int V>
+__device__ __forceinline__ void reduce_values(float (&v)[V])
+{
+    static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+    constexpr int N = reduced_count(V);
+    if constexpr (V >= 2) {
 #pragma unroll
-    for (int n = V; n > 1; n >>= 1, off >>= 1) {
-        idx = idx * 2 + ((lane & off) ? 1 : 0);
+        for (int i = 0; i < V / 2; ++i) {
+            float a = v[i], b = v[i + V / 2];
+            swap32(a, b);
+            v[i] = a + b;
+        }
+    } else {
+        float a = v[0], b = v[0];
+        swap32(a, b);
+        v[0] = a + b;
     }
-    return idx;
+    if constexpr (V >= 4) {
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) {
+            float a = v[i], b = v[i + V / 4];
+            swap16(a, b);
+            v[i] = a + b;
+        }
+    } else {
+        float a = v[0], b = v[0];
+        swap16(a, b);
+        v[0] = a + b;
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = dpp_add<0x128>(v[j]);  // row_ror:8
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = dpp_add<0x141>(v[j]);  // row_half_mirror
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = dpp_add<0x4E>(v[j]);   // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = dpp_add<0xB1>(v[j]);   // quad_perm [1,0,3,2]
+}
+
+// The value held by lane l ^ 32 (a gate row's up partner sits V/2 values
+// later, i.e. across lane bit 5).
+__device__ __forceinline__ float across32(float v)
+{
+    float a = v, b = v;
+    swap32(a, b);
+    return (threadIdx.x & 32) ? a : b;
 }
 
 // Entry -> (weights, scales, token list).  Returns the token count.
@@ -134,22 +228,22 @@ __device__ __forceinline__ void token_rows(const GemvArgs &a, const int32_t *lis
 
 // Buffer resource over [p, p + bytes): loads use 32-bit offsets from an
 // SGPR base (no 64-bit address arithmetic per lane); out-of-range reads
-// return 0.
+// return 0 without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0)
 {
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+__device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0)
 {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
 // Position of element i of an h row in the chunk-transposed layout used
@@ -163,8 +257,8 @@ __device__ __forceinline__ int ht_pos(int i, int chunks)
 
 // Marks the packed weights as redefined at this point.  The per-token loops
 // reuse the same packed codes for every token; without this the compiler
-// hoists all the code-to-float conversions out of the loop and keeps
-// hundreds of floats live, which collapses occupancy.  Emits no instruction.
+// hoists all the code-to-fp16 conversions out of the loop and keeps
+// hundreds of values live, which collapses occupancy.  Emits no instruction.
 template <int R, int P>
 __device__ __forceinline__ void opaque_codes(uint4 (&w)[R][P])
 {
@@ -175,14 +269,41 @@ __device__ __forceinline__ void opaque_codes(uint4 (&w)[R][P])
             asm volatile("" : "+v"(w[r][p].x), "+v"(w[r][p].y), "+v"(w[r][p].z), "+v"(w[r][p].w));
 }
 
-// Gate/up matmul + SwiGLU.  Grid: (I / (W * RW / 2), entries).  Wave w of a
-// workgroup owns RW/2 units (gate rows i and up rows I + i), keeps their
-// P chunks per lane in registers for all of the entry's token batches, and
-// stages each batch of NT token rows in LDS.
-template <int NT, int P, int W, int RW, bool ONE>
+// SwiGLU: h = silu(g) * u = g / (1 + e^-g) * u (fp32).
+__device__ __forceinline__ float swiglu(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// Lane that writes reduced value slot j (one lane per value).
+template <int V>
+__device__ __forceinline__ bool value_writer(int j, int lane)
+{
+    if (V >= 4) return (lane & 15) == j;
+    if (V == 2) return (lane & 31) == 0;
+    return lane == 0;
+}
+
+// Load an 8-float4 chunk row segment into 32 registers.
+__device__ __forceinline__ void load_chunk32(const float4 *src, int stride4, float (&v)[32])
+{
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 f = src[q * stride4];
+        v[4 * q + 0] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    }
+}
+
+// Gate/up matmul + SwiGLU, any batch.  Grid: (I / (W * RW / 2), entries).
+// Wave w of a workgroup owns RW/2 units (gate rows i and up rows I + i),
+// keeps their P chunks per lane in registers for all of the entry's token
+// batches, and stages each batch of NT token rows (plus the K of every
+// chunk) in LDS.
+template <int NT, int P, int W, int RW>
 __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
 {
-    extern __shared__ float xs[];  // [NT][K]
+    constexpr int V = RW * NT, N = reduced_count(V);
+    extern __shared__ float xs[];  // [NT][K] token rows, then [NT][K/32] chunk K
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ue = blockIdx.y;
     if (ue < a.cap && ue >= a.n_union[0]) return;
@@ -192,6 +313,7 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
     const int cnt = entry_info(a, ue, wb, sb, list);
     if (cnt <= 0) return;
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, K4 = K / 4;
+    float *ks = xs + NT * K;
     const auto rw = make_rsrc(wb, (uint32_t)(a.N * rb));
     const auto rs = make_rsrc(sb, (uint32_t)(a.N * sbs * 2));
     const int u0 = (blockIdx.x * W + wave) * (RW / 2);
@@ -215,9 +337,8 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
         }
     }
     const int CI = a.I / 32;
-    // ONE: every entry has exactly one token (T == 1): straight-line code
-    for (int t0 = 0; t0 < (ONE ? 1 : cnt); t0 += NT) {
-        const int nt = ONE ? 1 : min(NT, cnt - t0);
+    for (int t0 = 0; t0 < cnt; t0 += NT) {
+        const int nt = min(NT, cnt - t0);
         int in_row[NT], out_row[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) token_rows(a, list, t0 + (tt < nt ? tt : 0), in_row[tt], out_row[tt]);
@@ -228,52 +349,59 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
             for (int i = threadIdx.x; i < K4; i += blockDim.x) dst[i] = src[i];
         }
         __syncthreads();
-        float racc[RW * NT];
+        for (int j = threadIdx.x; j < nt * C; j += blockDim.x) {
+            const int tt = j / C, c = j - tt * C;
+            float v[32];
+            load_chunk32(reinterpret_cast<const float4 *>(xs + tt * K + c * 32), 1, v);
+            ks[tt * C + c] = chunk_K(v);
+        }
+        __syncthreads();
+        float racc[V];
 #pragma unroll
-        for (int i = 0; i < RW * NT; ++i) racc[i] = 0.f;
+        for (int i = 0; i < V; ++i) racc[i] = 0.f;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-            if (!ONE) opaque_codes(wv);  // convert per token: keeps registers low
+            opaque_codes(wv);  // convert per token: keeps registers low
             if (tt < nt) {
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
                     const int c = min(lane + 64 * p, C - 1);
-                    float xv[32];
-                    const float4 *xp = reinterpret_cast<const float4 *>(xs + tt * K + c * 32);
+                    float xv[1][32], kc[1];
+                    load_chunk32(reinterpret_cast<const float4 *>(xs + tt * K + c * 32), 1, xv[0]);
+                    kc[0] = ks[tt * C + c];
+                    uint4 wl[RW][1];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float4 v = xp[q];
-                        xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y;
-                        xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-                    }
+                    for (int r = 0; r < RW; ++r) wl[r][0] = wv[r][p];
+                    float dots[RW][1];
+                    chunk_dots<RW, 1>(wl, xv, kc, dots);
 #pragma unroll
                     for (int r = 0; r < RW; ++r)
-                        racc[r * NT + tt] = fmaf(chunk_dot16(wv[r][p], xv), f16_to_f32(sc[r][p]),
-                                                 racc[r * NT + tt]);
+                        racc[r * NT + tt] = fmaf(dots[r][0], f16_to_f32(sc[r][p]), racc[r * NT + tt]);
                 }
             }
         }
-        // value v = r * NT + tt; the up row of unit r sits RW/2 * NT values
-        // later, i.e. in the lane with bit 5 flipped
-        const float tot = reduce_scatter<RW * NT>(racc, lane) * 0.0625f;
-        const float up = __shfl_xor(tot, 32, 64);
-        const int vi = scatter_index<RW * NT>(lane);
-        const int r = vi / NT, tt = vi % NT;
-        constexpr int LPV = 64 / (RW * NT);
-        if ((lane % LPV) == 0 && r < RW / 2 && tt < nt) {
-            const float g = tot;
-            a.out[(size_t)out_row[tt] * a.out_ld + ht_pos(rows[r], CI)] = g / (1.0f + expf(-g)) * up;
+        // value v = r * NT + tt; the up row of unit r sits V/2 values later
+        reduce_values<V>(racc);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const float up = across32(racc[j]);
+            const int vi = reduced_value<V>(j, lane);
+            const int r = vi / NT, tt = vi % NT;
+            if (value_writer<V>(j, lane) && r < RW / 2 && tt < nt)
+                a.out[(size_t)out_row[tt] * a.out_ld + ht_pos(rows[r], CI)] =
+                    swiglu(racc[j], up);
         }
     }
 }
 
-// Down matmul.  Grid: (H / (W * RW), entries).  Wave w owns RW consecutive
-// rows (P chunks per lane in registers) and walks the entry's tokens; each
-// token's h chunk is read straight from the chunk-transposed h rows
-// (coalesced).  Writes o[row][n].
-template <int P, int W, int RW, bool ONE>
+// Down matmul, any batch.  Grid: (H / (W * RW), entries).  Wave w owns RW
+// consecutive rows (P chunks per lane in registers) and walks the entry's
+// tokens; each token's h chunk is read straight from the chunk-transposed
+// h rows (coalesced).  Writes o[row][n].
+template <int P, int W, int RW>
 __global__ __launch_bounds__(W * 64) void down_f32_kernel(GemvArgs a)
 {
+    constexpr int V = RW, N = reduced_count(V);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ue = blockIdx.y;
     if (ue < a.cap && ue >= a.n_union[0]) return;
@@ -298,32 +426,371 @@ __global__ __launch_bounds__(W * 64) void down_f32_kernel(GemvArgs a)
             sc[r][p] = live ? load2(rs, ((uint32_t)(n0 + r) * sbs + (c >> 1)) * 2) : (uint16_t)0;
         }
     }
-    for (int t = 0; t < (ONE ? 1 : cnt); ++t) {
+    for (int t = 0; t < cnt; ++t) {
         int in_row, out_row;
         token_rows(a, list, t, in_row, out_row);
         const float4 *hrow = reinterpret_cast<const float4 *>(a.in + (size_t)in_row * K);
-        if (!ONE) opaque_codes(wv);
-        float racc[RW];
+        opaque_codes(wv);
+        float racc[V];
 #pragma unroll
         for (int r = 0; r < RW; ++r) racc[r] = 0.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int c = min(lane + 64 * p, C - 1);  // dead lanes have a zero scale
-            float xv[32];
+            float xv[1][32], kc[1];
+            load_chunk32(hrow + c, C, xv[0]);
+            kc[0] = chunk_K(xv[0]);
+            uint4 wl[RW][1];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 v = hrow[q * C + c];
-                xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y;
-                xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-            }
+            for (int r = 0; r < RW; ++r) wl[r][0] = wv[r][p];
+            float dots[RW][1];
+            chunk_dots<RW, 1>(wl, xv, kc, dots);
 #pragma unroll
-            for (int r = 0; r < RW; ++r)
-                racc[r] = fmaf(chunk_dot16(wv[r][p], xv), f16_to_f32(sc[r][p]), racc[r]);
+            for (int r = 0; r < RW; ++r) racc[r] = fmaf(dots[r][0], f16_to_f32(sc[r][p]), racc[r]);
         }
-        const float tot = reduce_scatter<RW>(racc, lane) * 0.0625f;
-        constexpr int LPV = 64 / RW;
-        if ((lane % LPV) == 0) a.out[(size_t)out_row * a.out_ld + n0 + lane / LPV] = tot;
+        reduce_values<V>(racc);
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            if (value_writer<V>(j, lane))
+                a.out[(size_t)out_row * a.out_ld + n0 + reduced_value<V>(j, lane)] = racc[j];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Single-token streaming path (T == 1, the decode step).
+//
+// A decode step reads every union expert's weights exactly once and has no
+// reuse to exploit, so the kernels are built as HBM streams: a fixed grid of
+// persistent waves (a few per SIMD), each walking a contiguous share of one
+// entry's weight rows through a DEPTH-stage register ring.  The loads of
+// stage s + DEPTH are issued as soon as stage s has been consumed, so the
+// dequantising FMAs of one stage overlap the HBM latency of the next ones
+// inside every wave; the partial sums of M stages are reduced together.
+//
+// Stage loads: a row's chunk p of lane l sits at voffset (l + 64 p) * 16
+// (precomputed per lane) plus the row's byte offset in the scalar soffset,
+// so a stage costs no vector address arithmetic.  Every load is issued
+// unconditionally (branches around loads make the compiler's wait-count
+// analysis fall back to waiting for everything in flight): lanes past the
+// row's last chunk get a voffset beyond the buffer, and stages past the end
+// of a wave's work use a zero-size buffer resource; both read 0 without
+// touching memory.
+constexpr uint32_t kOOB = 0x40000000u;
+
+struct StageRsrc {
+    __amdgpu_buffer_rsrc_t w, s, w0, s0;  // weights, scales, and their empty twins
+};
+
+__device__ __forceinline__ StageRsrc stage_rsrc(const uint8_t *wb, const uint16_t *sb, int N,
+                                                int rb, int sbs)
+{
+    StageRsrc R;
+    R.w = make_rsrc(wb, (uint32_t)(N * rb));
+    R.s = make_rsrc(sb, (uint32_t)(N * sbs * 2));
+    R.w0 = make_rsrc(wb, 0);
+    R.s0 = make_rsrc(sb, 0);
+    return R;
+}
+
+template <int NR, int P>
+__device__ __forceinline__ void load_stage(const StageRsrc &R, const int (&rows)[NR], bool valid,
+                                           int rb, int sbs, const uint32_t (&vw)[P],
+                                           const uint32_t (&vs)[P], uint4 (&w)[NR][P],
+                                           uint16_t (&s)[NR][P])
+{
+    const __amdgpu_buffer_rsrc_t rw = valid ? R.w : R.w0, rs = valid ? R.s : R.s0;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            w[r][p] = load16(rw, vw[p], (uint32_t)rows[r] * rb);
+            s[r][p] = load2(rs, vs[p], (uint32_t)rows[r] * sbs * 2);
+        }
+}
+
+template <int P>
+__device__ __forceinline__ void lane_offsets(int lane, int C, uint32_t (&vw)[P], uint32_t (&vs)[P])
+{
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int c = lane + 64 * p;
+        vw[p] = c < C ? (uint32_t)c * 16 : kOOB;
+        vs[p] = c < C ? (uint32_t)(c >> 1) * 2 : kOOB;
+    }
+}
+
+// Entry ue of the compact entry list (union experts in union order, then the
+// shared expert): weight and scale bases and the output row of its token.
+__device__ __forceinline__ void t1_entry(const GemvArgs &a, int ue, int U, const uint8_t *&wb,
+                                         const uint16_t *&sb, int &out_row)
+{
+    if (ue < U) {
+        const int e = a.union_ids[ue];
+        wb = a.w + (size_t)e * a.N * (a.K / 2);
+        sb = a.s + (size_t)e * a.N * (a.K / 64);
+        out_row = a.slots[a.offsets[ue]];
+    } else {
+        wb = a.sh_w;
+        sb = a.sh_s;
+        out_row = a.T * a.k;
+    }
+}
+
+constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2); }
+
+// Work split of one token's streaming kernels: the wpe = waves / entries
+// waves of an entry take its row blocks round-robin (wave part p: blocks
+// p, p + wpe, ...), so at any moment an entry's waves read one contiguous
+// stretch of rows (DRAM page locality) while every wave stays inside one
+// entry (its activation chunk is loaded once).
+struct T1Split {
+    int ue, part, wpe, nsteps;
+};
+
+__device__ __forceinline__ T1Split t1_split(int gw, int GW, int ne, int nblocks)
+{
+    T1Split s;
+    s.wpe = ne > 0 ? GW / ne : 0;
+    const bool has = s.wpe > 0 && gw < ne * s.wpe;
+    s.ue = has ? gw / s.wpe : 0;
+    s.part = has ? gw - s.ue * s.wpe : 0;
+    s.nsteps = has && s.part < nblocks ? (nblocks - s.part + s.wpe - 1) / s.wpe : 0;
+    return s;
+}
+
+// Gate/up + SwiGLU for one token.  Unit (row block) = NP gate rows i and
+// their up rows I + i.  Each lane reads the x chunks it needs once (staged
+// through LDS) and keeps them in registers (XREG) or re-reads them from LDS
+// every stage.  h is written chunk-transposed.
+template <int P, int NP, int M, int DEPTH, bool XREG>
+__global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
+{
+    static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
+    constexpr int V = next_pow2(2 * NP * M), N = reduced_count(V);
+    static_assert(V <= 64, "at most 64 values per reduction");
+    extern __shared__ float xs[];  // [K] x, then [K/32] chunk K
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
+    const int U = a.n_union[0];
+    const int upe = a.I / NP;
+    const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, upe);
+    const int nsteps = sp.nsteps;
+    const uint8_t *wb;
+    const uint16_t *sb;
+    int orow;
+    t1_entry(a, sp.ue, U, wb, sb, orow);
+    const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
+    uint32_t vw[P], vs[P];
+    lane_offsets<P>(lane, C, vw, vs);
+
+    uint4 wv[DEPTH][2 * NP][P];
+    uint16_t sv[DEPTH][2 * NP][P];
+    auto issue = [&](int d, int step) {
+        const int blk = sp.part + step * sp.wpe;
+        int rows[2 * NP];
+#pragma unroll
+        for (int r = 0; r < NP; ++r) {
+            rows[r] = blk * NP + r;
+            rows[NP + r] = a.I + blk * NP + r;
+        }
+        load_stage<2 * NP, P>(R, rows, step < nsteps, rb, sbs, vw, vs, wv[d], sv[d]);
+    };
+    // the first stages go out before x is staged: one memory latency, not two
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, d);
+    float *ks = xs + K;
+    {
+        const float4 *src = reinterpret_cast<const float4 *>(a.in);
+        float4 *dst = reinterpret_cast<float4 *>(xs);
+        for (int i = threadIdx.x; i < K / 4; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+        for (int c = threadIdx.x; c < C; c += blockDim.x) {
+            float v[32];
+            load_chunk32(reinterpret_cast<const float4 *>(xs + c * 32), 1, v);
+            ks[c] = chunk_K(v);
+        }
+        __syncthreads();
+    }
+    if (nsteps == 0) return;
+    float *hrow = a.out + (size_t)orow * a.out_ld;
+    float xr[XREG ? P : 1][32], kx[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int c = min(lane + 64 * p, C - 1);  // dead lanes: scale 0
+        if constexpr (XREG) load_chunk32(reinterpret_cast<const float4 *>(xs + c * 32), 1, xr[p]);
+        kx[p] = ks[c];
+    }
+
+    for (int g0 = 0; g0 < nsteps; g0 += M) {
+        float racc[V];  // [gate, up][m][NP], zero padded to a power of two
+#pragma unroll
+        for (int i = 0; i < V; ++i) racc[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int d = m % DEPTH;
+            if (g0 + m < nsteps) {
+                float dots[2 * NP][P];
+                if constexpr (XREG) {
+                    chunk_dots<2 * NP, P>(wv[d], xr, kx, dots);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        float xl[1][32], kl[1] = {kx[p]};
+                        load_chunk32(reinterpret_cast<const float4 *>(xs + min(lane + 64 * p, C - 1) * 32), 1, xl[0]);
+                        uint4 wl[2 * NP][1];
+                        float dl[2 * NP][1];
+#pragma unroll
+                        for (int r = 0; r < 2 * NP; ++r) wl[r][0] = wv[d][r][p];
+                        chunk_dots<2 * NP, 1>(wl, xl, kl, dl);
+#pragma unroll
+                        for (int r = 0; r < 2 * NP; ++r) dots[r][p] = dl[r][0];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 2 * NP; ++r) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc = fmaf(dots[r][p], f16_to_f32(sv[d][r][p]), acc);
+                    racc[(r / NP) * (V / 2) + m * NP + r % NP] = acc;
+                }
+            }
+            issue(d, g0 + m + DEPTH);
+        }
+        reduce_values<V>(racc);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const float up = across32(racc[j]);
+            const int vi = reduced_value<V>(j, lane);
+            const int m = vi / NP, i = (sp.part + (g0 + m) * sp.wpe) * NP + vi % NP;
+            if (value_writer<V>(j, lane) && vi < NP * M && g0 + m < nsteps)
+                hrow[ht_pos(i, CI)] = swiglu(racc[j], up);
+        }
+    }
+}
+
+// Down projection for one token.  Unit (row block) = RD rows of one entry.
+// A wave loads its entry's h chunk once and keeps it in registers
+// while it streams its row blocks.
+template <int P, int RD, int M, int DEPTH>
+__global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
+{
+    static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
+    constexpr int V = next_pow2(RD * M), N = reduced_count(V);
+    static_assert(V <= 64, "at most 64 values per reduction");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32;
+    const int U = a.n_union[0];
+    const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, a.N / RD);
+    const int nsteps = sp.nsteps;
+    if (nsteps == 0) return;
+    const uint8_t *wb;
+    const uint16_t *sb;
+    int orow;
+    t1_entry(a, sp.ue, U, wb, sb, orow);
+    const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
+    uint32_t vw[P], vs[P];
+    lane_offsets<P>(lane, C, vw, vs);
+
+    // this lane's h chunks (chunk-transposed rows: piece q of chunk
+    // c at q*C + c), loaded before the weight ring so the first wait covers them
+    float hv[P][32], kh[P];
+    {
+        const float4 *hrow = reinterpret_cast<const float4 *>(a.in + (size_t)orow * K);
+#pragma unroll
+        for (int p = 0; p < P; ++p) load_chunk32(hrow + min(lane + 64 * p, C - 1), C, hv[p]);
+    }
+    uint4 wv[DEPTH][RD][P];
+    uint16_t sv[DEPTH][RD][P];
+    auto issue = [&](int d, int step) {
+        int rows[RD];
+#pragma unroll
+        for (int r = 0; r < RD; ++r) rows[r] = (sp.part + step * sp.wpe) * RD + r;
+        load_stage<RD, P>(R, rows, step < nsteps, rb, sbs, vw, vs, wv[d], sv[d]);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, d);
+#pragma unroll
+    for (int p = 0; p < P; ++p) kh[p] = chunk_K(hv[p]);
+    float *orow_p = a.out + (size_t)orow * a.out_ld;
+    for (int g0 = 0; g0 < nsteps; g0 += M) {
+        float racc[V];  // [m][RD], zero padded to a power of two
+#pragma unroll
+        for (int i = 0; i < V; ++i) racc[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int d = m % DEPTH;
+            if (g0 + m < nsteps) {
+                float dots[RD][P];
+                chunk_dots<RD, P>(wv[d], hv, kh, dots);
+#pragma unroll
+                for (int r = 0; r < RD; ++r) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc = fmaf(dots[r][p], f16_to_f32(sv[d][r][p]), acc);
+                    racc[m * RD + r] = acc;
+                }
+            }
+            issue(d, g0 + m + DEPTH);
+        }
+        reduce_values<V>(racc);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int vi = reduced_value<V>(j, lane), m = vi / RD;
+            if (value_writer<V>(j, lane) && vi < RD * M && g0 + m < nsteps)
+                orow_p[(sp.part + (g0 + m) * sp.wpe) * RD + vi % RD] = racc[j];
+        }
+    }
+}
+
+// T == 1: the streaming kernels.  Launch shapes measured on MI355X with the
+// decode layer (H 6144, I 2048, 9 entries): gate/up runs one 4-wave
+// workgroup per CU (its register ring plus the x chunks allow two waves per
+// SIMD, and more waves lose DRAM locality), down runs four per CU.
+static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs a, float *h,
+                                float *o, hipStream_t st, Marks *mk)
+{
+    const int entries = a.cap + a.n_shared;
+    const int cus = device_cu_count();
+    if (mk) mk->mark(st);
+    {
+        constexpr int NP = 1, M = 8, DEPTH = 2;
+        a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
+        a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
+        a.in = io.x; a.in_by_slot = 0;
+        a.out = h; a.out_ld = L.I;
+        const int P = (L.H / 32 + 63) / 64;
+        const int units = entries * (L.I / NP);
+        const dim3 grid(std::min(cus, (units + 3) / 4)), block(256);
+        const size_t lds = (size_t)(L.H + L.H / 32) * 4;
+#define COLI_GU1(P_) \
+        if (P == P_) hipLaunchKernelGGL((gateup_t1_kernel<P_, NP, M, DEPTH, true>), grid, block, lds, st, a);
+        COLI_GU1(1) COLI_GU1(2) COLI_GU1(3) COLI_GU1(4)
+#undef COLI_GU1
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (mk) mk->mark(st);
+    {
+        constexpr int RD = 4, M = 4, DEPTH = 2;
+        a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
+        a.N = L.H; a.K = L.I; a.upe = L.H;
+        a.in = h; a.in_by_slot = 1;
+        a.out = o; a.out_ld = L.H;
+        const int P = (L.I / 32 + 63) / 64;
+        const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
+#define COLI_DN1(P_) \
+        if (P == P_) hipLaunchKernelGGL((down_t1_kernel<P_, RD, M, DEPTH>), grid, block, 0, st, a);
+        COLI_DN1(1) COLI_DN1(2) COLI_DN1(3) COLI_DN1(4)
+#undef COLI_DN1
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (mk) mk->mark(st);
+    hipError_t err = launch_combine(o, io.w, io.T, L.k, L.H, L.n_shared, io.y, st);
+    if (mk) mk->mark(st);
+    return err;
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk)
@@ -337,6 +804,7 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     a.T = T; a.k = L.k; a.cap = (int)io.lay.cap; a.n_shared = L.n_shared;
     a.I = L.I;
     const int entries = a.cap + a.n_shared;
+    if (T == 1) return launch_f32_t1(L, io, a, h, o, st, mk);
     // gate/up + SwiGLU -> h (chunk-transposed rows)
     a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
     a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
@@ -346,16 +814,15 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     {
         constexpr int W = 4, RW = 4;
         const int P = (L.H / 32 + 63) / 64;
-        int nt = 65536 / (L.H * 4);  // staged token rows must fit 64 KB of LDS
+        // staged token rows and their chunk constants must fit 64 KB of LDS
+        int nt = 65536 / ((L.H + L.H / 32) * 4);
         nt = T < nt ? T : nt;
         nt = nt >= 2 ? 2 : 1;
         const dim3 grid(L.I / (W * RW / 2), entries), block(W * 64);
-        const size_t lds = (size_t)nt * L.H * 4;
-        const bool one = T == 1;
+        const size_t lds = (size_t)nt * (L.H + L.H / 32) * 4;
 #define COLI_GU(NT_, P_) \
-        if (nt == NT_ && P == P_) { \
-            if (one) hipLaunchKernelGGL((gateup_f32_kernel<NT_, P_, W, RW, true>), grid, block, lds, st, a); \
-            else hipLaunchKernelGGL((gateup_f32_kernel<NT_, P_, W, RW, false>), grid, block, lds, st, a); }
+        if (nt == NT_ && P == P_) \
+            hipLaunchKernelGGL((gateup_f32_kernel<NT_, P_, W, RW>), grid, block, lds, st, a);
         COLI_GU(1, 1) COLI_GU(1, 2) COLI_GU(1, 3) COLI_GU(1, 4)
         COLI_GU(2, 1) COLI_GU(2, 2) COLI_GU(2, 3) COLI_GU(2, 4)
 #undef COLI_GU
@@ -372,11 +839,8 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
         constexpr int W = 4, RW = 8;
         const int P = (L.I / 32 + 63) / 64;
         const dim3 grid(L.H / (W * RW), entries), block(W * 64);
-        const bool one = T == 1;
 #define COLI_DN(P_) \
-        if (P == P_) { \
-            if (one) hipLaunchKernelGGL((down_f32_kernel<P_, W, RW, true>), grid, block, 0, st, a); \
-            else hipLaunchKernelGGL((down_f32_kernel<P_, W, RW, false>), grid, block, 0, st, a); }
+        if (P == P_) hipLaunchKernelGGL((down_f32_kernel<P_, W, RW>), grid, block, 0, st, a);
         COLI_DN(1) COLI_DN(2) COLI_DN(3) COLI_DN(4)
 #undef COLI_DN
         hipError_t err = hipGetLastError();
