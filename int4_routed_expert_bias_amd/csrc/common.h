@@ -75,7 +75,7 @@ struct Workspace {
     int64_t max_tiles;
 };
 
-constexpr int kTileM = 16;  // token rows per integer-GEMM tile
+constexpr int kTileM = 64;  // token rows per integer-GEMM tile
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 

@@ -6,7 +6,7 @@
 //  quant:    per token per 64-group, scale = amax / 127 (IEEE divide),
 //            q = clamp(rint(v / scale), -127, 127); codes are stored in the
 //            permuted order [0,2,4,6,1,3,5,7] inside every 8-element block.
-//  schedule: one thread per union expert turns its slot count into 16-row
+//  schedule: one thread per union expert turns its slot count into 64-row
 //            tiles (device side: the union size never leaves the GPU).
 //  gemm:     v_mfma_i32_16x16x64_i8, one MFMA per 64-group, so the exact
 //            int32 group accumulator comes straight out of the matrix core.
@@ -16,9 +16,16 @@
 //            the code, so the MFMA yields 16 x acc exactly (|16 acc| < 2^21)
 //            and the activation layout above matches that byte order.
 //            Epilogue per group: out += float(acc) * act_scale * w_scale.
-//  gate/up:  each wave owns 64 gate rows and the matching 64 up rows, so the
-//            SwiGLU and the int8 quantisation of h (one 64-group) stay in
-//            registers; the down GEMM reads the quantised h.
+//            The epilogue's three VALU ops per output and group (convert,
+//            multiply, FMA) cost more issue cycles than the MFMA itself, so
+//            the kernel is built to keep the VALU fed: whole-row coalesced
+//            staging loads that are only waited for after the compute, an
+//            LDS double buffer, and each group's MFMAs issued before its
+//            epilogue.
+//  gate/up:  the SwiGLU pairs (gate row i, up row I + i) sit in the same
+//            lane and register, and the int8 quantisation of h (per 64-group
+//            of i) finishes in the epilogue; the down GEMM reads the
+//            quantised h.
 #include "common.h"
 
 namespace coli {
@@ -55,7 +62,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict
 // tiles[i] = (entry, first row) for i < count; count stored at tiles[max].x
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ offsets,
                                                         const int32_t *__restrict__ n_union,
-                                                        int cap, int T, int n_shared,
+                                                        int cap, int T, int n_shared, int tile_m,
                                                         int2 *__restrict__ tiles, int max_tiles)
 {
     __shared__ int32_t cnt[COLI_MAX_E_DEV + 1];
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
         } else {
             n = T;
         }
-        cnt[e] = (n + kTileM - 1) / kTileM;
+        cnt[e] = (n + tile_m - 1) / tile_m;
     }
     __syncthreads();
     if (tid < 64) {
@@ -93,12 +100,44 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
     __syncthreads();
     for (int e = tid; e < nent; e += blockDim.x) {
         int32_t b = scan[e];
-        for (int m = 0; m < cnt[e]; ++m) tiles[b + m] = make_int2(e, m * kTileM);
+        for (int m = 0; m < cnt[e] && b + m < max_tiles; ++m) tiles[b + m] = make_int2(e, m * tile_m);
     }
     if (tid == 0) tiles[max_tiles] = make_int2(min(scan[nent], max_tiles), 0);
 }
 
-// --- shared tile bookkeeping ---------------------------------------------
+// --- grouped GEMM ----------------------------------------------------------
+// One workgroup computes a BM x kBN output tile of one union entry: BM of
+// the entry's token rows (a tile from the schedule) against kBN weight rows
+// (gate/up: 64 gate rows i0.. and the 64 matching up rows I + i0..; down:
+// 128 output rows n0..).  The K loop walks kKG 64-groups per step through a
+// double-buffered LDS stage: the next step's activation codes, packed
+// weights and scales are loaded into registers while the current step
+// computes, then written to the other buffer.
+//
+// Four waves as 2 (rows) x 2 (columns): wave (wm, wn) owns BM/2 rows
+// (MT = BM/32 m-tiles of 16) and 64 columns (4 n-tiles of 16): gate/up:
+// gate rows i0 + 32 wn.. and their up rows, so SwiGLU pairs sit in the same
+// lane and register; down: rows n0 + 64 wn...  Per 64-group an m-tile x
+// n-tile pair is one v_mfma_i32_16x16x64_i8 whose result is the exact group
+// accumulator (times 16, from the unpacked codes); the epilogue adds
+// acc * sx * (sw / 16) into fp32 (cvt, mul, fma: the 1/16 is folded into
+// the weight scale, exactly).  Each A fragment read from LDS feeds 4 MFMAs
+// and each B fragment MT, which keeps LDS traffic under its bandwidth.
+constexpr int kBN = 128;
+
+// LDS of one workgroup: two stages of KG groups (row strides padded by 16
+// bytes, which keeps the fragment reads free of bank conflicts).
+template <int BM, int KG>
+struct __attribute__((aligned(16))) GemmLds {
+    static constexpr int AS = KG * 64 + 16;  // activation row stride (bytes)
+    static constexpr int BS = KG * 32 + 16;  // packed weight row stride (bytes)
+    alignas(16) uint8_t a[2][BM * AS];
+    alignas(16) uint8_t b[2][kBN * BS];
+    alignas(16) float sx[2][KG][BM];
+    alignas(16) float sw[2][KG][kBN];  // weight scale / 16
+    alignas(16) float amax[2][BM];
+};
+
 struct I8Args {
     const int8_t *qin;        // activation codes (permuted) [rows][K]
     const float *sin;         // activation scales [rows][K/64]
@@ -127,208 +166,335 @@ __device__ __forceinline__ v4i unpack_b(uint2 w)
     return r;
 }
 
-// Resolve the tile: entry, weight base, rows.  Returns false if past count.
-__device__ __forceinline__ bool tile_rows(const I8Args &a, int tile, int lane_m, int &mt,
-                                          int &in_row, int &out_row, const uint8_t *&wb,
-                                          const uint16_t *&sb)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_i8(const void *p, uint32_t bytes)
 {
-    const int count = a.tiles[a.max_tiles].x;
-    if (tile >= count) return false;
-    const int2 td = a.tiles[tile];
-    const int ue = td.x, m0 = td.y;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+constexpr uint32_t kOOB8 = 0x80000000u;  // beyond any buffer: reads 0
+
+// Tile of the schedule: entry, first row and row count.
+struct TileInfo {
+    int ue, m0, rows;
+    bool routed;
+    int o0;  // routed: first position in slots
+};
+
+// Input and output rows of tile row m (rows past the tile repeat its last).
+__device__ __forceinline__ void tile_row(const I8Args &a, const TileInfo &ti, int m, int &in_row,
+                                         int &out_row)
+{
     const int TK = a.T * a.k;
-    if (ue < a.cap) {
-        const int e = a.union_ids[ue];
-        const int o0 = a.offsets[ue];
-        const int n = a.offsets[ue + 1] - o0;
-        mt = min(kTileM, n - m0);
-        wb = a.w + (size_t)e * a.N * (a.K / 2);
-        sb = a.s + (size_t)e * a.N * (a.K / 64);
-        const int m = min(lane_m, mt - 1);
-        const int sl = a.slots[o0 + m0 + m];
+    const int mm = min(m, ti.rows - 1);
+    if (ti.routed) {
+        const int sl = a.slots[ti.o0 + ti.m0 + mm];
         out_row = sl;
         in_row = a.in_by_slot ? sl : sl / a.k;
     } else {
-        mt = min(kTileM, a.T - m0);
-        wb = a.sh_w;
-        sb = a.sh_s;
-        const int t = m0 + min(lane_m, mt - 1);
+        const int t = ti.m0 + mm;
         out_row = TK + t;
         in_row = a.in_by_slot ? TK + t : t;
     }
-    return true;
 }
 
-// --- gate/up GEMM + SwiGLU + quantisation of h ---------------------------
-// grid: (ceil(I / 256), max_tiles); 4 waves, wave w owns i in [i0, i0 + 64)
-__global__ __launch_bounds__(256) void ggemm_gateup_kernel(I8Args a)
+template <int BM, int KG, bool GATEUP, bool DUMP>
+__global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int MT = BM / 32;               // m-tiles per wave
+    constexpr int kKG = KG;
+    using Lds = GemmLds<BM, KG>;
+    constexpr int kAS = Lds::AS, kBS = Lds::BS;
+    __shared__ Lds sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
     const int n = lane & 15, q = lane >> 4;
-    const int i0 = (blockIdx.x * 4 + wave) * 64;
-    if (i0 >= a.I) return;
-    int mt, a_in, a_out;
+    const int count = a.tiles[a.max_tiles].x;
+    if ((int)blockIdx.y >= count) return;
+    const int2 td = a.tiles[blockIdx.y];
+    TileInfo ti;
+    ti.ue = td.x;
+    ti.m0 = td.y;
+    ti.routed = ti.ue < a.cap;
     const uint8_t *wb;
     const uint16_t *sb;
-    // A-operand row (token m = lane & 15)
-    if (!tile_rows(a, blockIdx.y, n, mt, a_in, a_out, wb, sb)) return;
-    const bool a_valid = n < mt;
-    // C rows owned by this lane: m = 4q + i
-    int c_in[4], c_out[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int mt2, wi, wo;
-        const uint8_t *wb2;
-        const uint16_t *sb2;
-        tile_rows(a, blockIdx.y, 4 * q + i, mt2, wi, wo, wb2, sb2);
-        c_in[i] = wi;
-        c_out[i] = wo;
+    if (ti.routed) {
+        const int e = a.union_ids[ti.ue];
+        ti.o0 = a.offsets[ti.ue];
+        ti.rows = min(BM, a.offsets[ti.ue + 1] - ti.o0 - ti.m0);
+        wb = a.w + (size_t)e * a.N * (a.K / 2);
+        sb = a.s + (size_t)e * a.N * (a.K / 64);
+    } else {
+        ti.o0 = 0;
+        ti.rows = min(BM, a.T - ti.m0);
+        wb = a.sh_w;
+        sb = a.sh_s;
     }
     const int K = a.K, G = K / 64, rb = K / 2;
-    const int8_t *arow = a.qin + (size_t)a_in * K + 16 * q;
-    const uint8_t *brow[8];
-    const uint16_t *srow[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int r = (b < 4) ? (i0 + 16 * b + n) : (a.I + i0 + 16 * (b - 4) + n);
-        brow[b] = wb + (size_t)r * rb + 8 * q;
-        srow[b] = sb + (size_t)r * G;
-    }
-    float out[8][4];
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[b][i] = 0.f;
-    const v4i zero = {0, 0, 0, 0};
+    const int nb0 = blockIdx.x * (GATEUP ? kBN / 2 : kBN);  // first unit / row of the block
+    // weight row of local LDS row r (-1: past the matrix)
+    auto wrow = [&](int r) -> int {
+        int row, lim;
+        if (GATEUP) {
+            row = (r < kBN / 2) ? nb0 + r : a.I + nb0 + (r - kBN / 2);
+            lim = (r < kBN / 2) ? a.I : 2 * a.I;
+        } else {
+            row = nb0 + r;
+            lim = a.N;
+        }
+        return row < lim ? row : -1;
+    };
+    const auto rB = rsrc_i8(wb, (uint32_t)((size_t)a.N * rb));
+    const auto rS = rsrc_i8(sb, (uint32_t)((size_t)a.N * G * 2));
 
-    for (int g = 0; g < G; ++g) {
-        v4i av = zero;
-        if (a_valid) av = *reinterpret_cast<const v4i *>(arow + 64 * g);
-        float sx[4];
+    // staging assignment (fixed for the tile).  A step holds KG * 64 bytes of
+    // every activation row and KG * 32 bytes of every weight row; lanes are
+    // laid out so that one load instruction of a wave reads whole row
+    // segments (LA lanes x 16 B per activation row, LB per weight row).
+    constexpr int LA = 4 * KG, LB = 2 * KG;
+    constexpr int NA = BM * LA / 256;           // activation loads per thread
+    constexpr int NB = kBN * LB / 256;          // weight loads per thread
+    const int a_byte = (tid % LA) * 16;         // byte within the row segment
+    int a_in[NA];
+    bool a_ok[NA];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sx[i] = a.sin[(size_t)c_in[i] * G + g];
+    for (int i = 0; i < NA; ++i) {
+        const int m = tid / LA + (256 / LA) * i;
+        int o_;
+        tile_row(a, ti, m, a_in[i], o_);
+        a_ok[i] = m < ti.rows;
+    }
+    const int b_byte = (tid % LB) * 16;
+    int b_row[NB];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint2 wv = *reinterpret_cast<const uint2 *>(brow[b] + 32 * g);
-            const v4i bv = unpack_b(wv);
-            const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, zero, 0, 0, 0);
-            const float sw = f16_to_f32(srow[b][g]);
+    for (int i = 0; i < NB; ++i) b_row[i] = wrow(tid / LB + (256 / LB) * i);
+    int x_in = 0, x_out;
+    if (tid < BM) tile_row(a, ti, tid, x_in, x_out);
+    const bool x_ok = tid < BM && tid < ti.rows;
+    const int s_row = tid < kBN ? wrow(tid) : -1;
+
+    const int nsteps = (G + kKG - 1) / kKG;
+    // load_step only issues loads (raw values land in registers while the
+    // current step computes); store_step masks, converts and writes them to
+    // LDS after the compute, so no load is waited for before it is needed
+    uint4 ra[NA], rbw[NB];
+    float rx[kKG];
+    uint32_t rs_[kKG];
+    auto load_step = [&](int ks) {
+        const int g0 = ks * kKG;
+        const int ga = g0 + a_byte / 64, gb = g0 + b_byte / 32;
+        // activation rows can exceed a 32-bit buffer range: 64-bit addresses;
+        // rows and groups past the tile read row 0 and are zeroed later
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const bool ok = a_ok[i] && ga < G;
+            ra[i] = *reinterpret_cast<const uint4 *>(
+                a.qin + (ok ? (size_t)a_in[i] * K + g0 * 64 + a_byte : 0));
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const uint32_t off = (b_row[i] >= 0 && gb < G)
+                ? (uint32_t)((size_t)b_row[i] * rb + g0 * 32 + b_byte) : kOOB8;
+            rbw[i] = ld16(rB, off);
+        }
+        // scales: every thread issues the same loads (no branches around
+        // loads); threads without a row read an out-of-range offset
+#pragma unroll
+        for (int j = 0; j < kKG; ++j) {
+            const int g = g0 + j;
+            rx[j] = a.sin[(x_ok && g < G) ? (size_t)x_in * G + g : 0];
+            const uint32_t so = (s_row >= 0 && g < G) ? (uint32_t)((size_t)s_row * G + g) * 2 : kOOB8;
+            rs_[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, so, 0, 0);
+        }
+    };
+    auto store_step = [&](int buf, int ks) {
+        const int g0 = ks * kKG;
+        const int ga = g0 + a_byte / 64;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            // zero by mask, component-wise (a select of whole vectors gets
+            // lowered through scratch memory)
+            const uint32_t m = (a_ok[i] && ga < G) ? 0xFFFFFFFFu : 0u;
+            const uint4 v = ra[i];
+            *reinterpret_cast<uint4 *>(sm.a[buf] + (tid / LA + (256 / LA) * i) * kAS + a_byte) =
+                make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            *reinterpret_cast<uint4 *>(sm.b[buf] + (tid / LB + (256 / LB) * i) * kBS + b_byte) = rbw[i];
+#pragma unroll
+        for (int j = 0; j < kKG; ++j) {
+            const int g = g0 + j;
+            if (tid < BM) sm.sx[buf][j][tid] = (x_ok && g < G) ? rx[j] : 0.f;
+            if (tid < kBN) sm.sw[buf][j][tid] = f16_to_f32((uint16_t)rs_[j]) * 0.0625f;
+        }
+    };
+
+    // this wave's local rows: A rows wm * BM/2 + 16 mt + n, B rows lb[nt] + n
+    int lb[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+        lb[nt] = GATEUP ? ((nt < 2) ? 32 * wn + 16 * nt : kBN / 2 + 32 * wn + 16 * (nt - 2))
+                        : 64 * wn + 16 * nt;
+    const int arow0 = wm * (BM / 2);
+    // a wave whose half of the tile holds no row skips its MFMAs (one
+    // uniform branch per group keeps the MFMA/epilogue block in one piece)
+    const bool wave_live = arow0 < ti.rows;
+    float out[MT][4][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[mt][nt][i] = 0.f;
+    // dump bookkeeping (tests only)
+    int d_out[MT][4], d_row[4];
+    if constexpr (DUMP) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int iacc = acc[i] >> 4;
-                if (a.dump_acc && 4 * q + i < mt) {
-                    const int r = (b < 4) ? (i0 + 16 * b + n) : (a.I + i0 + 16 * (b - 4) + n);
-                    a.dump_acc[((size_t)c_out[i] * a.N + r) * G + g] = iacc;
-                }
-                const float p = (float)iacc * sx[i];
-                out[b][i] = fmaf(p, sw, out[b][i]);
+                int ir;
+                tile_row(a, ti, arow0 + mt * 16 + 4 * q + i, ir, d_out[mt][i]);
             }
-        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) d_row[nt] = wrow(lb[nt] + n);
     }
 
-    // SwiGLU and int8 quantisation of the 64-wide h group [i0, i0 + 64)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float hv[4];
-        float amax = 0.f;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float gg = out[b][i], uu = out[b + 4][i];
-            hv[b] = gg / (1.0f + expf(-gg)) * uu;
-            amax = fmaxf(amax, fabsf(hv[b]));
-        }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-        const bool valid = 4 * q + i < mt;
-        float sc = 0.f;
-        if (amax > 0.f) sc = amax / 127.0f;
-        if (valid) {
-            int8_t *qrow = a.qh + (size_t)c_out[i] * a.I;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int col = i0 + 16 * b + n;
-                int8_t code = 0;
-                if (amax > 0.f) {
-                    float r = rintf(hv[b] / sc);
-                    r = fminf(fmaxf(r, -127.f), 127.f);
-                    code = (int8_t)r;
-                }
-                qrow[perm8_pos(col)] = code;
-                if (a.dump_qh) a.dump_qh[(size_t)c_out[i] * a.I + col] = code;
-            }
-            if (n == 0) {
-                a.sh[(size_t)c_out[i] * (a.I / 64) + i0 / 64] = sc;
-                if (a.dump_sh) a.dump_sh[(size_t)c_out[i] * (a.I / 64) + i0 / 64] = sc;
-            }
-        }
-    }
-}
-
-// --- down GEMM -------------------------------------------------------------
-// grid: (ceil(H / 256), max_tiles); wave w owns rows [n0, n0 + 64)
-__global__ __launch_bounds__(256) void ggemm_down_kernel(I8Args a)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = lane & 15, q = lane >> 4;
-    const int n0 = (blockIdx.x * 4 + wave) * 64;
-    if (n0 >= a.N) return;
-    int mt, a_in, a_out;
-    const uint8_t *wb;
-    const uint16_t *sb;
-    if (!tile_rows(a, blockIdx.y, n, mt, a_in, a_out, wb, sb)) return;
-    const bool a_valid = n < mt;
-    int c_in[4], c_out[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int mt2, wi, wo;
-        const uint8_t *wb2;
-        const uint16_t *sb2;
-        tile_rows(a, blockIdx.y, 4 * q + i, mt2, wi, wo, wb2, sb2);
-        c_in[i] = wi;
-        c_out[i] = wo;
-    }
-    const int K = a.K, G = K / 64, rb = K / 2;
-    const int8_t *arow = a.qin + (size_t)a_in * K + 16 * q;
-    const uint8_t *brow[4];
-    const uint16_t *srow[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int r = n0 + 16 * b + n;
-        brow[b] = wb + (size_t)r * rb + 8 * q;
-        srow[b] = sb + (size_t)r * G;
-    }
-    float out[4][4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[b][i] = 0.f;
+    load_step(0);
+    store_step(0, 0);
+    __syncthreads();
     const v4i zero = {0, 0, 0, 0};
-    for (int g = 0; g < G; ++g) {
-        v4i av = zero;
-        if (a_valid) av = *reinterpret_cast<const v4i *>(arow + 64 * g);
-        float sx[4];
+    for (int ks = 0; ks < nsteps; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nsteps) load_step(ks + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sx[i] = a.sin[(size_t)c_in[i] * G + g];
+        for (int j = 0; j < kKG; ++j) {
+            const int g = ks * kKG + j;
+            if (wave_live && g < G) {
+                // fragments of the group, then all its MFMAs, then the epilogue
+                // (no MFMA result is consumed right after its issue)
+                v4i bv[4], av[MT];
+                float sw[4], sx[MT][4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint2 wv = *reinterpret_cast<const uint2 *>(brow[b] + 32 * g);
-            const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, unpack_b(wv), zero, 0, 0, 0);
-            const float sw = f16_to_f32(srow[b][g]);
+                for (int nt = 0; nt < 4; ++nt) {
+                    bv[nt] = unpack_b(*reinterpret_cast<const uint2 *>(
+                        sm.b[buf] + (lb[nt] + n) * kBS + j * 32 + 8 * q));
+                    sw[nt] = sm.sw[buf][j][lb[nt] + n];
+                }
+                // m-tiles in pairs: fewer MFMA results live at once
+#pragma unroll
+                for (int m2 = 0; m2 < MT; m2 += 2) {
+#pragma unroll
+                    for (int mt = m2; mt < m2 + 2; ++mt) {
+                        av[mt] = *reinterpret_cast<const v4i *>(
+                            sm.a[buf] + (arow0 + mt * 16 + n) * kAS + j * 64 + 16 * q);
+                        const float4 sx4 = *reinterpret_cast<const float4 *>(
+                            &sm.sx[buf][j][arow0 + mt * 16 + 4 * q]);
+                        sx[mt][0] = sx4.x; sx[mt][1] = sx4.y; sx[mt][2] = sx4.z; sx[mt][3] = sx4.w;
+                    }
+                    v4i c[2][4];
+#pragma unroll
+                    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            c[mm][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[m2 + mm], bv[nt], zero, 0, 0, 0);
+#pragma unroll
+                    for (int mm = 0; mm < 2; ++mm) {
+                        const int mt = m2 + mm;
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                out[mt][nt][i] = fmaf((float)c[mm][nt][i] * sx[mt][i], sw[nt], out[mt][nt][i]);
+                            if constexpr (DUMP) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (arow0 + mt * 16 + 4 * q + i < ti.rows && d_row[nt] >= 0)
+                                        a.dump_acc[((size_t)d_out[mt][i] * a.N + d_row[nt]) * G + g] =
+                                            c[mm][nt][i] >> 4;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (ks + 1 < nsteps) store_step(buf ^ 1, ks + 1);
+        __syncthreads();
+    }
+
+    if constexpr (GATEUP) {
+        // SwiGLU, then int8 quantisation of h per (row, 64-group [nb0, nb0 + 64)):
+        // amax over the group's 64 columns = 16 lanes x 2 n-tiles x 2 waves (wn).
+        float h[MT][2][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int iacc = acc[i] >> 4;
-                if (a.dump_acc && 4 * q + i < mt)
-                    a.dump_acc[((size_t)c_out[i] * a.N + n0 + 16 * b + n) * G + g] = iacc;
-                out[b][i] = fmaf((float)iacc * sx[i], sw, out[b][i]);
+                float m = 0.f;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const float gg = out[mt][nt][i], uu = out[mt][nt + 2][i];
+                    h[mt][nt][i] = gg / (1.0f + expf(-gg)) * uu;
+                    m = fmaxf(m, fabsf(h[mt][nt][i]));
+                }
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, true)));
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, true)));
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, true)));
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x128, 0xF, 0xF, true)));
+                if (n == 0) sm.amax[wn][arow0 + mt * 16 + 4 * q + i] = m;
             }
-        }
-    }
+        __syncthreads();
+        const int G2 = a.I / 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (4 * q + i >= mt) continue;
-        float *orow = a.o + (size_t)c_out[i] * a.H;
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) orow[n0 + 16 * b + n] = out[b][i];
+            for (int i = 0; i < 4; ++i) {
+                const int m = arow0 + mt * 16 + 4 * q + i;
+                if (m >= ti.rows) continue;
+                const float amax = fmaxf(sm.amax[0][m], sm.amax[1][m]);
+                int ir, orow;
+                tile_row(a, ti, m, ir, orow);
+                const float sc = amax > 0.f ? amax / 127.0f : 0.f;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int col = nb0 + 32 * wn + 16 * nt + n;
+                    int8_t code = 0;
+                    if (amax > 0.f) {
+                        float r = rintf(h[mt][nt][i] / sc);
+                        r = fminf(fmaxf(r, -127.f), 127.f);
+                        code = (int8_t)r;
+                    }
+                    a.qh[(size_t)orow * a.I + perm8_pos(col)] = code;
+                    if (DUMP) a.dump_qh[(size_t)orow * a.I + col] = code;
+                }
+                if (wn == 0 && n == 0) {
+                    a.sh[(size_t)orow * G2 + nb0 / 64] = sc;
+                    if (DUMP) a.dump_sh[(size_t)orow * G2 + nb0 / 64] = sc;
+                }
+            }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = arow0 + mt * 16 + 4 * q + i;
+                if (m >= ti.rows) continue;
+                int ir, orow;
+                tile_row(a, ti, m, ir, orow);
+                float *op = a.o + (size_t)orow * a.H;
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int col = nb0 + lb[nt] + n;
+                    if (col < a.N) op[col] = out[mt][nt][i];
+                }
+            }
     }
 }
 
@@ -351,8 +517,13 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (mk) mk->mark(st);
+    // 64-row tiles: measured on MI355X they beat 128-row tiles even for dense
+    // entries (three workgroups per CU instead of two) and waste fewer rows on
+    // the last, partial tile of each entry
+    constexpr int kTileRows = 64;
+    const int tile_m = kTileRows;
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, io.offsets, io.n_union,
-                       (int)lay.cap, T, L.n_shared, tiles, (int)lay.max_tiles);
+                       (int)lay.cap, T, L.n_shared, tile_m, tiles, (int)lay.max_tiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     I8Args a{};
@@ -362,17 +533,23 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.qh = qh; a.sh = sh; a.o = o;
     int32_t *dump = io.acc_dump;
     uint8_t *dump_b = reinterpret_cast<uint8_t *>(dump);
-    // gate/up
     a.qin = qx; a.sin = sx; a.in_by_slot = 0;
     a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
     a.N = 2 * L.I; a.K = L.H;
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc13) : nullptr;
     a.dump_qh = dump ? reinterpret_cast<int8_t *>(dump_b + io.dump.qh) : nullptr;
     a.dump_sh = dump ? reinterpret_cast<float *>(dump_b + io.dump.sh) : nullptr;
+#define COLI_GG(GU_, GX_)                                                                      \
+    {                                                                                          \
+        const dim3 grid(GX_, (unsigned)lay.max_tiles);                                         \
+        if (dump) hipLaunchKernelGGL((ggemm_kernel<kTileRows, 2, GU_, true>), grid, dim3(256), 0, st, a); \
+        else hipLaunchKernelGGL((ggemm_kernel<kTileRows, 2, GU_, false>), grid, dim3(256), 0, st, a);     \
+        if ((err = hipGetLastError()) != hipSuccess) return err;                               \
+    }
+    // gate/up: grid x = 64-unit column blocks (32 for I = 2048: a multiple of 8,
+    // so the m-tiles of one entry and column block land on one XCD's L2)
     if (mk) mk->mark(st);
-    hipLaunchKernelGGL(ggemm_gateup_kernel, dim3((L.I + 255) / 256, (unsigned)lay.max_tiles),
-                       dim3(256), 0, st, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    COLI_GG(true, L.I / (kBN / 2))
     // down
     a.qin = qh; a.sin = sh; a.in_by_slot = 1;
     a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
@@ -380,9 +557,8 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc2) : nullptr;
     a.dump_qh = nullptr; a.dump_sh = nullptr;
     if (mk) mk->mark(st);
-    hipLaunchKernelGGL(ggemm_down_kernel, dim3((L.H + 255) / 256, (unsigned)lay.max_tiles),
-                       dim3(256), 0, st, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    COLI_GG(false, (L.H + kBN - 1) / kBN)
+#undef COLI_GG
     if (mk) mk->mark(st);
     err = launch_combine(o, io.w, T, L.k, L.H, L.n_shared, io.y, st);
     if (mk) mk->mark(st);
