@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (the reference for HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -94,7 +96,17 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
+        return
+
     import int4_routed_expert_bias_amd as coli
+    from int4_routed_expert_bias_amd import profiling
     import synth
 
     assert torch.cuda.is_available(), "needs a GPU"
@@ -190,9 +202,9 @@ def main():
 
     # ---- dominant kernel: per-kernel events on the library's stream ------
     hip = Hip()
-    names = coli.forward_kernel_names(mode)
+    names = coli.forward_kernel_names(mode, T)
     nk = len(names)
-    dom = 0 if mode == coli.ACT_F32 else names.index("ggemm_gateup_kernel")
+    dom = 0 if mode == coli.ACT_F32 else names.index("ggemm_kernel<gateup>")
     prof_steps = min(K, 64)
     ev = [[hip.event() for _ in range(nk + 1)] for _ in range(prof_steps * (w.layers if stacked else 1))]
     union_sizes = []
@@ -245,6 +257,14 @@ def main():
         ach = algo_bytes / dur_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as fp:
+            rec = json.load(fp).get(f"{w.name}:{names[dom]}")
+        if rec and rec.get("source_hash") == profiling.source_hash():
+            traffic = rec["hbm_bytes_per_launch"]
+    roof["traffic"] = traffic
     roof["kernel"] = names[dom]
     roof["kernel_us"] = round(per_kernel[dom] * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(algo_bytes)

@@ -188,9 +188,12 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
                               void *hip_stream);
 
 /* Number of kernels coli_moe_forward launches for act_mode (0 if unknown),
- * and the name of the i-th one (NULL if out of range). */
+ * and the name of the i-th one for a batch of T tokens: the HIP kernel
+ * function as it appears in a profiler trace (template arguments omitted),
+ * which depends on T in the fp32 family (T == 1 runs the single-token
+ * streaming kernels).  NULL if out of range. */
 int coli_moe_forward_kernel_count(int32_t act_mode);
-const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t i);
+const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
 
 /* Size in bytes of the acc_dump buffer of coli_moe_forward (0 if invalid). */
 size_t coli_moe_acc_dump_bytes(int32_t H, int32_t I, int32_t k, int32_t T, int32_t n_shared);

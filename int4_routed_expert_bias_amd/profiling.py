@@ -1,0 +1,133 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+Used on the measurement side only (never by the compute path):
+
+  python -m int4_routed_expert_bias_amd.profiling trace <run_kernel_trace.csv> --command "..."
+      markdown table of per-kernel durations (avg / min / max, grid, registers)
+
+  python -m int4_routed_expert_bias_amd.profiling traffic \
+      --fetch <pmc dir> --write <pmc dir> --copy-fetch <pmc dir> --copy-write <pmc dir> \
+      --kernel <label> --match <trace name substring> --workload <name> \
+      --out profiles/traffic.json
+      HBM bytes per launch of one kernel from the FETCH_SIZE and WRITE_SIZE
+      counters (KiB per dispatch), each scaled by the factor that maps the
+      same counter on a plain device copy of known size to its true bytes.
+
+The traffic record carries a hash of the kernel sources it was measured on;
+bench.py reports it only while the sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
+COPY_KERNEL = "copyBuffer"  # the runtime blit kernel behind a device-to-device tensor copy
+
+
+def source_hash(files=("expert_f32.hip", "expert_i8.hip", "common.h", "route.hip",
+                       "union.hip", "combine.hip")) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "csrc", f), "rb") as fp:
+            h.update(fp.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path_or_dir: str, name: str):
+    p = path_or_dir
+    if os.path.isdir(p):
+        hits = glob.glob(os.path.join(p, "**", name), recursive=True)
+        if not hits:
+            raise FileNotFoundError(f"{name} under {p}")
+        p = hits[0]
+    with open(p) as f:
+        return list(csv.DictReader(f))
+
+
+def trace_table(trace_csv: str, skip=("spin_kernel",)) -> str:
+    rows = _rows(trace_csv, "*kernel_trace.csv")
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if any(s in name for s in skip):
+            continue
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        e = per.setdefault(name, {"d": [], "grid": f"{r['Grid_Size_X']}x{r['Grid_Size_Y']}",
+                                  "block": r["Workgroup_Size_X"], "vgpr": r["VGPR_Count"],
+                                  "agpr": r.get("Accum_VGPR_Count", "0"),
+                                  "lds": r["LDS_Block_Size"]})
+        e["d"].append(d)
+    out = ["| kernel | calls | avg us | min us | max us | grid | block | VGPR | AGPR | LDS B |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, e in sorted(per.items(), key=lambda kv: -statistics.mean(kv[1]["d"]) * len(kv[1]["d"])):
+        d = e["d"]
+        out.append(f"| `{name[:90]}` | {len(d)} | {statistics.mean(d):.2f} | {min(d):.2f} | "
+                   f"{max(d):.2f} | {e['grid']} | {e['block']} | {e['vgpr']} | {e['agpr']} | "
+                   f"{e['lds']} |")
+    return "\n".join(out)
+
+
+def pmc_avg(pmc_dir: str, counter: str, kernel_sub: str) -> float:
+    rows = _rows(pmc_dir, "*counter_collection.csv")
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r["Counter_Name"] == counter and kernel_sub in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError(f"no {counter} rows for kernels matching {kernel_sub!r}")
+    return statistics.mean(vals)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("trace_csv")
+    t.add_argument("--command", default="")
+    tr = sub.add_parser("traffic")
+    for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "match", "workload", "out"):
+        tr.add_argument("--" + a.replace("_", "-"), required=True)
+    tr.add_argument("--bytes-per-launch", type=float, default=None,
+                    help="algorithmic bytes of one launch (for the ratio in the record)")
+    args = ap.parse_args(argv)
+    if args.cmd == "trace":
+        if args.command:
+            print("Command:\n\n```\n" + args.command + "\n```\n")
+        print(trace_table(args.trace_csv))
+        return
+    f_kib = pmc_avg(args.fetch, "FETCH_SIZE", args.match)
+    w_kib = pmc_avg(args.write, "WRITE_SIZE", args.match)
+    cf_kib = pmc_avg(args.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
+    cw_kib = pmc_avg(args.copy_write, "WRITE_SIZE", COPY_KERNEL)
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    rec = {
+        "kernel": args.kernel, "match": args.match, "workload": args.workload,
+        "source_hash": source_hash(),
+        "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
+        "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "hbm_bytes_per_launch": round(f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale),
+    }
+    if args.bytes_per_launch:
+        rec["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / args.bytes_per_launch, 3)
+    db = {}
+    if os.path.exists(args.out):
+        with open(args.out) as fp:
+            db = json.load(fp)
+    db[f"{args.workload}:{args.kernel}"] = rec
+    with open(args.out, "w") as fp:
+        json.dump(db, fp, indent=1, sort_keys=True)
+        fp.write("\n")
+    json.dump(rec, sys.stdout, indent=1)
+    print()
+
+
+if __name__ == "__main__":
+    main()
