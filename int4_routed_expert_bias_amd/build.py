@@ -22,12 +22,15 @@ FLAGS = [
     # never emit packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-file flags.  The router's fp64 MFMA accumulators stay in VGPRs (the
+# default AGPR form copies them across the loop every iteration).
+EXTRA = {"route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(SRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + lang + ["-c", os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass warns that it does not know the packed-fp32 feature: harmless
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

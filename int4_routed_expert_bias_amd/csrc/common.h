@@ -58,7 +58,7 @@ __device__ __forceinline__ int perm8_pos(int kk)
 // workspace layout (offsets in bytes, each region 256-byte aligned)
 
 struct Workspace {
-    size_t logits;   // route: [T][E] f32
+    size_t logits;   // route: [T][E] f32 logits, or [S][T][E] f64 partials
     size_t route_end;
     // forward, shared by both families
     size_t o;        // [R][H] f32 expert outputs per slot / shared row
@@ -77,6 +77,35 @@ struct Workspace {
 
 constexpr int kTileM = 64;  // token rows per integer-GEMM tile
 
+// Router: batches of up to kGemvTMax tokens stream Wr once (GEMV, fp32
+// logits); larger batches run an fp64 MFMA GEMM split over K whose fp64
+// partial sums [S][T][E] are added in split order by the top-k kernel.
+constexpr int kGemvTMax = 8;
+constexpr int kLogitTile = 64;  // tokens x experts per GEMM workgroup
+
+// K-splits of the router GEMM for T tokens: S splits of bps 16-wide
+// k-blocks each (S == 0: GEMV path).  A function of the shape only (never of
+// the device), so that the workspace size and the launch agree: about 512
+// workgroups, at least four k-blocks per split, at most 64 MiB of partials
+// unless S == 1, and every split non-empty ((S-1)*bps < H/16 <= S*bps).
+struct RouteSplit {
+    int S, bps;
+};
+
+inline RouteSplit route_split(int64_t T, int64_t H, int64_t E)
+{
+    if (T <= kGemvTMax) return {0, 0};
+    const int64_t tiles = ((T + kLogitTile - 1) / kLogitTile) * ((E + kLogitTile - 1) / kLogitTile);
+    const int64_t nb = H / 16;
+    int64_t s = (512 + tiles - 1) / tiles;
+    if (s > nb / 4) s = nb / 4;
+    const int64_t cap = (int64_t(64) << 20) / (T * E * 8);
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    const int64_t bps = (nb + s - 1) / s;
+    return {(int)((nb + bps - 1) / bps), (int)bps};
+}
+
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, int64_t T,
@@ -87,7 +116,8 @@ inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, in
     w.cap = (T * k < E) ? T * k : E;
     w.max_tiles = (T * k + kTileM - 1) / kTileM + w.cap + n_shared * ((T + kTileM - 1) / kTileM);
     size_t p = 0;
-    w.logits = p; p = align256(p + (size_t)T * E * 4);
+    const int S = route_split(T, H, E).S;
+    w.logits = p; p = align256(p + (S == 0 ? (size_t)T * E * 4 : (size_t)S * T * E * 8));
     w.route_end = p;
     p = 0;  // forward buffers alias the route scratch (stream-ordered)
     w.o = p; p = align256(p + (size_t)w.R * H * 4);

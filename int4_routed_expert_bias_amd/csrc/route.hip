@@ -6,14 +6,12 @@
 // logits = x . Wr^T accumulated in fp64 and rounded once to fp32, so the
 // selection does not depend on summation order at fp32 precision.
 //   small T: one workgroup per expert row streams Wr once (HBM-bound);
-//   large T: LDS-tiled fp64 GEMM.
+//   large T: fp64 MFMA GEMM split over K, partials added by the top-k kernel.
 // top-k: one wave per token; lane l holds experts l, l+64, ...; k rounds of
 // a wave-wide argmax on (key desc, expert asc).
 #include "common.h"
 
 namespace coli {
-
-constexpr int kGemvTMax = 8;
 
 // --- small T: grid = E workgroups of 256 threads (4 waves split H) -------
 template <int NT>
@@ -58,59 +56,103 @@ __global__ __launch_bounds__(256) void logits_gemv_kernel(const float *__restric
     }
 }
 
-// --- large T: 64 tokens x 64 experts per workgroup, 4x4 per thread -------
-constexpr int kLT = 64, kLE = 64, kLK = 16;
+// --- large T: fp64 MFMA GEMM, split over K -------------------------------
+// v_mfma_f64_16x16x4f64: lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// receives D[4v + l/16][l%16] in its v-th register pair, v < 4 (rows are
+// interleaved across the lane quarters, unlike the fp32 16x16x4 form).  The fp32 operands are widened to fp64
+// (exact) and each product is exact in fp64.  The K index assigned to a
+// lane's quarter is free as long as A and B agree: in a k-block of 16, lane
+// quarter q loads the float4 at k0+4q of its row and the m-th MFMA uses its
+// m-th element, so every load is a 16-byte vector.
+// Workgroup: 64 tokens x 64 experts, 2 x 2 waves of 32 x 32 (2 x 2 MFMA
+// tiles); split s covers k-blocks [s*bps, (s+1)*bps) and writes its fp64
+// partial sums to part[s][t][e].  Operands come straight from global memory:
+// a wave needs 4 KB per 16 MFMAs, which L2 serves.
+typedef double coli_d4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void logits_gemm_kernel(const float *__restrict__ x,
-                                                          const float *__restrict__ Wr,
-                                                          int T, int H, int E,
-                                                          float *__restrict__ logits)
+__device__ __forceinline__ float f4_at(const float4 &v, int m)
 {
-    __shared__ double xs[kLK][kLT + 1];
-    __shared__ double ws[kLK][kLE + 1];
-    const int t0 = blockIdx.y * kLT, e0 = blockIdx.x * kLE;
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;  // thread owns experts e0+tx+16j, tokens t0+ty+16i
-    double acc[4][4];
+    return m == 0 ? v.x : m == 1 ? v.y : m == 2 ? v.z : v.w;
+}
+
+__global__ __launch_bounds__(256) void logits_mfma_kernel(const float *__restrict__ x,
+                                                          const float *__restrict__ Wr,
+                                                          int T, int H, int E, int tilesE, int S,
+                                                          int bps, int nwg,
+                                                          double *__restrict__ part)
+{
+    // The dispatcher deals workgroups to the 8 XCDs round-robin; remap so
+    // that consecutive logical ids (the expert tiles of one token tile and
+    // split, which read the same x) run on one XCD and share its L2.
+    const int G = gridDim.x;  // a multiple of 8
+    const int L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (L >= nwg) return;
+    const int te = L % tilesE;
+    const int r = L / tilesE;
+    const int s = r % S;
+    const int tt = r / S;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w & 1, wn = w >> 1;
+    const int i = lane & 15, q = lane >> 4;
+    const int nb = H >> 4;
+    const int b0 = s * bps, b1 = min(nb, b0 + bps);
+    const float *ap[2], *bp[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    // loader mapping: 256 threads x float4 = 64 rows x 16 columns
-    const int lr = tid >> 2, lc = (tid & 3) * 4;
-    for (int k0 = 0; k0 < H; k0 += kLK) {
-        {
-            int t = t0 + lr;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < T) v = *reinterpret_cast<const float4 *>(x + (size_t)t * H + k0 + lc);
-            xs[lc + 0][lr] = v.x; xs[lc + 1][lr] = v.y; xs[lc + 2][lr] = v.z; xs[lc + 3][lr] = v.w;
-            int e = e0 + lr;
-            float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < E) u = *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + k0 + lc);
-            ws[lc + 0][lr] = u.x; ws[lc + 1][lr] = u.y; ws[lc + 2][lr] = u.z; ws[lc + 3][lr] = u.w;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < kLK; ++kk) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx + 16 * j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
+    for (int mt = 0; mt < 2; ++mt) {
+        const int t = min(tt * kLogitTile + wm * 32 + mt * 16 + i, T - 1);
+        ap[mt] = x + (size_t)t * H + 16 * b0 + 4 * q;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int nt = 0; nt < 2; ++nt) {
+        const int e = min(te * kLogitTile + wn * 32 + nt * 16 + i, E - 1);
+        bp[nt] = Wr + (size_t)e * H + 16 * b0 + 4 * q;
+    }
+    coli_d4 acc[2][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
-            if (t < T && e < E) logits[(size_t)t * E + e] = (float)acc[i][j];
-        }
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = coli_d4{0.0, 0.0, 0.0, 0.0};
+    // Two register buffers: the loads of block n+1 are in flight while the
+    // MFMAs of block n run.  Past the split's end the loads re-read the
+    // split's last block (in bounds) and are not used.
+    float4 a0[2], b0v[2], a1[2], b1v[2];
+    auto load = [&](float4 *a, float4 *b, int blk) {
+        const int off = 16 * (min(blk, b1 - 1) - b0);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) a[mt] = *reinterpret_cast<const float4 *>(ap[mt] + off);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) b[nt] = *reinterpret_cast<const float4 *>(bp[nt] + off);
+    };
+    auto mma = [&](const float4 *a, const float4 *b) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                        (double)f4_at(a[mt], m), (double)f4_at(b[nt], m), acc[mt][nt], 0, 0, 0);
+    };
+    if (b0 >= b1) return;  // no empty split is ever launched
+    load(a0, b0v, b0);
+    int blk = b0;
+    for (; blk + 1 < b1; blk += 2) {
+        load(a1, b1v, blk + 1);
+        mma(a0, b0v);
+        load(a0, b0v, blk + 2);
+        mma(a1, b1v);
+    }
+    if (blk < b1) mma(a0, b0v);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = tt * kLogitTile + wm * 32 + mt * 16 + 4 * v + q;
+                const int e = te * kLogitTile + wn * 32 + nt * 16 + i;
+                if (t < T && e < E) part[((size_t)s * T + t) * E + e] = acc[mt][nt][v];
+            }
 }
 
 // --- top-k: one wave per token, 4 tokens per workgroup -------------------
@@ -130,8 +172,29 @@ __device__ __forceinline__ uint32_t order_bits(float z)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Logit of (t, e): the GEMV's fp32 value, or the fp64 partials of the S
+// K-splits added in split order and rounded once to fp32.
+__device__ __forceinline__ float logit_at(const float *__restrict__ logits,
+                                          const double *__restrict__ part, int S, int T, int E,
+                                          int t, int e)
+{
+    if (S == 0) return logits[(size_t)t * E + e];
+    const size_t stride = (size_t)T * E;
+    const double *p = part + (size_t)t * E + e;
+    double acc = p[0];
+    int s = 1;
+    for (; s + 4 <= S; s += 4) {  // four loads in flight, added in split order
+        const double v0 = p[s * stride], v1 = p[(s + 1) * stride];
+        const double v2 = p[(s + 2) * stride], v3 = p[(s + 3) * stride];
+        acc += v0; acc += v1; acc += v2; acc += v3;
+    }
+    for (; s < S; ++s) acc += p[s * stride];
+    return (float)acc;
+}
+
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
+                                                   const double *__restrict__ part, int S,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
                                                    float *__restrict__ w)
@@ -142,12 +205,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     const bool live = t < T;
-    const float *lrow = logits + (size_t)(live ? t : 0) * E;
+    const int tr = live ? t : 0;
     uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = (live && e < E) ? order_bits(sigmoid_fp64(lrow[e]) + bias[e]) : 0u;
+        key[i] = (live && e < E) ? order_bits(sigmoid_fp64(logit_at(logits, part, S, T, E, tr, e)) +
+                                              bias[e])
+                                 : 0u;
     }
     // largest tau with #{key >= tau} >= k  (valid keys are >= 1)
     uint32_t tau = 0;
@@ -194,7 +259,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     __syncthreads();
     float sj = 0.f;
     if (live && lane < k) {
-        sj = sigmoid_fp64(lrow[me]);
+        sj = sigmoid_fp64(logit_at(logits, part, S, T, E, tr, me));
         ss[wv][rank] = sj;
     }
     __syncthreads();
@@ -210,7 +275,10 @@ hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st)
 {
     const int T = io.T, H = L.H, E = L.E;
     if (T <= 0) return hipSuccess;
-    if (T <= kGemvTMax) {
+    const RouteSplit rs = route_split(T, H, E);
+    const int S = rs.S;
+    const double *part = reinterpret_cast<const double *>(io.logits);
+    if (S == 0) {
         dim3 grid(E), block(256);
 #define COLI_GEMV_CASE(N) \
     case N: hipLaunchKernelGGL(logits_gemv_kernel<N>, grid, block, 0, st, io.x, L.router_w, T, H, E, io.logits); break;
@@ -222,16 +290,19 @@ hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st)
         }
 #undef COLI_GEMV_CASE
     } else {
-        dim3 grid((E + kLE - 1) / kLE, (T + kLT - 1) / kLT), block(256);
-        hipLaunchKernelGGL(logits_gemm_kernel, grid, block, 0, st, io.x, L.router_w, T, H, E,
-                           io.logits);
+        const int bps = rs.bps;
+        const int tilesT = (T + kLogitTile - 1) / kLogitTile, tilesE = (E + kLogitTile - 1) / kLogitTile;
+        const int nwg = tilesT * tilesE * S;
+        const int G = (nwg + 7) & ~7;
+        hipLaunchKernelGGL(logits_mfma_kernel, dim3(G), dim3(256), 0, st, io.x, L.router_w, T, H, E,
+                           tilesE, S, bps, nwg, reinterpret_cast<double *>(io.logits));
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int kpl = (E + 63) / 64;
 #define COLI_TOPK(N) \
     if (kpl <= N) { hipLaunchKernelGGL(topk_kernel<N>, dim3((T + 3) / 4), dim3(256), 0, st, io.logits, \
-                                       L.router_bias, T, E, L.k, io.ids, io.w); return hipGetLastError(); }
+                                       part, S, L.router_bias, T, E, L.k, io.ids, io.w); return hipGetLastError(); }
     COLI_TOPK(1)
     COLI_TOPK(2)
     COLI_TOPK(4)

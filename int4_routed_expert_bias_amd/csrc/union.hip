@@ -2,21 +2,21 @@
 // page, section "토큰당 처리 경로": experts picked by several tokens of the
 // batch are de-duplicated and computed once).
 //
-// One workgroup of 8 waves.  Wave w owns a contiguous range of slots.
+// One workgroup of W waves.  Wave w owns a contiguous range of slots.
 //   1. per-wave expert histograms in LDS (integer atomics: order-free),
 //   2. a block scan gives each expert its start and its union position, and
 //      each wave its private cursor per expert (start + counts of the
 //      waves before it),
-//   3. each wave walks its range in order, 64 slots at a time; lanes holding
-//      the same expert are grouped with a ballot match loop, ranked by lane
-//      order and scattered at the wave's cursor.
+//   3. each wave walks its range in order, 64 slots at a time: the 64 keys
+//      (expert << 6 | lane) are sorted with a bitonic network across the
+//      wave, so that equal experts form runs in lane order; a lane's rank in
+//      its run plus the wave's cursor of that expert is where its slot goes,
+//      and the last lane of a run advances the cursor.
 // The result is the stable order (ascending slot) and is deterministic.
 #include "common.h"
 
 namespace coli {
 
-constexpr int kUnionWaves = 8;
-constexpr int kUnionThreads = kUnionWaves * 64;
 
 __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *tmp)
 {
@@ -36,7 +36,25 @@ __device__ void block_exclusive_scan(int32_t *a, int n, int32_t *tmp)
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__restrict__ ids,
+// Bitonic sort of one key per lane across the wave, ascending by lane.
+__device__ __forceinline__ uint32_t wave_sort64(uint32_t key, int lane)
+{
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride >= 1; stride >>= 1) {
+            const uint32_t other = __shfl_xor(key, stride, 64);
+            const bool ascending = (lane & size) == 0 || size == 64;
+            const bool lower = (lane & stride) == 0;
+            const uint32_t lo = min(key, other), hi = max(key, other);
+            key = (lower == ascending) ? lo : hi;
+        }
+    }
+    return key;
+}
+
+template <int W>
+__global__ __launch_bounds__(W * 64) void union_kernel(const int32_t *__restrict__ ids,
                                                               int n, int E, int cap,
                                                               int32_t *__restrict__ union_ids,
                                                               int32_t *__restrict__ offsets,
@@ -44,16 +62,16 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__r
                                                               int32_t *__restrict__ n_union)
 {
     extern __shared__ int32_t smem[];
-    volatile int32_t *cur = smem;                       // [kUnionWaves][E]
-    int32_t *start = smem + kUnionWaves * E;            // [E]
+    volatile int32_t *cur = smem;                       // [W][E]
+    int32_t *start = smem + W * E;                      // [E]
     int32_t *upos = start + E;                          // [E]
     int32_t *tmp = upos + E;                            // [E]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    for (int i = tid; i < kUnionWaves * E; i += blockDim.x) cur[i] = 0;
+    for (int i = tid; i < W * E; i += blockDim.x) cur[i] = 0;
     __syncthreads();
 
-    const int per = ((n + kUnionWaves - 1) / kUnionWaves + 63) & ~63;
+    const int per = ((n + W - 1) / W + 63) & ~63;
     const int r0 = min(n, wave * per), r1 = min(n, r0 + per);
     for (int s = r0 + lane; s < r1; s += 64) {
         int id = ids[s];
@@ -63,7 +81,7 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__r
 
     for (int e = tid; e < E; e += blockDim.x) {
         int32_t c = 0;
-        for (int w = 0; w < kUnionWaves; ++w) c += cur[w * E + e];
+        for (int w = 0; w < W; ++w) c += cur[w * E + e];
         start[e] = c;
         upos[e] = c > 0 ? 1 : 0;
     }
@@ -72,8 +90,8 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__r
     for (int e = tid; e < E; e += blockDim.x) tmp[e] = start[e];
     __syncthreads();
     // keep the counts in the first row of a scratch region before scanning
-    block_exclusive_scan(start, E, smem + kUnionWaves * E + 3 * E);
-    block_exclusive_scan(upos, E, smem + kUnionWaves * E + 4 * E);
+    block_exclusive_scan(start, E, smem + W * E + 3 * E);
+    block_exclusive_scan(upos, E, smem + W * E + 4 * E);
 
     int32_t U = upos[E - 1] + (tmp[E - 1] > 0 ? 1 : 0);
     for (int e = tid; e < E; e += blockDim.x) {
@@ -83,7 +101,7 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__r
             offsets[upos[e]] = start[e];
         }
         int32_t base = start[e];
-        for (int w = 0; w < kUnionWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             int32_t v = cur[w * E + e];
             cur[w * E + e] = base;
             base += v;
@@ -94,23 +112,29 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const int32_t *__r
     if (tid == 0) n_union[0] = U;
     __syncthreads();
 
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int b = r0; b < r1; b += 64) {
-        int s = b + lane;
-        int id = (s < r1) ? ids[s] : -1;
-        bool valid = id >= 0 && id < E;
-        uint64_t active = __ballot(valid);
-        while (active) {
-            int leader = __ffsll((unsigned long long)active) - 1;
-            int v = __shfl(id, leader, 64);
-            uint64_t m = __ballot(valid && id == v);
-            int32_t base = cur[wave * E + v];
-            if (valid && id == v) slots[base + __popcll(m & lt_mask)] = s;
-            __builtin_amdgcn_wave_barrier();
-            if (lane == leader) cur[wave * E + v] = base + __popcll(m);
-            __builtin_amdgcn_wave_barrier();
-            active &= ~m;
+        const int s = b + lane;
+        const int id = (s < r1) ? ids[s] : -1;
+        const bool valid = id >= 0 && id < E;
+        const uint32_t key = wave_sort64(valid ? ((uint32_t)id << 6 | (uint32_t)lane) : 0xFFFFFFFFu,
+                                         lane);
+        const bool has = key != 0xFFFFFFFFu;
+        const int sid = has ? (int)(key >> 6) : -1;
+        const int prev = __shfl_up(sid, 1, 64);
+        const int next = __shfl_down(sid, 1, 64);
+        const bool head = has && (lane == 0 || prev != sid);
+        const bool tail = has && (lane == 63 || next != sid);
+        const uint64_t heads = __ballot(head);
+        const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1);
+        const int rank = lane - (63 - __clzll(heads & upto));  // lane of this run's head
+        int32_t base = 0;
+        if (has) {
+            base = cur[wave * E + sid];
+            slots[base + rank] = b + (int)(key & 63u);
         }
+        __builtin_amdgcn_wave_barrier();
+        if (tail) cur[wave * E + sid] = base + rank + 1;
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -169,9 +193,16 @@ hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int
                            offsets, slots, n_union);
         return hipGetLastError();
     }
-    const size_t lds = (size_t)(kUnionWaves + 5) * E * sizeof(int32_t);
-    hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), lds, st, ids, n, E, cap,
-                       union_ids, offsets, slots, n_union);
+    // 16 waves while the per-wave histograms fit in 64 KB of LDS, else 8
+    if (E <= 512) {
+        const size_t lds = (size_t)(16 + 5) * E * sizeof(int32_t);
+        hipLaunchKernelGGL(union_kernel<16>, dim3(1), dim3(16 * 64), lds, st, ids, n, E, cap,
+                           union_ids, offsets, slots, n_union);
+    } else {
+        const size_t lds = (size_t)(8 + 5) * E * sizeof(int32_t);
+        hipLaunchKernelGGL(union_kernel<8>, dim3(1), dim3(8 * 64), lds, st, ids, n, E, cap,
+                           union_ids, offsets, slots, n_union);
+    }
     return hipGetLastError();
 }
 
