@@ -258,13 +258,31 @@ def test_route_expert_counts(E, k, T):
     check_route(b.ids[:T].cpu().numpy(), b.w[:T].cpu().numpy(), ids, w, s, A["router_b"])
 
 
-@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
-def test_graph_replay_matches_eager(mode):
+@pytest.mark.parametrize("mode,T", [(coli.ACT_F32, 1), (coli.ACT_F32, 3), (coli.ACT_I8, 5)])
+def test_repeated_calls_on_one_workspace(mode, T):
+    """One workspace serves call after call with identical results, whatever
+    it held before each call (its contents are scratch)."""
+    import torch
+    lay = make_layer(512, 256, 16, 4, wid=69)
+    x = torch.from_numpy(synth.activations(512, T, wid=69)).cuda()
+    b = coli.Buffers(lay.dev, T, mode)
+    ys = []
+    for rep in range(3):
+        b.workspace.fill_(0xA5 if rep % 2 else 0x5A)  # stale contents between calls
+        coli.run_layer(lay.dev, x, b)
+        torch.cuda.synchronize()
+        ys.append(b.y.cpu().clone())
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int32), ys[0].view(torch.int32))
+
+
+@pytest.mark.parametrize("mode,T", [(coli.ACT_F32, 19), (coli.ACT_I8, 19), (coli.ACT_F32, 1)])
+def test_graph_replay_matches_eager(mode, T):
     """route -> union -> forward captured in a HIP graph: every replay (with
-    eager work and synchronisations in between) equals the eager result."""
+    eager work and synchronisations in between) equals the eager result, for
+    the multi-token and the single-token streaming kernels."""
     import torch
     lay = make_layer(512, 256, 16, 4, wid=68)
-    T = 19
     x1 = torch.from_numpy(synth.activations(512, T, wid=68)).cuda()
     x2 = torch.from_numpy(synth.activations(512, T, wid=68, layer=1)).cuda()
     eager = {}
