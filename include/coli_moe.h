@@ -191,7 +191,8 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
  * and the name of the i-th one for a batch of T tokens: the HIP kernel
  * function as it appears in a profiler trace (template arguments omitted),
  * which depends on T in the fp32 family (T == 1 runs the single-token
- * streaming kernels).  NULL if out of range. */
+ * streaming kernels, 2 <= T <= 4 the small-batch streaming kernels).  NULL
+ * if out of range. */
 int coli_moe_forward_kernel_count(int32_t act_mode);
 const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
 

@@ -242,13 +242,16 @@ const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
 {
     static const char *f32_one[kForwardKernelsF32] = {"gateup_t1_kernel", "down_t1_kernel",
                                                       "combine_kernel"};
+    static const char *f32_few[kForwardKernelsF32] = {"gateup_mt_kernel", "down_mt_kernel",
+                                                      "combine_kernel"};
     static const char *f32[kForwardKernelsF32] = {"gateup_f32_kernel", "down_f32_kernel",
                                                   "combine_kernel"};
     static const char *i8[kForwardKernelsI8] = {"quant_rows_kernel", "schedule_kernel",
                                                 "ggemm_kernel<gateup>", "ggemm_kernel<down>",
                                                 "combine_kernel"};
     if (i < 0) return nullptr;
-    if (act_mode == COLI_ACT_F32 && i < kForwardKernelsF32) return T == 1 ? f32_one[i] : f32[i];
+    if (act_mode == COLI_ACT_F32 && i < kForwardKernelsF32)
+        return T == 1 ? f32_one[i] : T <= 4 ? f32_few[i] : f32[i];
     if (act_mode == COLI_ACT_I8 && i < kForwardKernelsI8) return i8[i];
     return nullptr;
 }

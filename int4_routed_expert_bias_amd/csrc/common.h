@@ -12,6 +12,7 @@ namespace coli {
 constexpr int kWave = 64;
 #define COLI_MAX_K_DEV 16    // must equal COLI_MAX_K of the public header
 #define COLI_MAX_E_DEV 1024  // must equal COLI_MAX_E of the public header
+#define COLI_MAX_H_DEV 8192  // must equal COLI_MAX_H of the public header
 
 // ---------------------------------------------------------------------------
 // device helpers

@@ -27,6 +27,8 @@
 // variant runs it: a token alone and inside a batch give identical bits.
 #include "common.h"
 
+#include <type_traits>
+
 #include <algorithm>
 
 namespace coli {
@@ -303,7 +305,9 @@ template <int NT, int P, int W, int RW>
 __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
 {
     constexpr int V = RW * NT, N = reduced_count(V);
-    extern __shared__ float xs[];  // [NT][K] token rows, then [NT][K/32] chunk K
+    // [NT][K] token rows chunk-transposed (token t, piece q of chunk c at
+    // float4 (8 t + q) C + c: conflict-free wave reads), then [NT][K/32] chunk K
+    extern __shared__ float xs[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ue = blockIdx.y;
     if (ue < a.cap && ue >= a.n_union[0]) return;
@@ -314,6 +318,7 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
     if (cnt <= 0) return;
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, K4 = K / 4;
     float *ks = xs + NT * K;
+    const float4 *xt = reinterpret_cast<const float4 *>(xs);
     const auto rw = make_rsrc(wb, (uint32_t)(a.N * rb));
     const auto rs = make_rsrc(sb, (uint32_t)(a.N * sbs * 2));
     const int u0 = (blockIdx.x * W + wave) * (RW / 2);
@@ -345,14 +350,15 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
         if (t0 > 0) __syncthreads();
         for (int tt = 0; tt < nt; ++tt) {
             const float4 *src = reinterpret_cast<const float4 *>(a.in + (size_t)in_row[tt] * K);
-            float4 *dst = reinterpret_cast<float4 *>(xs + tt * K);
-            for (int i = threadIdx.x; i < K4; i += blockDim.x) dst[i] = src[i];
+            float4 *dst = reinterpret_cast<float4 *>(xs);
+            for (int i = threadIdx.x; i < K4; i += blockDim.x)
+                dst[(8 * tt + (i & 7)) * C + (i >> 3)] = src[i];
         }
         __syncthreads();
         for (int j = threadIdx.x; j < nt * C; j += blockDim.x) {
             const int tt = j / C, c = j - tt * C;
             float v[32];
-            load_chunk32(reinterpret_cast<const float4 *>(xs + tt * K + c * 32), 1, v);
+            load_chunk32(xt + 8 * tt * C + c, C, v);
             ks[tt * C + c] = chunk_K(v);
         }
         __syncthreads();
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
                 for (int p = 0; p < P; ++p) {
                     const int c = min(lane + 64 * p, C - 1);
                     float xv[1][32], kc[1];
-                    load_chunk32(reinterpret_cast<const float4 *>(xs + tt * K + c * 32), 1, xv[0]);
+                    load_chunk32(xt + 8 * tt * C + c, C, xv[0]);
                     kc[0] = ks[tt * C + c];
                     uint4 wl[RW][1];
 #pragma unroll
@@ -568,7 +574,9 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
     constexpr int V = next_pow2(2 * NP * M), N = reduced_count(V);
     static_assert(V <= 64, "at most 64 values per reduction");
-    extern __shared__ float xs[];  // [K] x, then [K/32] chunk K
+    // x chunk-transposed (piece q of chunk c at float4 q C + c: conflict-free
+    // wave reads), then [K/32] chunk K
+    extern __shared__ float xs[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
@@ -600,14 +608,15 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) issue(d, d);
     float *ks = xs + K;
+    const float4 *xt = reinterpret_cast<const float4 *>(xs);
     {
         const float4 *src = reinterpret_cast<const float4 *>(a.in);
         float4 *dst = reinterpret_cast<float4 *>(xs);
-        for (int i = threadIdx.x; i < K / 4; i += blockDim.x) dst[i] = src[i];
+        for (int i = threadIdx.x; i < K / 4; i += blockDim.x) dst[(i & 7) * C + (i >> 3)] = src[i];
         __syncthreads();
         for (int c = threadIdx.x; c < C; c += blockDim.x) {
             float v[32];
-            load_chunk32(reinterpret_cast<const float4 *>(xs + c * 32), 1, v);
+            load_chunk32(xt + c, C, v);
             ks[c] = chunk_K(v);
         }
         __syncthreads();
@@ -618,7 +627,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int c = min(lane + 64 * p, C - 1);  // dead lanes: scale 0
-        if constexpr (XREG) load_chunk32(reinterpret_cast<const float4 *>(xs + c * 32), 1, xr[p]);
+        if constexpr (XREG) load_chunk32(xt + c, C, xr[p]);
         kx[p] = ks[c];
     }
 
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
 #pragma unroll
                     for (int p = 0; p < P; ++p) {
                         float xl[1][32], kl[1] = {kx[p]};
-                        load_chunk32(reinterpret_cast<const float4 *>(xs + min(lane + 64 * p, C - 1) * 32), 1, xl[0]);
+                        load_chunk32(xt + min(lane + 64 * p, C - 1), C, xl[0]);
                         uint4 wl[2 * NP][1];
                         float dl[2 * NP][1];
 #pragma unroll
@@ -744,6 +753,379 @@ __global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
     }
 }
 
+// Small batches (2 <= T <= kStreamTMax, the verify step): the same streams,
+// each weight stage applied to every token of the wave's entry (at most
+// NTOK: the shared expert takes all T).  x of the T tokens and their chunk
+// constants sit in LDS (NTOK token rows do not fit in registers); the
+// per-(token, row) arithmetic is the single-token one, value for value, so
+// a token's h and o do not depend on its batch.
+constexpr int kStreamTMax = 4;
+
+// chunk_dots for CNT activation chunks at once: each code byte is converted
+// once and used by every token.  out[r][j] is chain (row r, token j) with
+// exactly the arithmetic of chunk_dots (start at -K[j], products in
+// ascending element order).
+template <int NR, int CNT, int NX>
+__device__ __forceinline__ void chunk_dots_tok(const uint4 (&w)[NR], const float (&x)[NX][32],
+                                               const float (&K)[NX], float (&out)[NR][NX])
+{
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int j = 0; j < CNT; ++j) out[r][j] = -K[j];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t lo[NR], hi[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const uint32_t q = word_of(w[r], d);
+            lo[r] = (q ^ 0x88888888u) & 0x0F0F0F0Fu;
+            hi[r] = ((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float fl = byte_f32(lo[r], b), fh = byte_f32(hi[r], b);
+#pragma unroll
+                for (int j = 0; j < CNT; ++j) {
+                    out[r][j] = fmaf(fl, x[j][8 * d + 2 * b], out[r][j]);
+                    out[r][j] = fmaf(fh, x[j][8 * d + 2 * b + 1], out[r][j]);
+                }
+            }
+    }
+}
+
+// f(std::integral_constant<int, c>) for the runtime count 1 <= c <= NMAX
+// (NMAX a power of two <= 4): one specialised body per count.
+template <int NMAX, class F>
+__device__ __forceinline__ void dispatch_count(int c, F &&f)
+{
+    if (c <= 1) f(std::integral_constant<int, 1>{});
+    else if (NMAX >= 2 && c == 2) f(std::integral_constant<int, (NMAX >= 2 ? 2 : 1)>{});
+    else if (NMAX >= 4 && c == 3) f(std::integral_constant<int, (NMAX >= 4 ? 3 : 1)>{});
+    else if (NMAX >= 4) f(std::integral_constant<int, (NMAX >= 4 ? 4 : 1)>{});
+}
+
+// Work split of the small-batch streaming kernels.  A wave streaming one
+// entry is bound by its load latency until its FMAs take longer, which a
+// few tokens do: measured on the 4-token verify layer, a stage costs about
+// (1 + tokens) / 2 single-token stages.  Entry e, of cost 1 + its token
+// count, gets waves [B(e), B(e+1)) with
+// B(e) = e + (GW - ne) * (cost of entries before e) / (total cost), so every
+// entry has at least one wave.  Within an entry the row blocks go
+// round-robin as in t1_split.
+__device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, int U,
+                                            int nblocks)
+{
+    T1Split s{0, 0, 0, 0};
+    const int ne = U + a.n_shared;
+    if (ne <= 0 || GW < ne) return s;
+    const int total = a.offsets[U] + a.n_shared * a.T + ne;
+    const long spare = GW - ne;
+    int before = 0;
+    for (int e = 0; e < ne; ++e) {
+        const int cnt = 1 + (e < U ? a.offsets[e + 1] - a.offsets[e] : a.T);
+        const int b0 = e + (int)(spare * before / total);
+        const int b1 = e + 1 + (int)(spare * (before + cnt) / total);
+        if (gw >= b0 && gw < b1) {
+            s.ue = e;
+            s.part = gw - b0;
+            s.wpe = b1 - b0;
+            s.nsteps = s.part < nblocks ? (nblocks - s.part + s.wpe - 1) / s.wpe : 0;
+            return s;
+        }
+        before += cnt;
+    }
+    return s;
+}
+
+template <int P, int M, int DEPTH, int NTOK, int WPB>
+__global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a)
+{
+    static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
+    constexpr int V = next_pow2(2 * M * NTOK), N = reduced_count(V);
+    static_assert(V <= 64, "at most 64 values per reduction");
+    // x of the T tokens chunk-transposed (token t, piece q of chunk c at
+    // float4 (8 t + q) C + c: the lanes of a wave read consecutive float4s,
+    // free of bank conflicts), then [T][K/32] chunk K
+    extern __shared__ float xs[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
+    const int U = a.n_union[0];
+    const T1Split sp = mt_split(a, blockIdx.x * WPB + wave, gridDim.x * WPB, U, a.I);
+    const int nsteps = sp.nsteps;
+    const uint8_t *wb;
+    const uint16_t *sb;
+    const int32_t *list;
+    const int cnt = min(entry_info(a, sp.ue, wb, sb, list), NTOK);
+    const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
+    uint32_t vw[P], vs[P];
+    lane_offsets<P>(lane, C, vw, vs);
+
+    uint4 wv[DEPTH][2][P];
+    uint16_t sv[DEPTH][2][P];
+    auto issue = [&](int d, int step) {
+        const int blk = sp.part + step * sp.wpe;
+        const int rows[2] = {blk, a.I + blk};
+        load_stage<2, P>(R, rows, step < nsteps, rb, sbs, vw, vs, wv[d], sv[d]);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, d);
+    float *ks = xs + a.T * K;
+    const float4 *xt = reinterpret_cast<const float4 *>(xs);
+    {
+        const float4 *src = reinterpret_cast<const float4 *>(a.in);
+        float4 *dst = reinterpret_cast<float4 *>(xs);
+        for (int i = threadIdx.x; i < a.T * (K / 4); i += blockDim.x) {
+            const int t = i / (K / 4), r = i - t * (K / 4), c = r >> 3, q = r & 7;
+            dst[(8 * t + q) * C + c] = src[i];
+        }
+        __syncthreads();
+        for (int tc = threadIdx.x; tc < a.T * C; tc += blockDim.x) {
+            const int t = tc / C, c = tc - t * C;
+            float v[32];
+            load_chunk32(xt + 8 * t * C + c, C, v);
+            ks[tc] = chunk_K(v);
+        }
+        __syncthreads();
+    }
+    if (nsteps == 0 || cnt <= 0) return;
+    int tok[NTOK], orow[NTOK];
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) {
+        int in_row = 0, out_row = 0;
+        if (j < cnt) token_rows(a, list, j, in_row, out_row);
+        tok[j] = in_row;
+        orow[j] = out_row;
+    }
+
+    for (int g0 = 0; g0 < nsteps; g0 += M) {
+        float racc[V];  // [gate, up][token][m], zero padded to a power of two
+#pragma unroll
+        for (int i = 0; i < V; ++i) racc[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int d = m % DEPTH;
+            if (g0 + m < nsteps) {
+                // per-lane sums over the P chunks (p ascending) for every token
+                auto stage = [&](auto cnt_c) {
+                    constexpr int CNT = decltype(cnt_c)::value;
+                    float acc[2][NTOK];
+#pragma unroll
+                    for (int j = 0; j < CNT; ++j) acc[0][j] = acc[1][j] = 0.f;
+                    if constexpr (CNT == 1) {
+                        // one token: all P chunks at once, 2 * P interleaved chains
+                        float xl[P][32], kl[P], dots[2][P];
+#pragma unroll
+                        for (int p = 0; p < P; ++p) {
+                            const int c = min(lane + 64 * p, C - 1);
+                            kl[p] = ks[tok[0] * C + c];
+                            load_chunk32(xt + 8 * tok[0] * C + c, C, xl[p]);
+                        }
+                        chunk_dots<2, P>(wv[d], xl, kl, dots);
+#pragma unroll
+                        for (int p = 0; p < P; ++p) {
+                            acc[0][0] = fmaf(dots[0][p], f16_to_f32(sv[d][0][p]), acc[0][0]);
+                            acc[1][0] = fmaf(dots[1][p], f16_to_f32(sv[d][1][p]), acc[1][0]);
+                        }
+                    } else {
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        const int c = min(lane + 64 * p, C - 1);  // dead lanes: scale 0
+                        float xl[NTOK][32], kl[NTOK];
+#pragma unroll
+                        for (int j = 0; j < CNT; ++j) {
+                            kl[j] = ks[tok[j] * C + c];
+                            load_chunk32(xt + 8 * tok[j] * C + c, C, xl[j]);
+                        }
+                        const uint4 wl[2] = {wv[d][0][p], wv[d][1][p]};
+                        float dl[2][NTOK];
+                        chunk_dots_tok<2, CNT, NTOK>(wl, xl, kl, dl);
+                        const float s0 = f16_to_f32(sv[d][0][p]), s1 = f16_to_f32(sv[d][1][p]);
+#pragma unroll
+                        for (int j = 0; j < CNT; ++j) {
+                            acc[0][j] = fmaf(dl[0][j], s0, acc[0][j]);
+                            acc[1][j] = fmaf(dl[1][j], s1, acc[1][j]);
+                        }
+                    }
+                    }
+#pragma unroll
+                    for (int j = 0; j < CNT; ++j) {
+                        racc[j * M + m] = acc[0][j];
+                        racc[V / 2 + j * M + m] = acc[1][j];
+                    }
+                };
+                dispatch_count<NTOK>(cnt, stage);
+            }
+            issue(d, g0 + m + DEPTH);
+        }
+        reduce_values<V>(racc);
+#pragma unroll
+        for (int jj = 0; jj < N; ++jj) {
+            const float up = across32(racc[jj]);
+            const int vi = reduced_value<V>(jj, lane);
+            const int j = vi / M, m = vi % M;
+            const int i = sp.part + (g0 + m) * sp.wpe;
+            if (value_writer<V>(jj, lane) && vi < NTOK * M && j < cnt && g0 + m < nsteps)
+                a.out[(size_t)orow[j] * a.out_ld + ht_pos(i, CI)] = swiglu(racc[jj], up);
+        }
+    }
+}
+
+template <int P, int RD, int M, int DEPTH, int NTOK>
+__global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
+{
+    static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
+    constexpr int V = next_pow2(RD * M * NTOK), N = reduced_count(V);
+    static_assert(V <= 64, "at most 64 values per reduction");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32;
+    const int U = a.n_union[0];
+    const T1Split sp = mt_split(a, blockIdx.x * 4 + wave, gridDim.x * 4, U, a.N / RD);
+    const int nsteps = sp.nsteps;
+    if (nsteps == 0) return;
+    const uint8_t *wb;
+    const uint16_t *sb;
+    const int32_t *list;
+    const int cnt = min(entry_info(a, sp.ue, wb, sb, list), NTOK);
+    if (cnt <= 0) return;
+    const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
+    uint32_t vw[P], vs[P];
+    lane_offsets<P>(lane, C, vw, vs);
+
+    // the h chunks of the entry's tokens (chunk-transposed rows), in registers
+    float hv[NTOK][P][32], kh[NTOK][P];
+    int orow[NTOK];
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) {
+        int in_row = 0, out_row = 0;
+        if (j < cnt) token_rows(a, list, j, in_row, out_row);
+        orow[j] = out_row;
+        const float4 *hrow = reinterpret_cast<const float4 *>(a.in + (size_t)in_row * K);
+#pragma unroll
+        for (int p = 0; p < P; ++p) load_chunk32(hrow + min(lane + 64 * p, C - 1), C, hv[j][p]);
+    }
+    uint4 wv[DEPTH][RD][P];
+    uint16_t sv[DEPTH][RD][P];
+    auto issue = [&](int d, int step) {
+        int rows[RD];
+#pragma unroll
+        for (int r = 0; r < RD; ++r) rows[r] = (sp.part + step * sp.wpe) * RD + r;
+        load_stage<RD, P>(R, rows, step < nsteps, rb, sbs, vw, vs, wv[d], sv[d]);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, d);
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j)
+#pragma unroll
+        for (int p = 0; p < P; ++p) kh[j][p] = chunk_K(hv[j][p]);
+    for (int g0 = 0; g0 < nsteps; g0 += M) {
+        float racc[V];  // [token][m][RD], zero padded to a power of two
+#pragma unroll
+        for (int i = 0; i < V; ++i) racc[i] = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int d = m % DEPTH;
+            if (g0 + m < nsteps) {
+                auto stage = [&](auto cnt_c) {
+                    constexpr int CNT = decltype(cnt_c)::value;
+                    float acc[RD][NTOK];
+#pragma unroll
+                    for (int r = 0; r < RD; ++r)
+#pragma unroll
+                        for (int j = 0; j < CNT; ++j) acc[r][j] = 0.f;
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        float xl[NTOK][32], kl[NTOK];
+#pragma unroll
+                        for (int j = 0; j < CNT; ++j) {
+                            kl[j] = kh[j][p];
+#pragma unroll
+                            for (int i = 0; i < 32; ++i) xl[j][i] = hv[j][p][i];
+                        }
+                        uint4 wl[RD];
+#pragma unroll
+                        for (int r = 0; r < RD; ++r) wl[r] = wv[d][r][p];
+                        float dl[RD][NTOK];
+                        chunk_dots_tok<RD, CNT, NTOK>(wl, xl, kl, dl);
+#pragma unroll
+                        for (int r = 0; r < RD; ++r) {
+                            const float sc = f16_to_f32(sv[d][r][p]);
+#pragma unroll
+                            for (int j = 0; j < CNT; ++j) acc[r][j] = fmaf(dl[r][j], sc, acc[r][j]);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < RD; ++r)
+#pragma unroll
+                        for (int j = 0; j < CNT; ++j) racc[(j * M + m) * RD + r] = acc[r][j];
+                };
+                dispatch_count<NTOK>(cnt, stage);
+            }
+            issue(d, g0 + m + DEPTH);
+        }
+        reduce_values<V>(racc);
+#pragma unroll
+        for (int jj = 0; jj < N; ++jj) {
+            const int vi = reduced_value<V>(jj, lane);
+            const int j = vi / (M * RD), m = (vi / RD) % M, r = vi % RD;
+            if (value_writer<V>(jj, lane) && vi < NTOK * M * RD && j < cnt && g0 + m < nsteps)
+                a.out[(size_t)orow[j] * a.out_ld + (sp.part + (g0 + m) * sp.wpe) * RD + r] =
+                    racc[jj];
+        }
+    }
+}
+
+template <int NTOK>
+static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs a, float *h,
+                                float *o, hipStream_t st, Marks *mk)
+{
+    const int entries = a.cap + a.n_shared;
+    const int cus = device_cu_count();
+    if (mk) mk->mark(st);
+    {
+        // one 4-wave workgroup per CU (eight waves measured slower: more
+        // concurrent streams lose DRAM locality)
+        constexpr int M = 4, DEPTH = 2, WPB = 4;
+        a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
+        a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
+        a.in = io.x; a.in_by_slot = 0;
+        a.out = h; a.out_ld = L.I;
+        const int P = (L.H / 32 + 63) / 64;
+        const dim3 grid(std::max(cus, (entries + WPB - 1) / WPB)), block(WPB * 64);
+        const size_t lds = (size_t)io.T * (L.H + L.H / 32) * 4;
+#define COLI_GUM(P_) \
+        if (P == P_) hipLaunchKernelGGL((gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB>), grid, block, lds, st, a);
+        COLI_GUM(1) COLI_GUM(2) COLI_GUM(3) COLI_GUM(4)
+#undef COLI_GUM
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (mk) mk->mark(st);
+    {
+        constexpr int RD = 4, M = (NTOK >= 4 ? 2 : 4), DEPTH = 2;
+        a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
+        a.N = L.H; a.K = L.I; a.upe = L.H;
+        a.in = h; a.in_by_slot = 1;
+        a.out = o; a.out_ld = L.H;
+        const int P = (L.I / 32 + 63) / 64;
+        const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
+#define COLI_DNM(P_) \
+        if (P == P_) hipLaunchKernelGGL((down_mt_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, 0, st, a);
+        COLI_DNM(1) COLI_DNM(2) COLI_DNM(3) COLI_DNM(4)
+#undef COLI_DNM
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (mk) mk->mark(st);
+    hipError_t err = launch_combine(o, io.w, io.T, L.k, L.H, L.n_shared, io.y, st);
+    if (mk) mk->mark(st);
+    return err;
+}
+
 // T == 1: the streaming kernels.  Launch shapes measured on MI355X with the
 // decode layer (H 6144, I 2048, 9 entries): gate/up runs one 4-wave
 // workgroup per CU (its register ring plus the x chunks allow two waves per
@@ -805,6 +1187,13 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     a.I = L.I;
     const int entries = a.cap + a.n_shared;
     if (T == 1) return launch_f32_t1(L, io, a, h, o, st, mk);
+    // the streaming kernels hold every token's x in LDS: at most
+    // 4 * (8192 + 256) * 4 = 132 KB of the 160 KB a workgroup may use
+    static_assert(kStreamTMax * (COLI_MAX_H_DEV + COLI_MAX_H_DEV / 32) * 4 <= 160 * 1024, "LDS");
+    if (T <= kStreamTMax) {
+        if (T == 2) return launch_f32_mt<2>(L, io, a, h, o, st, mk);
+        return launch_f32_mt<4>(L, io, a, h, o, st, mk);
+    }
     // gate/up + SwiGLU -> h (chunk-transposed rows)
     a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
     a.N = 2 * L.I; a.K = L.H; a.upe = L.I;

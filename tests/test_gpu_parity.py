@@ -187,6 +187,11 @@ def test_determinism_and_batch_invariance(mode):
         s = lay.run(x[t:t + 1], mode)
         assert np.array_equal(s["ids"][0], a["ids"][t])
         assert np.array_equal(s["y"][0].view(np.uint32), a["y"][t].view(np.uint32)), (mode, t)
+    # small batches (the streaming kernels for T <= 4): identical bits too
+    for t0, n in ((0, 2), (5, 3), (20, 4)):
+        s = lay.run(x[t0:t0 + n], mode)
+        assert np.array_equal(s["ids"], a["ids"][t0:t0 + n])
+        assert np.array_equal(s["y"].view(np.uint32), a["y"][t0:t0 + n].view(np.uint32)), (mode, n)
     # permuting the tokens permutes the outputs
     p = np.random.default_rng(5).permutation(24)
     c = lay.run(x[p], mode)
