@@ -81,6 +81,8 @@ def main():
                     choices=["decode", "verify", "prefill512", "prefill4096x8", "tiny"])
     ap.add_argument("--layers", type=int, default=None, help="resident layer copies cycled (decode/verify)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--act-mode", choices=["f32", "i8"], default=None,
+                    help="arithmetic family (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -116,7 +118,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     H, I, E, k, T = w.H, w.I, w.E, w.k, w.T
-    mode = coli.ACT_I8 if w.act_mode == "i8" else coli.ACT_F32
+    fam = args.act_mode or w.act_mode
+    mode = coli.ACT_I8 if fam == "i8" else coli.ACT_F32
     stacked = w.layers > 1
     defaults = {"decode": (256, 32), "verify": (128, 16), "prefill512": (20, 4),
                 "prefill4096x8": (4, 1), "tiny": (256, 32)}
@@ -204,7 +207,7 @@ def main():
     hip = Hip()
     names = coli.forward_kernel_names(mode, T)
     nk = len(names)
-    dom = 0 if mode == coli.ACT_F32 else names.index("ggemm_kernel<gateup>")
+    dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
     prof_steps = min(K, 64)
     ev = [[hip.event() for _ in range(nk + 1)] for _ in range(prof_steps * (w.layers if stacked else 1))]
     union_sizes = []
@@ -244,6 +247,8 @@ def main():
     gateup_bytes = n_exp * (2 * I * (H // 2) + 2 * I * (H // 64) * 2)
     if mode == coli.ACT_F32:
         algo_bytes = gateup_bytes + T * H * 4 + R * I * 4
+    elif "i8v" in names[dom]:  # small-batch integer kernels hand h on in fp32
+        algo_bytes = gateup_bytes + T * H + T * (H // 64) * 4 + R * I * 4
     else:
         algo_bytes = gateup_bytes + T * H + T * (H // 64) * 4 + R * I + R * (I // 64) * 4
     algo_ops = 2.0 * R * 2 * I * H  # int8 ops (or fp32 flops) of the gate/up matmul

@@ -155,7 +155,10 @@ int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int
  * act_mode COLI_ACT_I8: x and h quantised per token per 64-group to int8
  *   (scale = amax / 127, q = clamp(rint(v / scale), -127, 127), amax == 0
  *   gives scale 0), exact int32 accumulators per 64-group, output
- *   sum_g acc * act_scale * weight_scale in fp32.
+ *   sum_g acc * act_scale * weight_scale in fp32, the groups added in
+ *   ascending order by one fp32 FMA chain per output.  Every batch size runs
+ *   this same arithmetic (streaming kernels for T <= 4, the grouped GEMM
+ *   above), so a token's y does not depend on its batch.
  * Inputs are the outputs of coli_moe_route and coli_moe_union for the same
  * x and T; y [T][H] fp32 is written.
  * acc_dump (COLI_ACT_I8 only; NULL in production) receives, for every row r
@@ -176,7 +179,7 @@ int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
 /* Profiling variant of coli_moe_forward: the same work, and in addition
  * events[i] (hipEvent_t values created by the caller) is recorded on
  * hip_stream before the i-th kernel the call launches and events[n] after
- * its last kernel, n = coli_moe_forward_kernel_count(act_mode).  Requires
+ * its last kernel, n = coli_moe_forward_kernel_count(act_mode, T).  Requires
  * n_events >= n + 1 (else COLI_E_ARG, nothing enqueued).  For measurement
  * only; the production path is coli_moe_forward. */
 int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
@@ -187,13 +190,13 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
                               int32_t *acc_dump, void **events, int32_t n_events,
                               void *hip_stream);
 
-/* Number of kernels coli_moe_forward launches for act_mode (0 if unknown),
- * and the name of the i-th one for a batch of T tokens: the HIP kernel
- * function as it appears in a profiler trace (template arguments omitted),
- * which depends on T in the fp32 family (T == 1 runs the single-token
- * streaming kernels, 2 <= T <= 4 the small-batch streaming kernels).  NULL
- * if out of range. */
-int coli_moe_forward_kernel_count(int32_t act_mode);
+/* Number of kernels coli_moe_forward launches for act_mode and a batch of
+ * T tokens without acc_dump (0 if the mode is unknown), and the name of the
+ * i-th one: the HIP kernel function as it appears in a profiler trace
+ * (template arguments omitted).  Both depend on T: T == 1 and 2 <= T <= 4
+ * run streaming kernels in the fp32 family, T <= 4 streaming kernels in the
+ * int8 family (no tile schedule).  NULL if out of range. */
+int coli_moe_forward_kernel_count(int32_t act_mode, int32_t T);
 const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
 
 /* Size in bytes of the acc_dump buffer of coli_moe_forward (0 if invalid). */

@@ -63,7 +63,7 @@ def lib():
                                  ctypes.c_int),
             "coli_moe_forward_profiled": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp,
                                            vp, i32, vp], ctypes.c_int),
-            "coli_moe_forward_kernel_count": ([i32], ctypes.c_int),
+            "coli_moe_forward_kernel_count": ([i32, i32], ctypes.c_int),
             "coli_moe_forward_kernel_name": ([i32, i32, i32], ctypes.c_char_p),
             "coli_moe_acc_dump_bytes": ([i32, i32, i32, i32, i32], sz),
             "coli_moe_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -150,7 +150,7 @@ def forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, ac
 
 
 def forward_kernel_names(act_mode, T=2):
-    n = lib().coli_moe_forward_kernel_count(act_mode)
+    n = lib().coli_moe_forward_kernel_count(act_mode, T)
     return [lib().coli_moe_forward_kernel_name(act_mode, T, i).decode() for i in range(n)]
 
 

@@ -178,7 +178,7 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int32_t T,
     if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return COLI_E_UNSUPPORTED;
     if (acc_dump && act_mode != COLI_ACT_I8) return COLI_E_ARG;
     if (mk) {
-        const int need = (act_mode == COLI_ACT_I8 ? kForwardKernelsI8 : kForwardKernelsF32) + 1;
+        const int need = forward_kernel_count(act_mode, T) + 1;
         if (!mk->ev || mk->n < need) return COLI_E_ARG;
         for (int i = 0; i < need; ++i)
             if (!mk->ev[i]) return COLI_E_ARG;
@@ -232,28 +232,23 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
                         y, workspace, workspace_bytes, acc_dump, hip_stream, &mk);
 }
 
-int coli_moe_forward_kernel_count(int32_t act_mode)
+int coli_moe_forward_kernel_count(int32_t act_mode, int32_t T)
 {
-    return act_mode == COLI_ACT_F32 ? kForwardKernelsF32
-           : act_mode == COLI_ACT_I8 ? kForwardKernelsI8 : 0;
+    return forward_kernel_count(act_mode, T);
 }
 
 const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
 {
-    static const char *f32_one[kForwardKernelsF32] = {"gateup_t1_kernel", "down_t1_kernel",
-                                                      "combine_kernel"};
-    static const char *f32_few[kForwardKernelsF32] = {"gateup_mt_kernel", "down_mt_kernel",
-                                                      "combine_kernel"};
-    static const char *f32[kForwardKernelsF32] = {"gateup_f32_kernel", "down_f32_kernel",
-                                                  "combine_kernel"};
-    static const char *i8[kForwardKernelsI8] = {"quant_rows_kernel", "schedule_kernel",
-                                                "ggemm_kernel<gateup>", "ggemm_kernel<down>",
-                                                "combine_kernel"};
-    if (i < 0) return nullptr;
-    if (act_mode == COLI_ACT_F32 && i < kForwardKernelsF32)
-        return T == 1 ? f32_one[i] : T <= 4 ? f32_few[i] : f32[i];
-    if (act_mode == COLI_ACT_I8 && i < kForwardKernelsI8) return i8[i];
-    return nullptr;
+    static const char *f32_one[] = {"gateup_t1_kernel", "down_t1_kernel", "combine_kernel"};
+    static const char *f32_few[] = {"gateup_mt_kernel", "down_mt_kernel", "combine_kernel"};
+    static const char *f32[] = {"gateup_f32_kernel", "down_f32_kernel", "combine_kernel"};
+    static const char *i8_few[] = {"quant_rows_kernel", "gateup_i8v_kernel", "down_i8v_kernel",
+                                   "combine_kernel"};
+    static const char *i8[] = {"quant_rows_kernel", "schedule_kernel", "ggemm_kernel<gateup>",
+                               "ggemm_kernel<down>", "combine_kernel"};
+    if (i < 0 || i >= forward_kernel_count(act_mode, T)) return nullptr;
+    if (act_mode == COLI_ACT_F32) return T == 1 ? f32_one[i] : T <= 4 ? f32_few[i] : f32[i];
+    return T <= kI8StreamTMax ? i8_few[i] : i8[i];
 }
 
 int coli_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps, void *hip_stream)

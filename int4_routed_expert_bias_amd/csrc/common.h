@@ -77,6 +77,9 @@ struct Workspace {
 };
 
 constexpr int kTileM = 64;  // token rows per integer-GEMM tile
+// Batches up to this size run the streaming kernels of the integer family
+// (and, for T >= 2, of the fp32 family).
+constexpr int kI8StreamTMax = 4;
 
 // Router: batches of up to kGemvTMax tokens stream Wr once (GEMV, fp32
 // logits); larger batches run an fp64 MFMA GEMM split over K whose fp64
@@ -130,6 +133,9 @@ inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, in
         w.qh = p; p = align256(p + (size_t)w.R * I);
         w.sh = p; p = align256(p + (size_t)w.R * (I / 64) * 4);
         w.tiles = p; p = align256(p + (size_t)(w.max_tiles + 1) * 8);
+        if (T <= kI8StreamTMax) {  // the small-batch kernels pass h in fp32
+            w.h = p; p = align256(p + (size_t)w.R * I * 4);
+        }
     }
     w.forward_end = p;
     w.total = w.route_end > w.forward_end ? w.route_end : w.forward_end;
@@ -203,11 +209,20 @@ struct ForwardIO {
     int32_t *acc_dump; DumpLayout dump;
 };
 
-constexpr int kForwardKernelsF32 = 3;  // gate/up GEMV, down GEMV, combine
-constexpr int kForwardKernelsI8 = 5;   // quant, schedule, gate/up GEMM, down GEMM, combine
+// Kernels one forward call launches (without acc_dump): fp32 family gate/up,
+// down, combine; integer family quant, [schedule,] gate/up, down, combine
+// (batches of at most kI8StreamTMax tokens stream without a tile schedule).
+inline int forward_kernel_count(int act_mode, int T)
+{
+    if (act_mode == 0) return 3;
+    if (act_mode == 1) return T <= kI8StreamTMax ? 4 : 5;
+    return 0;
+}
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
+hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
+                                   const float *sx, float *h, float *o, hipStream_t st, Marks *mk);
 hipError_t launch_combine(const float *o, const float *w, int32_t T, int32_t k, int32_t H,
                           int32_t n_shared, float *y, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,

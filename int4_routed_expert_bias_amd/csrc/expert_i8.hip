@@ -127,12 +127,12 @@ constexpr int kBN = 128;
 
 // LDS of one workgroup: two stages of KG groups (row strides padded by 16
 // bytes, which keeps the fragment reads free of bank conflicts).
-template <int BM, int KG>
+template <int BM, int KG, bool UB>
 struct __attribute__((aligned(16))) GemmLds {
-    static constexpr int AS = KG * 64 + 16;  // activation row stride (bytes)
-    static constexpr int BS = KG * 32 + 16;  // packed weight row stride (bytes)
+    static constexpr int AS = KG * 64 + 16;             // activation row stride (bytes)
+    static constexpr int BS = UB ? KG * 64 + 16 : KG * 32 + 16;  // weight row stride
     alignas(16) uint8_t a[2][BM * AS];
-    alignas(16) uint8_t b[2][kBN * BS];
+    alignas(16) uint8_t b[2][kBN * BS];  // packed int4, or unpacked 16 x code (UB)
     alignas(16) float sx[2][KG][BM];
     alignas(16) float sw[2][KG][kBN];  // weight scale / 16
     alignas(16) float amax[2][BM];
@@ -203,12 +203,15 @@ __device__ __forceinline__ void tile_row(const I8Args &a, const TileInfo &ti, in
     }
 }
 
-template <int BM, int KG, bool GATEUP, bool DUMP>
-__global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
+// UB: the weight codes are unpacked once, when a stage is written to LDS,
+// instead of by each of the two waves that read a column block.  OCC: the
+// workgroups per CU the register budget is sized for.
+template <int BM, int KG, bool GATEUP, bool DUMP, bool UB = false, int OCC = 2>
+__global__ __launch_bounds__(256, OCC) void ggemm_kernel(I8Args a)
 {
     constexpr int MT = BM / 32;               // m-tiles per wave
     constexpr int kKG = KG;
-    using Lds = GemmLds<BM, KG>;
+    using Lds = GemmLds<BM, KG, UB>;
     constexpr int kAS = Lds::AS, kBS = Lds::BS;
     __shared__ Lds sm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -326,8 +329,15 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
                 make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
         }
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            *reinterpret_cast<uint4 *>(sm.b[buf] + (tid / LB + (256 / LB) * i) * kBS + b_byte) = rbw[i];
+        for (int i = 0; i < NB; ++i) {
+            uint8_t *dst = sm.b[buf] + (tid / LB + (256 / LB) * i) * kBS;
+            if constexpr (UB) {
+                *reinterpret_cast<v4i *>(dst + 2 * b_byte) = unpack_b(make_uint2(rbw[i].x, rbw[i].y));
+                *reinterpret_cast<v4i *>(dst + 2 * b_byte + 16) = unpack_b(make_uint2(rbw[i].z, rbw[i].w));
+            } else {
+                *reinterpret_cast<uint4 *>(dst + b_byte) = rbw[i];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kKG; ++j) {
             const int g = g0 + j;
@@ -384,8 +394,11 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
                 float sw[4], sx[MT][4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    bv[nt] = unpack_b(*reinterpret_cast<const uint2 *>(
-                        sm.b[buf] + (lb[nt] + n) * kBS + j * 32 + 8 * q));
+                    if constexpr (UB)
+                        bv[nt] = *reinterpret_cast<const v4i *>(sm.b[buf] + (lb[nt] + n) * kBS + j * 64 + 16 * q);
+                    else
+                        bv[nt] = unpack_b(*reinterpret_cast<const uint2 *>(
+                            sm.b[buf] + (lb[nt] + n) * kBS + j * 32 + 8 * q));
                     sw[nt] = sm.sw[buf][j][lb[nt] + n];
                 }
                 // m-tiles in pairs: fewer MFMA results live at once
@@ -516,6 +529,11 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
                        L.H, qx, sx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // small batches: streaming kernels with the same arithmetic (the test-only
+    // accumulator dump is written by the GEMM path)
+    if (T <= kI8StreamTMax && !io.acc_dump)
+        return launch_forward_i8_small(L, io, qx, sx, reinterpret_cast<float *>(io.ws + lay.h), o,
+                                       st, mk);
     if (mk) mk->mark(st);
     // 64-row tiles: measured on MI355X they beat 128-row tiles even for dense
     // entries (three workgroups per CU instead of two) and waste fewer rows on

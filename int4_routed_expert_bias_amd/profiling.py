@@ -32,8 +32,8 @@ COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
 COPY_KERNEL = "copyBuffer"  # the runtime blit kernel behind a device-to-device tensor copy
 
 
-def source_hash(files=("expert_f32.hip", "expert_i8.hip", "common.h", "route.hip",
-                       "union.hip", "combine.hip")) -> str:
+def source_hash(files=("expert_f32.hip", "expert_i8.hip", "expert_i8v.hip", "stream.h",
+                       "common.h", "route.hip", "union.hip", "combine.hip")) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(HERE, "csrc", f), "rb") as fp:

@@ -142,6 +142,25 @@ def test_verify_batch_full_size():
         assert np.array_equal(single["y"][0].view(np.uint32), out["y"][t].view(np.uint32)), t
 
 
+def test_decode_and_verify_int8_family():
+    """The int8 family at decode and verify sizes (the small-batch streaming
+    kernels): outputs against the oracle, and every token's output equal,
+    bit for bit, to the one the grouped GEMM gives it inside a prefill-sized
+    batch (one function for draft, verify and prefill)."""
+    lay = workload_layer("verify")
+    x = synth.workload_x("verify")
+    out, near, err = full_check(lay, x, coli.ACT_I8)
+    assert near == 0
+    single = lay.run(x[2:3], coli.ACT_I8)
+    assert np.array_equal(single["y"][0].view(np.uint32), out["y"][2].view(np.uint32))
+    # the same tokens inside a batch of 40 (T > 4: grouped GEMM path)
+    big = np.concatenate([x, synth.activations(x.shape[1], 36, wid=71)], axis=0)
+    b = lay.run(big, coli.ACT_I8)
+    for t in range(x.shape[0]):
+        assert np.array_equal(b["ids"][t], out["ids"][t])
+        assert np.array_equal(b["y"][t].view(np.uint32), out["y"][t].view(np.uint32)), t
+
+
 def test_prefill512_sampled():
     lay = workload_layer("prefill512")
     x = synth.workload_x("prefill512")
