@@ -46,6 +46,7 @@ def _setup(L):
         "orc_select": ([i32, i32, i32, vp, vp, vp, vp, vp], None),
         "orc_route": ([vp, vp, i32, vp, vp, vp, vp], None),
         "orc_union": ([i32, i32, i32, vp, vp, vp, vp, vp], None),
+        "orc_prune_topp": ([i32, i32, i32, ctypes.c_float, vp, vp, vp], None),
         "orc_quant_i8": ([i64, vp, vp, vp], None),
         "orc_expert_f32": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], None),
         "orc_expert_i8": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], None),
@@ -143,6 +144,20 @@ class Oracle:
         lg = np.empty((T, layer.E), np.float32)
         s = np.empty((T, layer.E), np.float32)
         self.L.orc_route(layer.ref, _p(x), T, _p(ids), _p(w), _p(lg), _p(s))
+        return ids, w, lg, s
+
+    def prune_topp(self, ids: np.ndarray, w: np.ndarray, scores: np.ndarray, p: float):
+        """Top-p pruning of a top-k selection (copies; see orc_prune_topp)."""
+        ids = np.array(ids, np.int32, copy=True)
+        w = np.array(w, np.float32, copy=True)
+        s = np.ascontiguousarray(scores, np.float32)
+        T, k = ids.shape
+        self.L.orc_prune_topp(s.shape[1], k, T, float(p), _p(s), _p(ids), _p(w))
+        return ids, w
+
+    def route_topp(self, layer: Layer, x: np.ndarray, p: float):
+        ids, w, lg, s = self.route(layer, x)
+        ids, w = self.prune_topp(ids, w, s, p)
         return ids, w, lg, s
 
     def union(self, ids: np.ndarray, E: int):

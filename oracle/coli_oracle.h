@@ -48,6 +48,8 @@ void orc_select(int32_t E, int32_t k, int32_t T, const float *logits, const floa
                 int32_t *ids, float *w, float *scores);
 void orc_route(const orc_layer *L, const float *x, int32_t T, int32_t *ids, float *w,
                float *logits, float *scores);
+void orc_prune_topp(int32_t E, int32_t k, int32_t T, float p, const float *scores, int32_t *ids,
+                    float *w);
 void orc_union(int32_t T, int32_t k, int32_t E, const int32_t *ids, int32_t *union_ids,
                int32_t *offsets, int32_t *slots, int32_t *n_union);
 

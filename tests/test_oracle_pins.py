@@ -395,9 +395,70 @@ def pin_relabel_and_independence(o):
         assert np.array_equal(f32_bits(yp), f32_bits(y[p]))
 
 
+def pin_topp(o):
+    """Adaptive top-p pruning of the top-k selection, checked by properties
+    in exact rational arithmetic: the kept experts are the shortest prefix of
+    the selection whose weights reach p, and the kept weights are the
+    original ones rescaled to sum to one."""
+    for (T, k, E, wid) in ((6, 8, 32, 100), (5, 4, 9, 101), (4, 16, 64, 102)):
+        A, lay = tiny_layer(H=64, I=64, E=E, k=k, wid=wid)
+        A["router_w"] *= 40.0  # spread the scores so that prefixes differ
+        x = RNG.standard_normal((T, 64)).astype(np.float32)
+        ids, w, _, sc = o.route(lay, x)
+        for p in (1e-9, 0.2, 0.5, 0.7, 0.9, 0.99):
+            pi, pw = o.prune_topp(ids, w, sc, p)
+            for t in range(T):
+                kp = int((pi[t] >= 0).sum())
+                assert 1 <= kp <= k
+                assert np.array_equal(pi[t, :kp], ids[t, :kp]), (p, t)
+                assert np.all(pi[t, kp:] == -1) and np.all(pw[t, kp:] == 0.0)
+                csum = [Fraction(0)]
+                for j in range(k):
+                    csum.append(csum[-1] + Fraction(float(w[t, j])))
+                pf = Fraction(float(np.float32(p)))
+                eps = Fraction(1, 10 ** 6)
+                # reaches p with kp experts, not with kp - 1 (away from rounding)
+                if kp < k or csum[k] >= pf + eps:
+                    assert csum[kp] >= pf - eps, (p, t, kp)
+                if kp > 1:
+                    assert csum[kp - 1] < pf + eps, (p, t, kp)
+                tot = sum(Fraction(float(v)) for v in pw[t, :kp])
+                assert abs(tot - 1) < Fraction(1, 10 ** 6)
+                for j in range(kp):
+                    r_new = Fraction(float(pw[t, j])) / Fraction(float(pw[t, 0]))
+                    r_old = Fraction(float(w[t, j])) / Fraction(float(w[t, 0]))
+                    assert abs(r_new - r_old) <= Fraction(1, 10 ** 5) * r_old
+            if p == 1e-9:
+                assert np.all((pi >= 0).sum(axis=1) == 1) and np.all(pw[:, 0] == 1.0)
+        # p >= 1: the selection is unchanged, bit for bit
+        for p in (1.0, 1.5):
+            pi, pw = o.prune_topp(ids, w, sc, p)
+            assert np.array_equal(pi, ids) and np.array_equal(f32_bits(pw), f32_bits(w))
+    # union of a pruned selection: brute force over the kept slots only
+    ids = np.array([[4, 2, -1, -1], [2, -1, -1, -1], [7, 4, 1, -1]], np.int32)
+    u, off, slots, nu = o.union(ids, 8)
+    flat = ids.reshape(-1)
+    kept = [s_ for s_ in range(flat.size) if flat[s_] >= 0]
+    assert nu == 4 and list(u[:nu]) == [1, 2, 4, 7]
+    assert off[nu] == len(kept) and all(v == len(kept) for v in off[nu:])
+    for i, e in enumerate(u[:nu]):
+        assert list(slots[off[i]:off[i + 1]]) == [s_ for s_ in kept if flat[s_] == e]
+    # forward: a dropped slot contributes exactly nothing (same bits as the
+    # same expert list with that slot's weight set to zero)
+    for mode in (oracle_mod.ACT_F32, oracle_mod.ACT_I8):
+        A, lay = tiny_layer(H=128, I=64, E=6, k=3, wid=103)
+        x = RNG.standard_normal((2, 128)).astype(np.float32)
+        ids, w, _, sc = o.route(lay, x)
+        pi, pw = o.prune_topp(ids, w, sc, 0.3)
+        z = np.where(pi >= 0, pi, ids).astype(np.int32)
+        y1 = o.forward(lay, x, pi, pw, mode)
+        y2 = o.forward(lay, x, z, pw, mode)
+        assert np.array_equal(f32_bits(y1), f32_bits(y2)), mode
+
+
 PINS = [pin_f16, pin_int4, pin_logits, pin_sigmoid, pin_select_brute, pin_select_special,
         pin_union, pin_quant, pin_swiglu, pin_f32_expert_exact, pin_i8_expert, pin_combine,
-        pin_rmsnorm, pin_relabel_and_independence]
+        pin_rmsnorm, pin_relabel_and_independence, pin_topp]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -465,6 +526,11 @@ MUTANTS = [
     ("gate/up swapped", "float gf = (float)ag, uf = (float)au;", "float gf = (float)au, uf = (float)ag;"),
     ("i8 gate/up swapped", "float gf = (float)val[0], uf = (float)val[1];",
      "float gf = (float)val[1], uf = (float)val[0];"),
+    ("topp keeps one more", "                kp = m;\n", "                kp = m < k ? m + 1 : m;\n"),
+    ("topp not renormalised", "wt[j] = scores[(size_t)t * E + it[j]] / sum;", "wt[j] = wt[j];"),
+    ("topp drops from the front", "if (j < kp) {\n                wt[j]", "if (j >= k - kp) {\n                wt[j]"),
+    ("union counts dropped slots", "    for (int32_t u = U; u <= cap; ++u) offsets[u] = run;",
+     "    for (int32_t u = U; u <= cap; ++u) offsets[u] = n;"),
 ]
 
 
