@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--act-mode", choices=["f32", "i8"], default=None,
                     help="arithmetic family (default: the workload's own)")
+    ap.add_argument("--topp", type=float, default=None,
+                    help="adaptive expert top-p router (coli_moe_route_topp) instead of top-k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -164,10 +166,10 @@ def main():
             resid.copy_(xs[0])
             for l, lay in enumerate(layers):
                 coli.rmsnorm(resid, xhat, T, H, 1e-6)
-                coli.run_layer(lay, xhat, bufs)
+                coli.run_layer(lay, xhat, bufs, top_p=args.topp)
                 coli.add_inplace(resid, bufs.y, T * H)
         else:
-            coli.run_layer(layers[s % NL], xs[s], bufs)
+            coli.run_layer(layers[s % NL], xs[s], bufs, top_p=args.topp)
 
     # ---- warmup ----------------------------------------------------------
     for s in range(W):
@@ -223,7 +225,10 @@ def main():
             x_in = xs[W + s] if not stacked else xhat
             if stacked:
                 coli.rmsnorm(resid, xhat, T, H, 1e-6)
-            coli.route(lay, x_in, T, bufs.ids, bufs.w, bufs.workspace)
+            if args.topp is None:
+                coli.route(lay, x_in, T, bufs.ids, bufs.w, bufs.workspace)
+            else:
+                coli.route_topp(lay, x_in, T, args.topp, bufs.ids, bufs.w, bufs.workspace)
             coli.union(bufs.ids, T, k, E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union)
             coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
                                   bufs.slots, bufs.n_union, mode, bufs.y, bufs.workspace, ev[i])
@@ -288,7 +293,8 @@ def main():
         omode = oracle.ACT_I8 if mode == coli.ACT_I8 else oracle.ACT_F32
         while True:
             xt = xh[done % T:done % T + 1]
-            ids, wt, _, _ = orc.route(olay, xt)
+            ids, wt, _, _ = (orc.route(olay, xt) if args.topp is None
+                             else orc.route_topp(olay, xt, args.topp))
             orc.union(ids, E)
             orc.forward(olay, xt, ids, wt, omode)
             done += 1
@@ -306,7 +312,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.note, "H": H, "I": I, "E": E, "k": k,
                    "T": T, "n_shared": w.n_shared, "layers": NL,
-                   "act_mode": "i8" if mode == coli.ACT_I8 else "f32",
+                   "act_mode": "i8" if mode == coli.ACT_I8 else "f32", "top_p": args.topp,
                    "graph": use_graph, "union_size_mean": round(float(U.mean()), 2),
                    "union_size_minmax": [int(U.min()), int(U.max())],
                    "kernels_us": kernels_us},

@@ -126,19 +126,38 @@ size_t coli_moe_workspace_bytes(int32_t H, int32_t I, int32_t E, int32_t k, int3
 int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *topk_ids,
                    float *topk_w, void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Route with adaptive expert top-p ([Heart] "使えるかどうかの判定材料", knob
+ * list: an adaptive expert top-p, `--topp 0.7`, reading 30-40% fewer expert
+ * bytes; the pages give no formula, this is the library's reading).  The
+ * top-k selection of coli_moe_route, then per token: with the routing
+ * weights w[0..k) in selection order,
+ *   c_m = w[0] + ... + w[m-1]                 (fp32, in order),
+ *   k'  = the least m in [1, k] with c_m >= top_p (k if none),
+ *   topk_ids[t][j] = the selection for j < k', -1 for j >= k',
+ *   topk_w[t][j]   = s[id_j] / (s[id_0] + ... + s[id_{k'-1}]) for j < k',
+ *                    0 for j >= k'.
+ * top_p >= 1 gives exactly coli_moe_route; top_p must be > 0 (COLI_E_ARG
+ * otherwise).  coli_moe_union and coli_moe_forward skip the slots marked -1,
+ * so only the kept experts' weights are read. */
+int coli_moe_route_topp(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                        int32_t *topk_ids, float *topk_w, void *workspace,
+                        size_t workspace_bytes, void *hip_stream);
+
 /* Union ([Start] "토큰당 처리 경로": batch-union of the experts chosen by
  * several tokens; [Hysen] "エンドツーエンドの測定で...": batched expert union).
- * From topk_ids [T][k] (each row holds distinct ids in [0, E)):
+ * From topk_ids [T][k] (each row holds distinct ids in [0, E), or -1 for
+ * a slot the top-p router dropped):
  *   n_union[0]     = U, the number of distinct experts,
  *   union_ids[u]   = the distinct experts in ascending order (u < U),
  *   offsets[u]     = first position in slots of expert union_ids[u],
- *                    offsets[U] = T*k,
+ *                    offsets[U] = n_kept, the number of slots with an expert
+ *                    (T*k without dropped slots),
  *   slots[p]       = slot index t*k + j, grouped by expert in union order,
- *                    ascending within an expert.
+ *                    ascending within an expert (p < n_kept).
  * Capacities: union_ids [min(E, T*k)], offsets [min(E, T*k) + 1],
- * slots [T*k].  Entries past U are set to -1 (union_ids) and T*k (offsets).
- * All results stay on the device.  Out-of-range ids give unspecified
- * (memory-safe) results. */
+ * slots [T*k].  Entries past U are set to -1 (union_ids) and n_kept
+ * (offsets); slots past n_kept are unspecified.  All results stay on the
+ * device.  Other out-of-range ids are skipped like -1 (memory-safe). */
 int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                    int32_t *offsets, int32_t *slots, int32_t *n_union, void *hip_stream);
 
@@ -149,7 +168,8 @@ int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int
  *   g, u = x[t] . W13_e^T    (gate rows, up rows)
  *   h    = g / (1 + exp(-g)) * u                        (SwiGLU, fp32)
  *   o    = h . W2_e^T
- *   y[t] = sum_j topk_w[t][j] * o_(t,j) + o_shared(t)   (j ascending)
+ *   y[t] = sum_j topk_w[t][j] * o_(t,j) + o_shared(t)   (j ascending, slots
+ *          with topk_ids -1 skipped)
  * act_mode COLI_ACT_F32: dot products of fp32 x / h with the dequantised
  *   weights (code * scale), fp32 accumulation.
  * act_mode COLI_ACT_I8: x and h quantised per token per 64-group to int8

@@ -21,7 +21,7 @@ COLI_OK, COLI_E_ARG, COLI_E_SHAPE, COLI_E_ALIGN, COLI_E_WORKSPACE, COLI_E_DEVICE
 
 # every symbol declared in include/coli_moe.h
 EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
-           "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
+           "coli_moe_route_topp", "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
            "coli_rmsnorm", "coli_add_inplace")
@@ -58,6 +58,7 @@ def lib():
             "coli_moe_abi_version": ([], ctypes.c_int),
             "coli_moe_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
             "coli_moe_route": ([vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "coli_moe_route_topp": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp], ctypes.c_int),
             "coli_moe_union": ([vp, i32, i32, i32, vp, vp, vp, vp, vp], ctypes.c_int),
             "coli_moe_forward": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp, vp],
                                  ctypes.c_int),
@@ -121,6 +122,12 @@ def route(layer, x, T, ids, w, workspace, workspace_nbytes=None, stream=None):
     nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
     _check(lib().coli_moe_route(layer.ref, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(workspace), nb,
                                 _stream(stream)), "coli_moe_route")
+
+
+def route_topp(layer, x, T, top_p, ids, w, workspace, workspace_nbytes=None, stream=None):
+    nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    _check(lib().coli_moe_route_topp(layer.ref, _ptr(x), T, float(top_p), _ptr(ids), _ptr(w),
+                                     _ptr(workspace), nb, _stream(stream)), "coli_moe_route_topp")
 
 
 def union(ids, T, k, E, union_ids, offsets, slots, n_union, stream=None):
@@ -226,10 +233,14 @@ class Buffers:
             self.dump = torch.empty((max(db, 256),), dtype=torch.uint8, device=device)
 
 
-def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None):
-    """route -> union -> forward for x [T][H] (device fp32)."""
+def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None, top_p=None):
+    """route -> union -> forward for x [T][H] (device fp32); top_p selects
+    the adaptive top-p router."""
     T = bufs.T
-    route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+    if top_p is None:
+        route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+    else:
+        route_topp(layer, x, T, top_p, bufs.ids, bufs.w, bufs.workspace, stream=stream)
     union(bufs.ids, T, layer.k, layer.E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union,
           stream=stream)
     forward(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,

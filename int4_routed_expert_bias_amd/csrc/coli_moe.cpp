@@ -134,11 +134,13 @@ const char *coli_moe_strerror(int status)
 
 int coli_moe_device_check(void) { return device_check(); }
 
-int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *topk_ids,
-                   float *topk_w, void *workspace, size_t workspace_bytes, void *hip_stream)
+static int route_impl(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                      int32_t *topk_ids, float *topk_w, void *workspace, size_t workspace_bytes,
+                      void *hip_stream)
 {
     if (int st = check_layer(L, false)) return st;
     if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    if (!(top_p > 0.0f)) return COLI_E_ARG;  // also rejects NaN
     if (T == 0) return COLI_OK;
     if (!x || !topk_ids || !topk_w || !workspace) return COLI_E_ARG;
     if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(workspace))
@@ -147,8 +149,21 @@ int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *
     if (workspace_bytes < lay.route_end) return COLI_E_WORKSPACE;
     if (int st = device_check()) return st;
     RouteIO io{x, T, topk_ids, topk_w,
-               reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + lay.logits)};
+               reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + lay.logits), top_p};
     return status_of(launch_route(to_dev(L), io, static_cast<hipStream_t>(hip_stream)));
+}
+
+int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *topk_ids,
+                   float *topk_w, void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    return route_impl(L, x, T, 1.0f, topk_ids, topk_w, workspace, workspace_bytes, hip_stream);
+}
+
+int coli_moe_route_topp(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                        int32_t *topk_ids, float *topk_w, void *workspace, size_t workspace_bytes,
+                        void *hip_stream)
+{
+    return route_impl(L, x, T, top_p, topk_ids, topk_w, workspace, workspace_bytes, hip_stream);
 }
 
 int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,

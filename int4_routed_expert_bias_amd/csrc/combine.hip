@@ -7,9 +7,11 @@
 
 namespace coli {
 
-// y[t][n] = sum_j w[t][j] * o[t*k + j][n]  (j ascending, fp32 fma chain)
+// y[t][n] = sum_j w[t][j] * o[t*k + j][n]  (j ascending, fp32 fma chain,
+//           slots dropped by the top-p router -- id -1 -- skipped)
 //           + o[T*k + t][n]                (shared expert, if present)
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o,
+                                                      const int32_t *__restrict__ ids,
                                                       const float *__restrict__ w, int T, int k,
                                                       int H, int n_shared, float *__restrict__ y)
 {
@@ -18,6 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     if (n4 >= H / 4) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
+        if (ids[(size_t)t * k + j] < 0) continue;
         const float wj = w[(size_t)t * k + j];
         const float4 v = reinterpret_cast<const float4 *>(o + ((size_t)t * k + j) * H)[n4];
         acc.x = fmaf(wj, v.x, acc.x);
@@ -32,12 +35,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     reinterpret_cast<float4 *>(y + (size_t)t * H)[n4] = acc;
 }
 
-hipError_t launch_combine(const float *o, const float *w, int32_t T, int32_t k, int32_t H,
-                          int32_t n_shared, float *y, hipStream_t st)
+hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, int32_t T, int32_t k,
+                          int32_t H, int32_t n_shared, float *y, hipStream_t st)
 {
     if (T <= 0) return hipSuccess;
     dim3 grid((H / 4 + 255) / 256, T), block(256);
-    hipLaunchKernelGGL(combine_kernel, grid, block, 0, st, o, w, T, k, H, n_shared, y);
+    hipLaunchKernelGGL(combine_kernel, grid, block, 0, st, o, ids, w, T, k, H, n_shared, y);
     return hipGetLastError();
 }
 

@@ -190,6 +190,7 @@ struct RouteIO {
     const float *x; int32_t T;
     int32_t *ids; float *w;
     float *logits;  // workspace
+    float top_p;    // >= 1: plain top-k
 };
 
 // Compute units of the current device (cached per device on first use).
@@ -223,8 +224,8 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
 hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
                                    const float *sx, float *h, float *o, hipStream_t st, Marks *mk);
-hipError_t launch_combine(const float *o, const float *w, int32_t T, int32_t k, int32_t H,
-                          int32_t n_shared, float *y, hipStream_t st);
+hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, int32_t T, int32_t k,
+                          int32_t H, int32_t n_shared, float *y, hipStream_t st);
 hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
                           hipStream_t st);
 hipError_t launch_add(float *x, const float *y, int64_t n, hipStream_t st);

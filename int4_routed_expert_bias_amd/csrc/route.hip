@@ -196,7 +196,7 @@ template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    const double *__restrict__ part, int S,
                                                    const float *__restrict__ bias, int T, int E,
-                                                   int k, int32_t *__restrict__ ids,
+                                                   int k, float top_p, int32_t *__restrict__ ids,
                                                    float *__restrict__ w)
 {
     __shared__ uint32_t sk[4][COLI_MAX_K_DEV];
@@ -266,8 +266,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (live && lane < k) {
         float sum = 0.f;
         for (int j = 0; j < k; ++j) sum += ss[wv][j];  // fp32, selection order
-        ids[(size_t)t * k + rank] = me;
-        w[(size_t)t * k + rank] = sj / sum;
+        // adaptive top-p: keep the shortest prefix of the selection whose
+        // weights reach top_p (fp32, in order), renormalised over the kept
+        int kp = k;
+        if (top_p < 1.0f) {
+            float c = 0.f;
+            for (int m = 1; m <= k; ++m) {
+                c += ss[wv][m - 1] / sum;
+                if (c >= top_p) {
+                    kp = m;
+                    break;
+                }
+            }
+            sum = 0.f;
+            for (int j = 0; j < kp; ++j) sum += ss[wv][j];
+        }
+        ids[(size_t)t * k + rank] = rank < kp ? me : -1;
+        w[(size_t)t * k + rank] = rank < kp ? sj / sum : 0.f;
     }
 }
 
@@ -302,7 +317,7 @@ hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st)
     const int kpl = (E + 63) / 64;
 #define COLI_TOPK(N) \
     if (kpl <= N) { hipLaunchKernelGGL(topk_kernel<N>, dim3((T + 3) / 4), dim3(256), 0, st, io.logits, \
-                                       part, S, L.router_bias, T, E, L.k, io.ids, io.w); return hipGetLastError(); }
+                                       part, S, L.router_bias, T, E, L.k, io.top_p, io.ids, io.w); return hipGetLastError(); }
     COLI_TOPK(1)
     COLI_TOPK(2)
     COLI_TOPK(4)

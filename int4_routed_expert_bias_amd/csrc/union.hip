@@ -94,6 +94,7 @@ __global__ __launch_bounds__(W * 64) void union_kernel(const int32_t *__restrict
     block_exclusive_scan(upos, E, smem + W * E + 4 * E);
 
     int32_t U = upos[E - 1] + (tmp[E - 1] > 0 ? 1 : 0);
+    const int32_t kept = start[E - 1] + tmp[E - 1];  // slots with an expert
     for (int e = tid; e < E; e += blockDim.x) {
         int32_t c = tmp[e];
         if (c > 0) {
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(W * 64) void union_kernel(const int32_t *__restrict
         }
     }
     for (int u = U + tid; u < cap; u += blockDim.x) union_ids[u] = -1;
-    for (int u = U + tid; u <= cap; u += blockDim.x) offsets[u] = n;
+    for (int u = U + tid; u <= cap; u += blockDim.x) offsets[u] = kept;
     if (tid == 0) n_union[0] = U;
     __syncthreads();
 
@@ -175,11 +176,12 @@ __global__ __launch_bounds__(64) void union_small_kernel(const int32_t *__restri
         union_ids[upos] = sid;
         offsets[upos] = lane;
     }
+    const int kept = __popcll(__ballot(has));  // slots with an expert
     if (lane >= U && lane < cap) union_ids[lane] = -1;
-    if (lane >= U && lane <= cap) offsets[lane] = n;
+    if (lane >= U && lane <= cap) offsets[lane] = kept;
     if (lane == 0) {
         n_union[0] = U;
-        if (cap == 64) offsets[64] = n;
+        if (cap == 64) offsets[64] = kept;
     }
 }
 

@@ -103,6 +103,20 @@ def test_route_argument_errors(L):
     assert route(L, layer(), T=0) == coli.COLI_OK  # no-op, nothing enqueued
 
 
+def test_route_topp_argument_errors(L):
+    def rt(lay, p, T=4, x=FAKE, nb=1 << 20):
+        return L.coli_moe_route_topp(ctypes.byref(lay) if lay is not None else None, x, T,
+                                     ctypes.c_float(p), FAKE, FAKE, FAKE, nb, None)
+    assert rt(None, 0.7) == coli.COLI_E_ARG
+    assert rt(layer(H=100), 0.7) == coli.COLI_E_SHAPE
+    assert rt(layer(), 0.0) == coli.COLI_E_ARG
+    assert rt(layer(), -0.5) == coli.COLI_E_ARG
+    assert rt(layer(), float("nan")) == coli.COLI_E_ARG
+    assert rt(layer(), 0.7, x=MIS) == coli.COLI_E_ALIGN
+    assert rt(layer(), 0.7, nb=16) == coli.COLI_E_WORKSPACE
+    assert rt(layer(), 0.7, T=0) == coli.COLI_OK
+
+
 def test_union_argument_errors(L):
     U = L.coli_moe_union
     assert U(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE

@@ -161,6 +161,62 @@ def test_decode_and_verify_int8_family():
         assert np.array_equal(b["y"][t].view(np.uint32), out["y"][t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
+@pytest.mark.parametrize("name,p", [("tiny", 0.5), ("decode", 0.7), ("verify", 0.7),
+                                    ("verify", 0.3)])
+def test_topp_route_union_forward(name, p, mode):
+    """Adaptive expert top-p: pruned selections equal the oracle's, the union
+    skips the dropped slots, and the layer output matches the oracle on the
+    GPU's own routing; fewer experts are read than with plain top-k."""
+    import torch
+    lay = workload_layer(name)
+    x = synth.workload_x(name)
+    T, k = x.shape[0], lay.k
+    b = coli.Buffers(lay.dev, T, mode)
+    coli.run_layer(lay.dev, torch.from_numpy(x).cuda(), b, top_p=p)
+    torch.cuda.synchronize()
+    gi, gw = b.ids[:T].cpu().numpy(), b.w[:T].cpu().numpy()
+    oi, ow, _, s = orc().route_topp(lay.orc, x, p)
+    ti, tw, _, _ = orc().route(lay.orc, x)
+    for t in range(T):
+        if np.array_equal(gi[t], oi[t]):
+            continue
+        # only at the prune point's rounding boundary may the kept count differ
+        kg, ko = int((gi[t] >= 0).sum()), int((oi[t] >= 0).sum())
+        m = min(kg, ko)
+        assert np.array_equal(gi[t, :m], oi[t, :m]), (t, gi[t], oi[t])
+        c = np.cumsum(tw[t].astype(np.float64))
+        assert abs(c[m - 1] - p) < 1e-5 or abs(c[max(kg, ko) - 1] - p) < 1e-5, (t, gi[t], oi[t])
+    kept = gw[gi >= 0]
+    assert np.all(gw[gi < 0] == 0.0)
+    assert_close(gw, ow, "topk_w (top-p)")
+    nu = int(b.n_union[0].item())
+    u, off, slots, onu = orc().union(gi, lay.E)
+    assert nu == onu and np.array_equal(b.union_ids.cpu().numpy()[:nu], u[:nu])
+    off_g = b.offsets.cpu().numpy()
+    assert np.array_equal(off_g[:nu + 1], off[:nu + 1]) and off_g[nu] == int((gi >= 0).sum())
+    assert np.array_equal(b.slots.cpu().numpy()[:off[nu]], slots[:off[nu]])
+    ref = orc().forward(lay.orc, x, gi, gw, mode)
+    assert_close(b.y[:T].cpu().numpy(), ref, f"y top-p={p} mode={mode}")
+    plain = orc().union(ti, lay.E)[3]
+    assert nu <= plain
+    print(f"{name} p={p}: union {nu} of {plain} experts, kept slots {kept.size}/{T * k}")
+
+
+def test_topp_one_is_plain_topk():
+    import torch
+    lay = workload_layer("tiny")
+    x = torch.from_numpy(synth.workload_x("tiny")).cuda()
+    T = x.shape[0]
+    a = coli.Buffers(lay.dev, T, coli.ACT_F32)
+    b = coli.Buffers(lay.dev, T, coli.ACT_F32)
+    coli.run_layer(lay.dev, x, a)
+    coli.run_layer(lay.dev, x, b, top_p=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.ids, b.ids) and torch.equal(a.w.view(torch.int32), b.w.view(torch.int32))
+    assert torch.equal(a.y.view(torch.int32), b.y.view(torch.int32))
+
+
 def test_prefill512_sampled():
     lay = workload_layer("prefill512")
     x = synth.workload_x("prefill512")
