@@ -89,6 +89,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (the reference for HBM counters)")
+    ap.add_argument("--place-slots", type=int, default=None,
+                    help="Place + Overlap: routed experts in pinned host memory, this many "
+                         "device slots per layer (coli_moe_forward_placed)")
+    ap.add_argument("--place-chunk", type=int, default=1, help="loaded experts per compute pass")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="placed mode: copies on the compute stream (no copy/compute overlap)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -122,6 +128,8 @@ def main():
     H, I, E, k, T = w.H, w.I, w.E, w.k, w.T
     fam = args.act_mode or w.act_mode
     mode = coli.ACT_I8 if fam == "i8" else coli.ACT_F32
+    if args.place_slots is not None:
+        return bench_placed(args, w, mode)
     stacked = w.layers > 1
     defaults = {"decode": (256, 32), "verify": (128, 16), "prefill512": (20, 4),
                 "prefill4096x8": (4, 1), "tiny": (256, 32)}
@@ -318,6 +326,123 @@ def main():
                    "kernels_us": kernels_us},
         "roofline": roof,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction (the MI355X host link)
+
+
+def bench_placed(args, w, mode):
+    """Place + Overlap: every layer's routed experts live in pinned host
+    memory, --place-slots of them at a time in device slots (LRU).  Steps run
+    eagerly (the placed forward synchronises once per layer to read the
+    union).  The layers' routers and shared experts differ; their host tiers
+    alias one pinned copy of the routed experts (the copy traffic is the
+    same as with distinct copies)."""
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_bias_amd as coli
+    import synth
+
+    H, I, E, k, T = w.H, w.I, w.E, w.k, w.T
+    if w.layers > 1:
+        raise SystemExit("placed mode runs the single-layer workloads (decode, verify, prefill512, tiny)")
+    NL = args.layers if args.layers is not None else (8 if w.name in ("decode", "verify") else 1)
+    defaults = {"decode": (64, 16), "verify": (32, 8), "prefill512": (8, 4), "tiny": (64, 16)}
+    K = args.steps if args.steps is not None else defaults[w.name][0]
+    W = args.warmup if args.warmup is not None else defaults[w.name][1]
+    n_slots = args.place_slots
+    t0 = time.time()
+    host = None
+    layers = []
+    for l in range(NL):
+        # layers after the first take their routed experts from layer 0's host tier
+        A = synth.workload_layer(w, layer=l, experts=None if l == 0 else [0])
+        pl = coli.PlacedLayer(A, k, n_slots, T_max=T, chunk=args.place_chunk,
+                              n_shared=w.n_shared, host=host)
+        host = pl.host
+        layers.append(pl)
+        del A
+    eb = expert_bytes(H, I)
+    log(f"[bench] placed: {NL} layer(s), host tier {E * eb / 1e9:.1f} GB pinned, "
+        f"{n_slots} slots/layer ({NL * n_slots * eb / 1e9:.1f} GB device) in {time.time() - t0:.1f}s")
+
+    # plain pinned host -> device copy rate (the ceiling of the staging)
+    src = torch.empty(1 << 30, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t_c = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_gbs = 3 * (1 << 30) / (time.perf_counter() - t_c) / 1e9
+    del src, dst
+
+    nsteps_in = W + K
+    if w.x_kind == "overlap":
+        xs = [torch.from_numpy(synth.activations(H, T, wid=w.wid, layer=100 + s, kind="overlap")).cuda()
+              for s in range(nsteps_in)]
+    else:
+        xall = torch.from_numpy(synth.activations(H, T * nsteps_in, wid=w.wid)).cuda()
+        xs = [xall[s * T:(s + 1) * T] for s in range(nsteps_in)]
+    bufs = coli.Buffers(layers[0], T, mode)
+    pws = torch.empty((coli.place_ws_bytes(E, k, T),), dtype=torch.uint8, device="cuda")
+    copy_stream = None if args.no_overlap else torch.cuda.Stream()
+    # fill every layer's slots (experts 0..n_slots-1), then warm the LRU state
+    for pl in layers:
+        coli.place_prefetch(pl, list(range(n_slots)), copy_stream=copy_stream)
+    torch.cuda.synchronize()
+
+    def step(s, stats):
+        for pl in layers:
+            st = coli.run_layer_placed(pl, xs[s], bufs, pws, copy_stream=copy_stream,
+                                       top_p=args.topp)
+            stats.append(st)
+
+    warm = []
+    for s in range(W):
+        step(s, warm)
+    torch.cuda.synchronize()
+    stats = []
+    t_start = time.perf_counter()
+    for s in range(K):
+        step(W + s, stats)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    U = np.array([st["n_union"] for st in stats])
+    hits = np.array([st["hits"] for st in stats])
+    loads = np.array([st["loads"] for st in stats])
+    loaded_bytes = loads.sum() * eb
+    pcie = loaded_bytes / elapsed / 1e9
+    out = {
+        "metric": METRIC, "value": round(K * NL * T / elapsed, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8" if mode == coli.ACT_I8 else "f32", "data": "synthetic",
+        "config": {"workload": w.name + "-placed", "description": w.note + "; routed experts in "
+                   "pinned host memory, LRU slots in device memory; a step is the token batch "
+                   f"through {NL} layer(s), value counts tokens per layer pass", "H": H, "I": I, "E": E, "k": k, "T": T,
+                   "n_shared": w.n_shared, "layers": NL,
+                   "act_mode": "i8" if mode == coli.ACT_I8 else "f32", "top_p": args.topp,
+                   "graph": False, "union_size_mean": round(float(U.mean()), 2),
+                   "union_size_minmax": [int(U.min()), int(U.max())]},
+        "placement": {"n_slots": n_slots, "chunk": args.place_chunk,
+                      "overlap": not args.no_overlap,
+                      "hit_rate": round(float(hits.sum() / U.sum()), 4),
+                      "loads_per_layer_call": round(float(loads.mean()), 3),
+                      "passes_per_layer_call": round(float(np.mean([st["passes"] for st in stats])), 3),
+                      "h2d_bytes_per_step": int(loaded_bytes / K),
+                      "h2d_copy_gbs_measured": round(h2d_gbs, 2),
+                      # share of the wall time the link needs for these bytes at the
+                      # measured plain-copy rate
+                      "copy_busy_frac": round(loaded_bytes / (h2d_gbs * 1e9) / elapsed, 4)},
+        "roofline": {"bound": "pcie", "achieved": round(pcie, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(pcie / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "expert staging (host-to-device copies)"},
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

@@ -25,6 +25,10 @@ EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
            "coli_rmsnorm", "coli_add_inplace")
+# every symbol declared in include/coli_place.h
+PLACE_EXPORTS = ("coli_moe_placer_create", "coli_moe_placer_destroy", "coli_moe_placer_reset",
+                 "coli_moe_placer_slot_of", "coli_moe_place_plan", "coli_moe_place_ws_bytes",
+                 "coli_moe_forward_placed", "coli_moe_place_prefetch")
 
 
 class ColiError(RuntimeError):
@@ -71,6 +75,15 @@ def lib():
             "coli_moe_device_check": ([], ctypes.c_int),
             "coli_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
             "coli_add_inplace": ([vp, vp, i64, vp], ctypes.c_int),
+            "coli_moe_placer_create": ([i32, i32, i32, i32, i32, i32, i32, vp], ctypes.c_int),
+            "coli_moe_placer_destroy": ([vp], None),
+            "coli_moe_placer_reset": ([vp], ctypes.c_int),
+            "coli_moe_placer_slot_of": ([vp, i32], i32),
+            "coli_moe_place_plan": ([vp, vp, i32, vp, vp, vp, vp, vp], ctypes.c_int),
+            "coli_moe_place_ws_bytes": ([i32, i32, i32], sz),
+            "coli_moe_forward_placed": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                         sz, vp, sz, vp, vp, vp], ctypes.c_int),
+            "coli_moe_place_prefetch": ([vp, vp, vp, i32, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -267,3 +280,151 @@ def dump_views(dump_host, H, I, k, T, n_shared):
     off = a256(off + R * I)
     sh = dump_host[off:off + R * (I // 64) * 4].view(np.float32).reshape(R, I // 64)
     return dict(acc13=acc13, acc2=acc2, qh=qh, sh=sh)
+
+
+# ---- placement across pinned host memory and device slots (coli_place.h) ----
+
+class ColiTiers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("host_w13", "host_s13", "host_w2", "host_s2",
+                                               "slot_w13", "slot_s13", "slot_w2", "slot_s2",
+                                               "slot_table")]
+
+
+class PlaceStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_union", "hits", "loads", "passes")]
+
+
+def place_ws_bytes(E, k, T) -> int:
+    return lib().coli_moe_place_ws_bytes(E, k, T)
+
+
+class Placer:
+    """Residency state of one layer's experts (coli_moe_placer)."""
+
+    def __init__(self, H, I, E, k, n_slots, T_max, chunk=1):
+        h = ctypes.c_void_p()
+        _check(lib().coli_moe_placer_create(H, I, E, k, n_slots, T_max, chunk, ctypes.byref(h)),
+               "coli_moe_placer_create")
+        self.handle = h.value
+        self.E, self.n_slots, self.chunk = E, n_slots, chunk
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().coli_moe_placer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self):
+        _check(lib().coli_moe_placer_reset(self.handle), "coli_moe_placer_reset")
+
+    def slot_of(self, e) -> int:
+        return lib().coli_moe_placer_slot_of(self.handle, e)
+
+    def plan(self, union_ids):
+        """coli_moe_place_plan on a host list; returns the plan as lists."""
+        U = len(union_ids)
+        A = ctypes.c_int32 * max(U, 1)
+        uid, es, ep, le, lw = A(*union_ids), A(), A(), A(), A()
+        counts = (ctypes.c_int32 * 3)()
+        _check(lib().coli_moe_place_plan(self.handle, uid, U, es, ep, le, lw, counts),
+               "coli_moe_place_plan")
+        hits, nl, npass = counts
+        return dict(slot=list(es[:U]), pass_=list(ep[:U]),
+                    loads=[(le[i], lw[i]) for i in range(nl)], hits=hits, passes=npass)
+
+
+class PlacedLayer:
+    """A layer whose routed experts live in pinned host memory, with a pool
+    of n_slots device slots in front of them.  Router and shared expert are
+    in device memory.  ``host`` may pass the pinned host tier of another
+    PlacedLayer (dict of tensors) to share it."""
+
+    def __init__(self, arrays: dict, k: int, n_slots: int, T_max: int, chunk: int = 1,
+                 n_shared: int = 1, device="cuda", host=None):
+        import numpy as np
+        import torch
+
+        def t(a):
+            if isinstance(a, np.ndarray):
+                if a.dtype == np.uint16:
+                    a = a.view(np.int16)
+                a = torch.from_numpy(np.ascontiguousarray(a))
+            return a
+
+        self.H, self.I, self.E, self.k, self.n_shared = (int(arrays["H"]), int(arrays["I"]),
+                                                        int(arrays["E"]), k, n_shared)
+        self.n_slots = n_slots
+        self.t = {}
+        for n in ("router_w", "router_b"):
+            self.t[n] = t(arrays[n]).to(device).contiguous()
+        if n_shared:
+            for n in ("sh_w13", "sh_s13", "sh_w2", "sh_s2"):
+                self.t[n] = t(arrays[n]).to(device).contiguous()
+        if host is None:
+            host = {n: t(arrays[n]).contiguous().pin_memory() for n in ("w13", "s13", "w2", "s2")}
+        self.host = host
+        self.slots = {n: torch.empty((n_slots,) + tuple(host[n].shape[1:]), dtype=host[n].dtype,
+                                     device=device) for n in ("w13", "s13", "w2", "s2")}
+        self.slot_table = torch.empty((max(self.E, 4),), dtype=torch.int32, device=device)
+        s = ColiLayer(self.H, self.I, self.E, k, n_shared)
+        s.router_w = _ptr(self.t["router_w"])
+        s.router_bias = _ptr(self.t["router_b"])
+        if n_shared:
+            for n in ("sh_w13", "sh_s13", "sh_w2", "sh_s2"):
+                setattr(s, n, _ptr(self.t[n]))
+        self.struct = s
+        tr = ColiTiers()
+        for n in ("w13", "s13", "w2", "s2"):
+            setattr(tr, "host_" + n, _ptr(host[n]))
+            setattr(tr, "slot_" + n, _ptr(self.slots[n]))
+        tr.slot_table = _ptr(self.slot_table)
+        self.tiers = tr
+        self.placer = Placer(self.H, self.I, self.E, k, n_slots, T_max, chunk)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def forward_placed(layer: PlacedLayer, x, T, ids, w, union_ids, offsets, slots, n_union,
+                   act_mode, y, workspace, place_ws, stream=None, copy_stream=None):
+    """coli_moe_forward_placed; returns the call's PlaceStats as a dict."""
+    nb = workspace.numel() * workspace.element_size()
+    pb = place_ws.numel() * place_ws.element_size()
+    st = PlaceStats()
+    cs = _stream(stream) if copy_stream is None else _stream(copy_stream)
+    _check(lib().coli_moe_forward_placed(layer.ref, ctypes.byref(layer.tiers),
+                                         layer.placer.handle, _ptr(x), T, _ptr(ids), _ptr(w),
+                                         _ptr(union_ids), _ptr(offsets), _ptr(slots),
+                                         _ptr(n_union), act_mode, _ptr(y), _ptr(workspace), nb,
+                                         _ptr(place_ws), pb, ctypes.byref(st), _stream(stream),
+                                         cs), "coli_moe_forward_placed")
+    return dict(n_union=st.n_union, hits=st.hits, loads=st.loads, passes=st.passes)
+
+
+def place_prefetch(layer: PlacedLayer, experts, stream=None, copy_stream=None):
+    n = len(experts)
+    arr = (ctypes.c_int32 * max(n, 1))(*experts)
+    cs = _stream(stream) if copy_stream is None else _stream(copy_stream)
+    _check(lib().coli_moe_place_prefetch(layer.placer.handle, ctypes.byref(layer.tiers), arr, n,
+                                         _stream(stream), cs), "coli_moe_place_prefetch")
+
+
+def run_layer_placed(layer: PlacedLayer, x, bufs: "Buffers", place_ws, stream=None,
+                     copy_stream=None, top_p=None):
+    """route -> union -> forward_placed; returns the call's placement stats."""
+    T = bufs.T
+    if top_p is None:
+        route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+    else:
+        route_topp(layer, x, T, top_p, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+    union(bufs.ids, T, layer.k, layer.E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union,
+          stream=stream)
+    return forward_placed(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
+                          bufs.slots, bufs.n_union, bufs.act_mode, bufs.y, bufs.workspace,
+                          place_ws, stream=stream, copy_stream=copy_stream)

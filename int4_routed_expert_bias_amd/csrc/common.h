@@ -208,6 +208,9 @@ struct ForwardIO {
     float *y;
     uint8_t *ws; Workspace lay;
     int32_t *acc_dump; DumpLayout dump;
+    // false: the expert outputs stay in the workspace (o) and y is not
+    // written; the placed forward combines once after its last pass
+    bool combine = true;
 };
 
 // Kernels one forward call launches (without acc_dump): fp32 family gate/up,

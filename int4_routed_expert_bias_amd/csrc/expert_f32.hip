@@ -1024,7 +1024,9 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         if (err != hipSuccess) return err;
     }
     if (mk) mk->mark(st);
-    hipError_t err = launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st);
+    hipError_t err = io.combine
+        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st)
+        : hipSuccess;
     if (mk) mk->mark(st);
     return err;
 }
@@ -1073,7 +1075,9 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         if (err != hipSuccess) return err;
     }
     if (mk) mk->mark(st);
-    hipError_t err = launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st);
+    hipError_t err = io.combine
+        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st)
+        : hipSuccess;
     if (mk) mk->mark(st);
     return err;
 }
@@ -1139,7 +1143,9 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
         if (err != hipSuccess) return err;
     }
     if (mk) mk->mark(st);
-    hipError_t err = launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st);
+    hipError_t err = io.combine
+        ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st)
+        : hipSuccess;
     if (mk) mk->mark(st);
     return err;
 }

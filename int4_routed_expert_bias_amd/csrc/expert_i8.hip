@@ -578,7 +578,9 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     COLI_GG(false, (L.H + kBN - 1) / kBN)
 #undef COLI_GG
     if (mk) mk->mark(st);
-    err = launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st);
+    err = io.combine
+        ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st)
+        : hipSuccess;
     if (mk) mk->mark(st);
     return err;
 }

@@ -397,7 +397,9 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
         if (err != hipSuccess) return err;
     }
     if (mk) mk->mark(st);
-    hipError_t err = launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st);
+    hipError_t err = io.combine
+        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st)
+        : hipSuccess;
     if (mk) mk->mark(st);
     return err;
 }

@@ -5,6 +5,7 @@ documented status codes before any HIP call.
 Every call here carries at least one invalid argument, so no call reaches
 the device (fake pointers are never dereferenced)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -13,7 +14,8 @@ import pytest
 import int4_routed_expert_bias_amd as coli
 from conftest import ROOT, gpu_available
 
-HEADER = os.path.join(ROOT, "include", "coli_moe.h")
+HEADERS = {os.path.join(ROOT, "include", "coli_moe.h"): "EXPORTS",
+           os.path.join(ROOT, "include", "coli_place.h"): "PLACE_EXPORTS"}
 
 
 @pytest.fixture(scope="module")
@@ -24,17 +26,19 @@ def L():
     return coli.lib()
 
 
-def header_functions():
-    src = open(HEADER).read()
+def header_functions(path):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(coli_\w+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(L):
-    names = header_functions()
-    assert set(names) == set(coli.EXPORTS), names
-    for n in names:
-        assert hasattr(L, n), n
+    for path, attr in HEADERS.items():
+        names = header_functions(path)
+        assert set(names) == set(getattr(coli, attr)), (path, names)
+        for n in names:
+            assert hasattr(L, n), n
+    assert set(glob.glob(os.path.join(ROOT, "include", "*.h"))) == set(HEADERS)
     assert L.coli_moe_abi_version() == 1
 
 
