@@ -18,8 +18,9 @@ Workloads (--workload):
 
 The timed steps are captured once in a HIP graph and replayed between two
 synchronisations (wall clock).  The dominant kernel's duration comes from
-HIP events the library records on its own stream around each kernel
-(coli_moe_forward_profiled), over the same inputs.  Prints one JSON line.
+HIP events that each kernel's own dispatch records at its start and end
+(coli_moe_forward_profiled launches through hipExtLaunchKernel on the
+library's stream), over the same inputs.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -219,7 +220,7 @@ def main():
     nk = len(names)
     dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
     prof_steps = min(K, 64)
-    ev = [[hip.event() for _ in range(nk + 1)] for _ in range(prof_steps * (w.layers if stacked else 1))]
+    ev = [[hip.event() for _ in range(2 * nk)] for _ in range(prof_steps * (w.layers if stacked else 1))]
     union_sizes = []
     torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
     i = 0
@@ -248,7 +249,7 @@ def main():
     per_kernel = np.zeros(nk)
     for e in ev:
         for j in range(nk):
-            per_kernel[j] += hip.elapsed_ms(e[j], e[j + 1])
+            per_kernel[j] += hip.elapsed_ms(e[2 * j], e[2 * j + 1])
     per_kernel /= len(ev)
     for e in ev:
         for x_ in e:
@@ -280,7 +281,8 @@ def main():
     if os.path.exists(tpath):
         with open(tpath) as fp:
             rec = json.load(fp).get(f"{w.name}:{names[dom]}")
-        if rec and rec.get("source_hash") == profiling.source_hash():
+        # the counters were taken with plain top-k routing
+        if rec and rec.get("source_hash") == profiling.source_hash() and args.topp is None:
             traffic = rec["hbm_bytes_per_launch"]
     roof["traffic"] = traffic
     roof["kernel"] = names[dom]

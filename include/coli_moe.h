@@ -197,11 +197,13 @@ int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
                      int32_t *acc_dump, void *hip_stream);
 
 /* Profiling variant of coli_moe_forward: the same work, and in addition
- * events[i] (hipEvent_t values created by the caller) is recorded on
- * hip_stream before the i-th kernel the call launches and events[n] after
- * its last kernel, n = coli_moe_forward_kernel_count(act_mode, T).  Requires
- * n_events >= n + 1 (else COLI_E_ARG, nothing enqueued).  For measurement
- * only; the production path is coli_moe_forward. */
+ * events[2i] and events[2i + 1] (hipEvent_t values created by the caller,
+ * with timing) receive the start and the end of the i-th kernel the call
+ * launches, recorded by that kernel's own dispatch (hipExtLaunchKernel), so
+ * hipEventElapsedTime(events[2i], events[2i + 1]) is the kernel's duration
+ * as a kernel trace reports it.  i < n = coli_moe_forward_kernel_count(
+ * act_mode, T); requires n_events >= 2n (else COLI_E_ARG, nothing enqueued).
+ * For measurement only; the production path is coli_moe_forward. */
 int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
                               const int32_t *topk_ids, const float *topk_w,
                               const int32_t *union_ids, const int32_t *offsets,

@@ -193,7 +193,7 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int32_t T,
     if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return COLI_E_UNSUPPORTED;
     if (acc_dump && act_mode != COLI_ACT_I8) return COLI_E_ARG;
     if (mk) {
-        const int need = forward_kernel_count(act_mode, T) + 1;
+        const int need = 2 * forward_kernel_count(act_mode, T);
         if (!mk->ev || mk->n < need) return COLI_E_ARG;
         for (int i = 0; i < need; ++i)
             if (!mk->ev[i]) return COLI_E_ARG;

@@ -36,11 +36,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, int32_t T, int32_t k,
-                          int32_t H, int32_t n_shared, float *y, hipStream_t st)
+                          int32_t H, int32_t n_shared, float *y, hipStream_t st, Marks *mk)
 {
     if (T <= 0) return hipSuccess;
     dim3 grid((H / 4 + 255) / 256, T), block(256);
-    hipLaunchKernelGGL(combine_kernel, grid, block, 0, st, o, ids, w, T, k, H, n_shared, y);
+    launch(mk, combine_kernel, grid, block, 0, st, o, ids, w, T, k, H, n_shared, y);
     return hipGetLastError();
 }
 

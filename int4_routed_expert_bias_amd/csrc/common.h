@@ -3,6 +3,7 @@
 // and the kernel translation units).  Written for gfx950 (CDNA4, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -164,18 +165,33 @@ inline DumpLayout dump_layout(int64_t H, int64_t I, int64_t k, int64_t T, int64_
 // ---------------------------------------------------------------------------
 // launcher interface (each returns hipError_t of the launch)
 
-// Optional profiling marks: records caller-created events on the stream
-// before each kernel of a call and after the last one.
+// Optional profiling marks: caller-created events, two per kernel of a call
+// (ev[2i], ev[2i + 1]), set to the start and the end of kernel i by its own
+// dispatch (hipExtLaunchKernel), i.e. the durations a kernel trace reports.
 struct Marks {
     void **ev = nullptr;
-    int n = 0;
-    int i = 0;
-    void mark(hipStream_t st)
+    int n = 0;  // events available
+    int i = 0;  // kernels launched so far
+    bool next(hipEvent_t &start, hipEvent_t &end)
     {
-        if (ev && i < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
-        ++i;
+        const int j = 2 * i++;
+        if (!ev || j + 1 >= n) return false;
+        start = static_cast<hipEvent_t>(ev[j]);
+        end = static_cast<hipEvent_t>(ev[j + 1]);
+        return true;
     }
 };
+
+// Every kernel of a forward call is launched through this: a plain launch,
+// or with marks one whose dispatch records the kernel's start and end.
+template <typename F, typename... Args>
+inline void launch(Marks *mk, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                   Args... args)
+{
+    hipEvent_t a, b;
+    if (mk && mk->next(a, b)) hipExtLaunchKernelGGL(kernel, grid, block, lds, st, a, b, 0, args...);
+    else hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
 
 struct LayerDev {
     int32_t H, I, E, k, n_shared;
@@ -228,7 +244,8 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
 hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
                                    const float *sx, float *h, float *o, hipStream_t st, Marks *mk);
 hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, int32_t T, int32_t k,
-                          int32_t H, int32_t n_shared, float *y, hipStream_t st);
+                          int32_t H, int32_t n_shared, float *y, hipStream_t st,
+                          Marks *mk = nullptr);
 hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
                           hipStream_t st);
 hipError_t launch_add(float *x, const float *y, int64_t n, hipStream_t st);

@@ -988,7 +988,6 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
-    if (mk) mk->mark(st);
     {
         // one 4-wave workgroup per CU (eight waves measured slower: more
         // concurrent streams lose DRAM locality)
@@ -1001,13 +1000,12 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         const dim3 grid(std::max(cus, (entries + WPB - 1) / WPB)), block(WPB * 64);
         const size_t lds = (size_t)io.T * (L.H + L.H / 32) * 4;
 #define COLI_GUM(P_) \
-        if (P == P_) hipLaunchKernelGGL((gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB>), grid, block, lds, st, a);
+        if (P == P_) launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB>), grid, block, lds, st, a);
         COLI_GUM(1) COLI_GUM(2) COLI_GUM(3) COLI_GUM(4)
 #undef COLI_GUM
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     {
         constexpr int RD = 4, M = (NTOK >= 4 ? 2 : 4), DEPTH = 2;
         a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
@@ -1017,17 +1015,15 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         const int P = (L.I / 32 + 63) / 64;
         const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
 #define COLI_DNM(P_) \
-        if (P == P_) hipLaunchKernelGGL((down_mt_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, 0, st, a);
+        if (P == P_) launch(mk, (down_mt_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, 0, st, a);
         COLI_DNM(1) COLI_DNM(2) COLI_DNM(3) COLI_DNM(4)
 #undef COLI_DNM
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     hipError_t err = io.combine
-        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st)
+        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st, mk)
         : hipSuccess;
-    if (mk) mk->mark(st);
     return err;
 }
 
@@ -1040,7 +1036,6 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
-    if (mk) mk->mark(st);
     {
         constexpr int NP = 1, M = 8, DEPTH = 2;
         a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
@@ -1052,13 +1047,12 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         const dim3 grid(std::min(cus, (units + 3) / 4)), block(256);
         const size_t lds = (size_t)(L.H + L.H / 32) * 4;
 #define COLI_GU1(P_) \
-        if (P == P_) hipLaunchKernelGGL((gateup_t1_kernel<P_, NP, M, DEPTH, true>), grid, block, lds, st, a);
+        if (P == P_) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true>), grid, block, lds, st, a);
         COLI_GU1(1) COLI_GU1(2) COLI_GU1(3) COLI_GU1(4)
 #undef COLI_GU1
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     {
         constexpr int RD = 4, M = 4, DEPTH = 2;
         a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
@@ -1068,17 +1062,15 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         const int P = (L.I / 32 + 63) / 64;
         const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
 #define COLI_DN1(P_) \
-        if (P == P_) hipLaunchKernelGGL((down_t1_kernel<P_, RD, M, DEPTH>), grid, block, 0, st, a);
+        if (P == P_) launch(mk, (down_t1_kernel<P_, RD, M, DEPTH>), grid, block, 0, st, a);
         COLI_DN1(1) COLI_DN1(2) COLI_DN1(3) COLI_DN1(4)
 #undef COLI_DN1
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     hipError_t err = io.combine
-        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st)
+        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st, mk)
         : hipSuccess;
-    if (mk) mk->mark(st);
     return err;
 }
 
@@ -1106,7 +1098,6 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
     a.in = io.x; a.in_by_slot = 0;
     a.out = h; a.out_ld = L.I;
-    if (mk) mk->mark(st);
     {
         constexpr int W = 4, RW = 4;
         const int P = (L.H / 32 + 63) / 64;
@@ -1118,7 +1109,7 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
         const size_t lds = (size_t)nt * (L.H + L.H / 32) * 4;
 #define COLI_GU(NT_, P_) \
         if (nt == NT_ && P == P_) \
-            hipLaunchKernelGGL((gateup_f32_kernel<NT_, P_, W, RW>), grid, block, lds, st, a);
+            launch(mk, (gateup_f32_kernel<NT_, P_, W, RW>), grid, block, lds, st, a);
         COLI_GU(1, 1) COLI_GU(1, 2) COLI_GU(1, 3) COLI_GU(1, 4)
         COLI_GU(2, 1) COLI_GU(2, 2) COLI_GU(2, 3) COLI_GU(2, 4)
 #undef COLI_GU
@@ -1130,23 +1121,20 @@ hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_
     a.N = L.H; a.K = L.I; a.upe = L.H;
     a.in = h; a.in_by_slot = 1;
     a.out = o; a.out_ld = L.H;
-    if (mk) mk->mark(st);
     {
         constexpr int W = 4, RW = 8;
         const int P = (L.I / 32 + 63) / 64;
         const dim3 grid(L.H / (W * RW), entries), block(W * 64);
 #define COLI_DN(P_) \
-        if (P == P_) hipLaunchKernelGGL((down_f32_kernel<P_, W, RW>), grid, block, 0, st, a);
+        if (P == P_) launch(mk, (down_f32_kernel<P_, W, RW>), grid, block, 0, st, a);
         COLI_DN(1) COLI_DN(2) COLI_DN(3) COLI_DN(4)
 #undef COLI_DN
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     hipError_t err = io.combine
-        ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st)
+        ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st, mk)
         : hipSuccess;
-    if (mk) mk->mark(st);
     return err;
 }
 

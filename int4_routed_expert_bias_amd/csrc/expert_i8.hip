@@ -524,8 +524,7 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     int2 *tiles = reinterpret_cast<int2 *>(io.ws + lay.tiles);
 
     const int64_t ng = (int64_t)T * (L.H / 64);
-    if (mk) mk->mark(st);
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, st, io.x, ng,
+    launch(mk, quant_rows_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, st, io.x, ng,
                        L.H, qx, sx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -534,13 +533,12 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     if (T <= kI8StreamTMax && !io.acc_dump)
         return launch_forward_i8_small(L, io, qx, sx, reinterpret_cast<float *>(io.ws + lay.h), o,
                                        st, mk);
-    if (mk) mk->mark(st);
     // 64-row tiles: measured on MI355X they beat 128-row tiles even for dense
     // entries (three workgroups per CU instead of two) and waste fewer rows on
     // the last, partial tile of each entry
     constexpr int kTileRows = 64;
     const int tile_m = kTileRows;
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, st, io.offsets, io.n_union,
+    launch(mk, schedule_kernel, dim3(1), dim3(1024), 0, st, io.offsets, io.n_union,
                        (int)lay.cap, T, L.n_shared, tile_m, tiles, (int)lay.max_tiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
@@ -560,13 +558,12 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
 #define COLI_GG(GU_, GX_)                                                                      \
     {                                                                                          \
         const dim3 grid(GX_, (unsigned)lay.max_tiles);                                         \
-        if (dump) hipLaunchKernelGGL((ggemm_kernel<kTileRows, 2, GU_, true>), grid, dim3(256), 0, st, a); \
-        else hipLaunchKernelGGL((ggemm_kernel<kTileRows, 2, GU_, false>), grid, dim3(256), 0, st, a);     \
+        if (dump) launch(mk, (ggemm_kernel<kTileRows, 2, GU_, true>), grid, dim3(256), 0, st, a); \
+        else launch(mk, (ggemm_kernel<kTileRows, 2, GU_, false>), grid, dim3(256), 0, st, a);     \
         if ((err = hipGetLastError()) != hipSuccess) return err;                               \
     }
     // gate/up: grid x = 64-unit column blocks (32 for I = 2048: a multiple of 8,
     // so the m-tiles of one entry and column block land on one XCD's L2)
-    if (mk) mk->mark(st);
     COLI_GG(true, L.I / (kBN / 2))
     // down
     a.qin = qh; a.sin = sh; a.in_by_slot = 1;
@@ -574,14 +571,11 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.N = L.H; a.K = L.I;
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc2) : nullptr;
     a.dump_qh = nullptr; a.dump_sh = nullptr;
-    if (mk) mk->mark(st);
     COLI_GG(false, (L.H + kBN - 1) / kBN)
 #undef COLI_GG
-    if (mk) mk->mark(st);
     err = io.combine
-        ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st)
+        ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st, mk)
         : hipSuccess;
-    if (mk) mk->mark(st);
     return err;
 }
 

@@ -355,7 +355,6 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
 {
     const int cus = device_cu_count();
     const int entries = (int)io.lay.cap + L.n_shared;
-    if (mk) mk->mark(st);
     {
         // measured on MI355X with the decode layer: one token streams best with
         // two workgroups per CU and a three-stage ring (28.6 us vs 32.2 for one
@@ -370,13 +369,12 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
         const size_t lds = (size_t)4 * Lds::rows() * (L.H / 64 + 1) * 4;
         const dim3 grid(std::max((NTOK == 1 ? 2 : 1) * cus, (entries + 3) / 4)), block(256);
 #define COLI_GUV(P_) \
-        if (P == P_) hipLaunchKernelGGL((gateup_i8v_kernel<P_, M, DEPTH, NTOK>), grid, block, lds, st, a);
+        if (P == P_) launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK>), grid, block, lds, st, a);
         COLI_GUV(1) COLI_GUV(2) COLI_GUV(3) COLI_GUV(4)
 #undef COLI_GUV
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     {
         // one token: RD 4, M 8, a four-stage ring, two workgroups per CU
         // (15.4 us vs 16.7 for four workgroups and two stages)
@@ -390,17 +388,15 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
         const size_t lds = (size_t)4 * Lds::rows() * (L.I / 64 + 1) * 4;
         const dim3 grid(std::max((NTOK == 1 ? 2 : 4) * cus, (entries + 3) / 4)), block(256);
 #define COLI_DNV(P_) \
-        if (P == P_) hipLaunchKernelGGL((down_i8v_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, lds, st, a);
+        if (P == P_) launch(mk, (down_i8v_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, lds, st, a);
         COLI_DNV(1) COLI_DNV(2) COLI_DNV(3) COLI_DNV(4)
 #undef COLI_DNV
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (mk) mk->mark(st);
     hipError_t err = io.combine
-        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st)
+        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st, mk)
         : hipSuccess;
-    if (mk) mk->mark(st);
     return err;
 }
 

@@ -160,3 +160,19 @@ def test_glue_argument_errors(L):
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path of a GPU-less host")
 def test_no_device_reports_device_error(L):
     assert L.coli_moe_device_check() in (coli.COLI_E_DEVICE, coli.COLI_E_UNSUPPORTED)
+
+
+def test_forward_profiled_needs_two_events_per_kernel(L):
+    lay = layer()
+    for mode, T in ((0, 1), (0, 4), (0, 9), (1, 2), (1, 9)):
+        n = coli.lib().coli_moe_forward_kernel_count(mode, T)
+        short = (ctypes.c_void_p * (2 * n - 1))(*([FAKE] * (2 * n - 1)))
+        st = L.coli_moe_forward_profiled(ctypes.byref(lay), FAKE, T, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, mode, FAKE, FAKE, 1 << 30, None, short, 2 * n - 1,
+                                         None)
+        assert st == coli.COLI_E_ARG, (mode, T)
+        holes = (ctypes.c_void_p * (2 * n))(*([FAKE] * (2 * n - 1) + [None]))
+        st = L.coli_moe_forward_profiled(ctypes.byref(lay), FAKE, T, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, mode, FAKE, FAKE, 1 << 30, None, holes, 2 * n,
+                                         None)
+        assert st == coli.COLI_E_ARG, (mode, T)
