@@ -55,6 +55,7 @@ def _setup(L):
         "orc_forward": ([vp, vp, i32, vp, vp, i32, vp], None),
         "orc_forward_rows": ([vp, vp, vp, vp, i32, i32, vp, vp], None),
         "orc_rmsnorm": ([i32, i32, vp, vp], None),
+        "orc_mla_decode": ([i32, i32, vp, i32, vp, vp, vp, i32, ctypes.c_float, vp], None),
         "orc_swiglu": ([ctypes.c_float, ctypes.c_float], ctypes.c_float),
     }
     for name, (args, res) in sig.items():
@@ -226,6 +227,20 @@ class Oracle:
         x = np.ascontiguousarray(x, np.float32)
         out = np.empty_like(x)
         self.L.orc_rmsnorm(x.shape[0], x.shape[1], _p(x), _p(out))
+        return out
+
+    def mla_decode(self, q: np.ndarray, kv: np.ndarray, scale: float, lens=None, idx=None):
+        """q [B][n_heads][576], kv [T][576]; lens [B] or idx [B][n_sel]
+        -> out [B][n_heads][512] (orc_mla_decode)."""
+        q = np.ascontiguousarray(q, np.float32)
+        kv = np.ascontiguousarray(kv, np.float32)
+        B, nh, _ = q.shape
+        out = np.empty((B, nh, 512), np.float32)
+        ln = None if lens is None else np.ascontiguousarray(lens, np.int32)
+        ix = None if idx is None else np.ascontiguousarray(idx, np.int32)
+        n_sel = 0 if ix is None else ix.shape[1]
+        self.L.orc_mla_decode(B, nh, _p(q), kv.shape[0], _p(kv), _p(ln), _p(ix), n_sel,
+                              float(scale), _p(out))
         return out
 
 

@@ -476,3 +476,67 @@ void orc_rmsnorm(int32_t T, int32_t H, const float *x, float *xhat)
         for (int32_t h = 0; h < H; ++h) xhat[(size_t)t * H + h] = (float)((double)r[h] * inv);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the compressed (MLA) KV cache, in its absorbed form.
+ * The Colibri pages (mcpfield.com "Colibri", section "コアアーキテクチャ",
+ * item 5; dashen-tech.com guide, table "コア技術のハイライト"; getting-started
+ * page, section "압축 KV 상태") state that MLA keeps 576 floats per token in
+ * the KV cache instead of 32,768.  Reading: the 576 floats are the 512-wide
+ * latent c_t followed by the 64-wide rotary key k_t; a query head arrives
+ * already absorbed as 576 floats (its latent query, then its rotary query),
+ * so that for head h of query b
+ *   s_t  = scale * sum_{d<576} q[b][h][d] * kv[t][d]          (double)
+ *   p_t  = exp(s_t - max_t s_t) / sum_t exp(s_t - max_t s_t)
+ *   o    = fp32( sum_t p_t * kv[t][0..512) )
+ * over the keys t of query b: t < lens[b] (the cached prefix), or, with a
+ * key list idx (the sparse top-k selection the pages' DSA indexer makes),
+ * the listed rows idx[b][j] that lie in [0, T).  A query with no key gets
+ * o = 0. */
+void orc_mla_decode(int32_t B, int32_t n_heads, const float *q, int32_t T, const float *kv,
+                    const int32_t *lens, const int32_t *idx, int32_t n_sel, float scale,
+                    float *out)
+{
+    const int32_t D = 576, DV = 512;
+    const int32_t n_max = idx ? n_sel : T;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(n_max > 0 ? n_max : 1));
+    int32_t *row = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n_max > 0 ? n_max : 1));
+    double *o = (double *)malloc(sizeof(double) * DV);
+    for (int32_t b = 0; b < B; ++b) {
+        /* the keys of query b */
+        int32_t nk = 0;
+        if (idx) {
+            for (int32_t j = 0; j < n_sel; ++j) {
+                int32_t t = idx[(size_t)b * n_sel + j];
+                if (t >= 0 && t < T) row[nk++] = t;
+            }
+        } else {
+            int32_t len = lens[b] < 0 ? 0 : (lens[b] > T ? T : lens[b]);
+            for (int32_t t = 0; t < len; ++t) row[nk++] = t;
+        }
+        for (int32_t h = 0; h < n_heads; ++h) {
+            const float *qv = q + ((size_t)b * n_heads + h) * D;
+            float *ov = out + ((size_t)b * n_heads + h) * DV;
+            double m = -INFINITY;
+            for (int32_t j = 0; j < nk; ++j) {
+                const float *kr = kv + (size_t)row[j] * D;
+                double acc = 0.0;
+                for (int32_t d = 0; d < D; ++d) acc += (double)qv[d] * (double)kr[d];
+                s[j] = (double)scale * acc;
+                if (s[j] > m) m = s[j];
+            }
+            double den = 0.0;
+            for (int32_t d = 0; d < DV; ++d) o[d] = 0.0;
+            for (int32_t j = 0; j < nk; ++j) {
+                const float *vr = kv + (size_t)row[j] * D;
+                double p = exp(s[j] - m);
+                den += p;
+                for (int32_t d = 0; d < DV; ++d) o[d] += p * (double)vr[d];
+            }
+            for (int32_t d = 0; d < DV; ++d) ov[d] = den > 0.0 ? (float)(o[d] / den) : 0.0f;
+        }
+    }
+    free(s);
+    free(row);
+    free(o);
+}

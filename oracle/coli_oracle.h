@@ -74,6 +74,15 @@ void orc_forward_rows(const orc_layer *L, const float *x, const int32_t *ids, co
 
 void orc_rmsnorm(int32_t T, int32_t H, const float *x, float *xhat);
 
+/* Decode attention over the compressed (MLA) KV cache, absorbed form:
+ * q [B][n_heads][576], kv [T][576] (latent 512 then rotary key 64),
+ * keys of query b: t < lens[b] (idx NULL) or the rows idx[b][0..n_sel) in
+ * [0, T); out [B][n_heads][512] = softmax(scale * q.kv_t) weighted sum of
+ * kv_t[0..512), computed in double, 0 when a query has no key. */
+void orc_mla_decode(int32_t B, int32_t n_heads, const float *q, int32_t T, const float *kv,
+                    const int32_t *lens, const int32_t *idx, int32_t n_sel, float scale,
+                    float *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -456,9 +456,126 @@ def pin_topp(o):
         assert np.array_equal(f32_bits(y1), f32_bits(y2)), mode
 
 
+# ----------------------------------------------------------------------------
+# compressed-KV (MLA) decode attention
+
+
+def _ulps(a, b):
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)
+
+
+def _mla_ref(q, kv, scale, keys):
+    """Library routines only: scipy's softmax over numpy float64 scores."""
+    from scipy.special import softmax
+    q64, kv64 = q.astype(np.float64), kv.astype(np.float64)
+    scale = float(np.float32(scale))  # the oracle takes the scale as a float
+    out = np.zeros(q.shape[:2] + (512,), np.float64)
+    for b in range(q.shape[0]):
+        rows = keys[b]
+        if len(rows) == 0:
+            continue
+        s = scale * (q64[b] @ kv64[rows].T)          # [heads][keys]
+        out[b] = softmax(s, axis=1) @ kv64[rows, :512]
+    return out
+
+
+def pin_mla_brute(o):
+    for B, nh, T, scale in ((2, 3, 37, 0.07), (1, 16, 5, 0.3), (3, 2, 64, 0.0417)):
+        q = RNG.standard_normal((B, nh, 576)).astype(np.float32)
+        kv = RNG.standard_normal((T, 576)).astype(np.float32)
+        lens = RNG.integers(1, T + 1, B).astype(np.int32)
+        lens[0] = T
+        got = o.mla_decode(q, kv, scale, lens=lens)
+        ref = _mla_ref(q, kv, scale, [list(range(l)) for l in lens])
+        assert _ulps(got, ref.astype(np.float32)).max() <= 1
+    # large scores: the exponentials must stay finite
+    q = (RNG.standard_normal((1, 4, 576)) * 30).astype(np.float32)
+    kv = RNG.standard_normal((50, 576)).astype(np.float32)
+    got = o.mla_decode(q, kv, 1.0, lens=np.array([50], np.int32))
+    ref = _mla_ref(q, kv, 1.0, [list(range(50))])
+    assert np.isfinite(got).all() and _ulps(got, ref.astype(np.float32)).max() <= 1
+
+
+def pin_mla_closed_forms(o):
+    T = 40
+    kv = RNG.standard_normal((T, 576)).astype(np.float32)
+    q = RNG.standard_normal((2, 8, 576)).astype(np.float32)
+    # scale 0: every key weighs the same, o is the mean of the value rows
+    lens = np.array([T, 13], np.int32)
+    got = o.mla_decode(q, kv, 0.0, lens=lens)
+    for b, l in enumerate(lens):
+        mean = kv[:l, :512].astype(np.float64).mean(axis=0).astype(np.float32)
+        assert _ulps(got[b], np.broadcast_to(mean, got[b].shape)).max() <= 1
+    # one dominant key through the last rotary dimension: o is its value row
+    qd = np.zeros((1, 3, 576), np.float32)
+    qd[..., 575] = 1.0
+    for target, l in ((7, 20), (19, 20), (20, 20)):
+        kd = kv.copy()
+        kd[:, 575] = 0.0
+        kd[target, 575] = 1.0
+        got = o.mla_decode(qd, kd, 80.0, lens=np.array([l], np.int32))
+        if target < l:
+            want = kd[target, :512]
+        else:  # outside the prefix: every kept key scores 0
+            want = kd[:l, :512].astype(np.float64).mean(axis=0).astype(np.float32)
+        assert _ulps(got[0], np.broadcast_to(want, got[0].shape)).max() <= 1, (target, l)
+    # a constant added to every score changes nothing
+    qs = q.copy()
+    qs[..., 575] = 1.0
+    k0 = kv.copy()
+    k0[:, 575] = 0.0
+    base = o.mla_decode(qs, k0, 0.05, lens=lens)
+    ks = k0.copy()
+    ks[:, 575] = np.float32(37.0)  # every score moves by exactly 0.05 * 37
+    assert _ulps(o.mla_decode(qs, ks, 0.05, lens=lens), base).max() <= 2
+    # values use the latent part only
+    qz = q.copy()
+    qz[..., 512:] = 0.0
+    kz = kv.copy()
+    kz[:, 512:] = 1e6
+    a = o.mla_decode(qz, kz, 0.05, lens=lens)
+    kz[:, 512:] = 0.0
+    assert np.array_equal(a, o.mla_decode(qz, kz, 0.05, lens=lens))
+    # a query without keys gets zeros
+    z = o.mla_decode(q[:1], kv, 0.05, lens=np.array([0], np.int32))
+    assert not z.any()
+    z = o.mla_decode(q[:1], kv, 0.05, idx=np.full((1, 5), -1, np.int32))
+    assert not z.any()
+
+
+def pin_mla_key_lists(o):
+    T = 70
+    kv = RNG.standard_normal((T, 576)).astype(np.float32)
+    q = RNG.standard_normal((3, 4, 576)).astype(np.float32)
+    lens = np.array([70, 33, 1], np.int32)
+    dense = o.mla_decode(q, kv, 0.06, lens=lens)
+    # the prefix as an explicit list, padded with -1 and out-of-range rows
+    idx = np.full((3, 90), -1, np.int32)
+    for b, l in enumerate(lens):
+        idx[b, :l] = np.arange(l)
+    idx[1, 50] = T
+    idx[2, 7] = 10 ** 6
+    assert np.array_equal(o.mla_decode(q, kv, 0.06, idx=idx), dense)
+    # any order of the listed keys (only rounding differs)
+    perm = idx.copy()
+    for b, l in enumerate(lens):
+        perm[b, :l] = RNG.permutation(l)
+    assert _ulps(o.mla_decode(q, kv, 0.06, idx=perm), dense).max() <= 1
+    # a sparse selection equals attention over those rows alone
+    sel = np.sort(RNG.choice(T, 24, replace=False)).astype(np.int32)
+    got = o.mla_decode(q[:1], kv, 0.06, idx=sel[None])
+    ref = _mla_ref(q[:1], kv, 0.06, [sel.tolist()])
+    assert _ulps(got, ref.astype(np.float32)).max() <= 1
+
+
 PINS = [pin_f16, pin_int4, pin_logits, pin_sigmoid, pin_select_brute, pin_select_special,
         pin_union, pin_quant, pin_swiglu, pin_f32_expert_exact, pin_i8_expert, pin_combine,
-        pin_rmsnorm, pin_relabel_and_independence, pin_topp]
+        pin_rmsnorm, pin_relabel_and_independence, pin_topp, pin_mla_brute,
+        pin_mla_closed_forms, pin_mla_key_lists]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -531,6 +648,14 @@ MUTANTS = [
     ("topp drops from the front", "if (j < kp) {\n                wt[j]", "if (j >= k - kp) {\n                wt[j]"),
     ("union counts dropped slots", "    for (int32_t u = U; u <= cap; ++u) offsets[u] = run;",
      "    for (int32_t u = U; u <= cap; ++u) offsets[u] = n;"),
+    ("mla no max shift", "double p = exp(s[j] - m);", "double p = exp(s[j]);"),
+    ("mla value offset", "for (int32_t d = 0; d < DV; ++d) o[d] += p * (double)vr[d];",
+     "for (int32_t d = 0; d < DV; ++d) o[d] += p * (double)vr[d + 64];"),
+    ("mla prefix short", "for (int32_t t = 0; t < len; ++t) row[nk++] = t;",
+     "for (int32_t t = 0; t + 1 < len; ++t) row[nk++] = t;"),
+    ("mla scale dropped", "s[j] = (double)scale * acc;", "s[j] = acc;"),
+    ("mla rotary part dropped", "for (int32_t d = 0; d < D; ++d) acc += (double)qv[d] * (double)kr[d];",
+     "for (int32_t d = 0; d < DV; ++d) acc += (double)qv[d] * (double)kr[d];"),
 ]
 
 
