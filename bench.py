@@ -79,7 +79,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "verify", "prefill512", "prefill4096x8", "tiny"])
+                    choices=["decode", "verify", "prefill512", "prefill4096x8", "tiny",
+                             "mla", "mla_verify", "mla_dsa"])
     ap.add_argument("--layers", type=int, default=None, help="resident layer copies cycled (decode/verify)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--act-mode", choices=["f32", "i8"], default=None,
@@ -125,6 +126,8 @@ def main():
     if coli.device_check() != coli.COLI_OK:
         raise SystemExit("device is not gfx950: " + coli.strerror(coli.device_check()))
 
+    if args.workload.startswith("mla"):
+        return bench_mla(args)
     w = synth.WORKLOADS[args.workload]
     H, I, E, k, T = w.H, w.I, w.E, w.k, w.T
     fam = args.act_mode or w.act_mode
@@ -447,6 +450,152 @@ def bench_placed(args, w, mode):
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+
+
+FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix / vector peak
+
+# Decode attention over the compressed (576-float) MLA cache: query tokens,
+# heads, cache length, sparse key-list width (0: the whole prefix).
+MLA_WORKLOADS = {
+    "mla": dict(B=1, H=64, T=32768, n_sel=0,
+                note="one decode token, 64 heads, 32,768 cached tokens"),
+    "mla_verify": dict(B=4, H=64, T=32768, n_sel=0,
+                       note="a 4-token verify batch (causal prefixes) over 32,768 cached tokens"),
+    "mla_dsa": dict(B=1, H=64, T=131072, n_sel=2048,
+                    note="one decode token, 64 heads, 2,048 keys selected from 131,072 cached"),
+}
+
+
+def bench_mla(args):
+    """Steps are coli_mla_decode calls that cycle over --layers distinct caches
+    (so each step reads its cache from HBM, not from the 256 MB Infinity
+    Cache), captured in one HIP graph.  Kernel durations come from events the
+    kernels' own dispatches record (coli_mla_decode_profiled)."""
+    import numpy as np
+    import torch
+
+    import int4_routed_expert_bias_amd as coli
+    import synth
+
+    cfg = MLA_WORKLOADS[args.workload]
+    B, Hh, T, n_sel = cfg["B"], cfg["H"], cfg["T"], cfg["n_sel"]
+    NL = args.layers if args.layers is not None else 8
+    K = args.steps if args.steps is not None else 256
+    W = args.warmup if args.warmup is not None else 32
+    scale = float(np.float32(1.0 / np.sqrt(192.0)))
+    wid = 400 + list(MLA_WORKLOADS).index(args.workload) * 10
+    t0 = time.time()
+    q = torch.from_numpy(synth.activations(576, B * Hh, wid=wid).reshape(B, Hh, 576)).cuda()
+    kvs = [torch.from_numpy(synth.activations(576, T, wid=wid + 1, layer=l)).cuda()
+           for l in range(NL)]
+    lens = torch.tensor([T - B + 1 + b for b in range(B)], dtype=torch.int32, device="cuda")
+    idx = None
+    if n_sel:
+        rng = np.random.default_rng(wid)
+        idx = torch.from_numpy(np.stack([np.sort(rng.choice(T, n_sel, replace=False))
+                                         for _ in range(B)]).astype(np.int32)).cuda()
+    out = torch.empty((B, Hh, 512), device="cuda")
+    ws = torch.empty((coli.mla_workspace_bytes(B, Hh, T, n_sel),), dtype=torch.uint8, device="cuda")
+    log(f"[bench] mla: {NL} caches of {T} x 576 fp32 ({NL * T * 2304 / 1e9:.2f} GB) "
+        f"in {time.time() - t0:.1f}s")
+
+    def step(s):
+        coli.mla_decode(q, kvs[s % NL], out, ws, scale, lens=None if idx is not None else lens,
+                        idx=idx)
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for s in range(K):
+                    step(W + s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    else:
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(K):
+            step(W + s)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+
+    hip = Hip()
+    prof = min(K, 64)
+    evs = [[hip.event() for _ in range(4)] for _ in range(prof)]
+    torch.cuda._sleep(100_000_000)
+    for s in range(prof):
+        coli.mla_decode_profiled(q, kvs[(W + s) % NL], out, ws, scale, evs[s],
+                                 lens=None if idx is not None else lens, idx=idx)
+    torch.cuda.synchronize()
+    attn_ms = np.mean([hip.elapsed_ms(e[0], e[1]) for e in evs])
+    merge_ms = np.mean([hip.elapsed_ms(e[2], e[3]) for e in evs])
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+    nk = [n_sel] * B if n_sel else [T - B + 1 + b for b in range(B)]
+    flops = sum(2.0 * Hh * kk * (576 + 512) for kk in nk)
+    keys_read = n_sel * B if n_sel else T   # the prefixes overlap: one read of the cache
+    hbm = keys_read * 576 * 4 + B * Hh * 576 * 4
+    t_attn = attn_ms * 1e-3
+    ach = flops / t_attn / 1e12
+    bound = "mfma" if flops / (FP32_PEAK_TFLOPS * 1e12) > hbm / (HBM_PEAK_GBS * 1e9) else "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        gbs = hbm / t_attn / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    roof.update({"kernel": "mla_attn_kernel", "kernel_us": round(attn_ms * 1e3, 2),
+                 "algorithmic_flops_per_launch": int(flops), "algorithmic_bytes_per_launch": int(hbm)})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        qh = q.cpu().numpy()
+        kvh = kvs[0].cpu().numpy()
+        idxh = None if idx is None else idx.cpu().numpy()
+        done, t_c = 0, time.perf_counter()
+        while True:  # one query token (all heads) at a time
+            b = done % B
+            if idxh is None:
+                orc.mla_decode(qh[b:b + 1], kvh, scale, lens=np.array([nk[b]], np.int32))
+            else:
+                orc.mla_decode(qh[b:b + 1], kvh, scale, idx=idxh[b:b + 1])
+            done += 1
+            if time.perf_counter() - t_c >= args.cpu_seconds or done >= 1000:
+                break
+        t_cpu = time.perf_counter() - t_c
+        cpu = {"value": round(done / t_cpu, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} query token(s) of the {args.workload} workload, all {Hh} heads "
+                         f"({t_cpu:.1f} s, single-threaded C oracle)"}
+
+    res = {
+        "metric": "MLA decode attention query tokens/s + achieved fp32 matrix TFLOP/s",
+        "value": round(K * B / elapsed, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(elapsed * 1e3 / K, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "description": cfg["note"], "B": B, "heads": Hh,
+                   "T": T, "n_sel": n_sel, "dim": 576, "latent": 512, "scale": scale,
+                   "caches": NL, "graph": use_graph,
+                   "kernels_us": {"mla_attn_kernel": round(attn_ms * 1e3, 2),
+                                  "mla_merge_kernel": round(merge_ms * 1e3, 2)}},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -25,6 +25,8 @@ EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
            "coli_rmsnorm", "coli_add_inplace")
+# every symbol declared in include/coli_mla.h
+MLA_EXPORTS = ("coli_mla_workspace_bytes", "coli_mla_decode", "coli_mla_decode_profiled")
 # every symbol declared in include/coli_place.h
 PLACE_EXPORTS = ("coli_moe_placer_create", "coli_moe_placer_destroy", "coli_moe_placer_reset",
                  "coli_moe_placer_slot_of", "coli_moe_place_plan", "coli_moe_place_ws_bytes",
@@ -84,6 +86,11 @@ def lib():
             "coli_moe_forward_placed": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                          sz, vp, sz, vp, vp, vp], ctypes.c_int),
             "coli_moe_place_prefetch": ([vp, vp, vp, i32, vp, vp], ctypes.c_int),
+            "coli_mla_workspace_bytes": ([i32, i32, i32, i32], sz),
+            "coli_mla_decode": ([vp, i32, i32, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, sz,
+                                 vp], ctypes.c_int),
+            "coli_mla_decode_profiled": ([vp, i32, i32, vp, i32, vp, vp, i32, ctypes.c_float, vp,
+                                          vp, sz, vp, i32, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -428,3 +435,34 @@ def run_layer_placed(layer: PlacedLayer, x, bufs: "Buffers", place_ws, stream=No
     return forward_placed(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
                           bufs.slots, bufs.n_union, bufs.act_mode, bufs.y, bufs.workspace,
                           place_ws, stream=stream, copy_stream=copy_stream)
+
+
+# ---- decode attention over the compressed MLA KV cache (coli_mla.h) ---------
+
+MLA_DIM, MLA_LATENT = 576, 512
+
+
+def mla_workspace_bytes(B, n_heads, T, n_sel=0) -> int:
+    return lib().coli_mla_workspace_bytes(B, n_heads, T, n_sel)
+
+
+def mla_decode(q, kv, out, workspace, scale, lens=None, idx=None, stream=None):
+    """coli_mla_decode: q [B][n_heads][576], kv [T][576], out [B][n_heads][512]
+    (device fp32); lens [B] or idx [B][n_sel] (device int32)."""
+    B, nh = q.shape[0], q.shape[1]
+    n_sel = 0 if idx is None else idx.shape[1]
+    nb = workspace.numel() * workspace.element_size()
+    _check(lib().coli_mla_decode(_ptr(q), B, nh, _ptr(kv), kv.shape[0], _ptr(lens), _ptr(idx),
+                                 n_sel, float(scale), _ptr(out), _ptr(workspace), nb,
+                                 _stream(stream)), "coli_mla_decode")
+
+
+def mla_decode_profiled(q, kv, out, workspace, scale, events, lens=None, idx=None, stream=None):
+    B, nh = q.shape[0], q.shape[1]
+    n_sel = 0 if idx is None else idx.shape[1]
+    nb = workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib().coli_mla_decode_profiled(_ptr(q), B, nh, _ptr(kv), kv.shape[0], _ptr(lens),
+                                          _ptr(idx), n_sel, float(scale), _ptr(out),
+                                          _ptr(workspace), nb, arr, len(events),
+                                          _stream(stream)), "coli_mla_decode_profiled")

@@ -12,7 +12,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcoli_moe.so")
 
 SOURCES = ["coli_moe.cpp", "route.hip", "union.hip", "expert_f32.hip", "expert_i8.hip", "place.hip",
-           "expert_i8v.hip", "combine.hip"]
+           "expert_i8v.hip", "combine.hip", "mla.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -15,7 +15,8 @@ import int4_routed_expert_bias_amd as coli
 from conftest import ROOT, gpu_available
 
 HEADERS = {os.path.join(ROOT, "include", "coli_moe.h"): "EXPORTS",
-           os.path.join(ROOT, "include", "coli_place.h"): "PLACE_EXPORTS"}
+           os.path.join(ROOT, "include", "coli_place.h"): "PLACE_EXPORTS",
+           os.path.join(ROOT, "include", "coli_mla.h"): "MLA_EXPORTS"}
 
 
 @pytest.fixture(scope="module")
@@ -176,3 +177,32 @@ def test_forward_profiled_needs_two_events_per_kernel(L):
                                          FAKE, mode, FAKE, FAKE, 1 << 30, None, holes, 2 * n,
                                          None)
         assert st == coli.COLI_E_ARG, (mode, T)
+
+
+
+def test_mla_argument_errors(L):
+    def call(q=FAKE, B=1, nh=64, kv=FAKE, T=100, lens=FAKE, idx=None, n_sel=0, scale=0.07,
+             out=FAKE, ws=FAKE, nb=1 << 30):
+        return L.coli_mla_decode(q, B, nh, kv, T, lens, idx, n_sel, ctypes.c_float(scale), out,
+                                 ws, nb, None)
+    assert call(B=0) == coli.COLI_E_SHAPE
+    assert call(B=257) == coli.COLI_E_SHAPE
+    assert call(nh=0) == coli.COLI_E_SHAPE
+    assert call(nh=129) == coli.COLI_E_SHAPE
+    assert call(T=0) == coli.COLI_E_SHAPE
+    assert call(idx=FAKE, n_sel=0) == coli.COLI_E_SHAPE
+    assert call(scale=float("inf")) == coli.COLI_E_ARG
+    assert call(scale=float("nan")) == coli.COLI_E_ARG
+    assert call(q=None) == coli.COLI_E_ARG
+    assert call(lens=None) == coli.COLI_E_ARG          # neither lens nor a key list
+    assert call(ws=None) == coli.COLI_E_ARG
+    assert call(kv=MIS) == coli.COLI_E_ALIGN
+    assert call(lens=MIS) == coli.COLI_E_ALIGN
+    assert call(nb=16) == coli.COLI_E_WORKSPACE
+    ev = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert L.coli_mla_decode_profiled(FAKE, 1, 64, FAKE, 100, FAKE, None, 0, ctypes.c_float(0.1),
+                                      FAKE, FAKE, 1 << 30, ev, 3, None) == coli.COLI_E_ARG
+    assert coli.mla_workspace_bytes(1, 64, 32768) >= 64 * 516 * 4
+    assert coli.mla_workspace_bytes(4, 128, 100, 2048) > 0
+    assert coli.mla_workspace_bytes(0, 64, 100) == 0
+    assert coli.mla_workspace_bytes(1, 64, 0) == 0
