@@ -10,16 +10,20 @@
 // mla_attn_kernel: one workgroup = 8 waves for 64 heads of one query and
 // one range of its keys; the two waves of a pair share 16 heads and split
 // the work in halves (score dims 0..287 / 288..575, output dims 0..255 /
-// 256..511).  Keys are staged 16 at a time through LDS (double buffered,
-// loads for the next tile in flight during the compute of this one).  A
-// wave computes its half of the 16 x 16 score tile with fp32 matrix-core
-// products (v_mfma_f32_16x16x4_f32, 72 per tile: its query half lives in 72
-// registers as MFMA A operands), the pair adds the halves through LDS (the
-// same sum in both waves), both run the same online base-2 softmax per head
-// row, and each accumulates P x V into its 16 output tiles.  The cached row
-// serves as key (576 dims) and value (first 512).  Partial (max, sum,
-// unnormalised output) per head and key range go to the workspace;
-// mla_merge_kernel combines the ranges in a fixed order.
+// 256..511).  Keys are staged 16 at a time through three LDS buffers (the
+// next tile's loads are in flight during the current tile, one barrier per
+// tile).  Everything is computed transposed, with the heads as the MFMA
+// columns: a wave forms its half of S^T = K Q^T (v_mfma_f32_16x16x4_f32, 72
+// per tile; its query half lives in 72 registers as B operands), the pair
+// adds the halves through LDS (the same sum in both waves), both run the same
+// online base-2 softmax per head (column), and each accumulates
+// O^T += V^T P^T into its 16 output tiles.  In that orientation the
+// probabilities are already where the next MFMA wants its B operand (key
+// 4k + s of k-step s sits in register s of the lanes of k-slot k), and the
+// rescale of a head's accumulators is lane-local.  The cached row serves as
+// key (576 dims) and value (first 512).  Partial (max, sum, unnormalised
+// output) per head and key range go to the workspace; mla_merge_kernel
+// combines the ranges in a fixed order.
 #include "../../include/coli_mla.h"
 
 #include <hip/hip_runtime.h>
@@ -34,7 +38,9 @@ namespace {
 constexpr int kD = 576, kDv = 512;
 constexpr int kKT = 16;        // keys per staged tile
 constexpr int kStr = kD + 4;   // LDS row stride in floats (conflict-free b128 reads)
-constexpr int kRec = kDv + 4;  // partial record: O[512], m, l, 2 pad (16-byte aligned)
+// partial record: O[512], m, l, padding to whole 128-byte lines (records of
+// different workgroups never share a cache line)
+constexpr int kRec = kDv + 32;
 constexpr int kHeadsPerBlock = 64;
 
 using v4f = __attribute__((__vector_size__(4 * sizeof(float)))) float;
@@ -42,15 +48,14 @@ using v4f = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 struct MlaArgs {
     const float *q, *kv;
     const int32_t *lens, *idx;
-    float *part;  // [B][H][S][kRec]
+    float *part;  // [B][S][H][kRec]
     int B, H, T, n_sel, S, kps, HG, G;
     float sl2;    // scale * log2(e)
 };
 
 struct MlaLds {
-    float kt[2][kKT][kStr];    // 74,240 B
-    float pt[4][16][kKT + 1];  // P tile of each wave pair, 4,352 B
-    float4 sx[8][64];          // score halves, 8,192 B
+    float kt[3][kKT][kStr];  // 111,360 B
+    float4 sx[2][8][64];     // score halves, by tile parity, 16,384 B
 };
 
 // Output dim of tile c = 4u + i (u < 4), column n, within a half:
@@ -72,6 +77,8 @@ __device__ __forceinline__ float row_sum16(float x)
     return x;
 }
 
+// LIST: the keys of a query are the rows of its key list, else its prefix.
+template <bool LIST>
 __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
 {
     __shared__ MlaLds sm;
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
     const int split = (L / a.HG) % a.S;
     const int b = L / (a.HG * a.S);
     int nkeys;
-    if (a.idx) nkeys = a.n_sel;
+    if constexpr (LIST) nkeys = a.n_sel;
     else nkeys = min(max(a.lens[b], 0), a.T);
     const int k0 = split * a.kps;
     const int k1 = min(nkeys, k0 + a.kps);
@@ -95,30 +102,19 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
     const int h0 = hg * kHeadsPerBlock + hb * 16;
     const bool live = h0 < a.H;  // uniform over the wave pair
 
-    // this wave's half of the query rows as MFMA A operands: qa[4m + i]
-    // holds dim 16 (18 half + m) + 4 q4 + i of head h0 + n
-    float qa[72];
-    {
-        const int hr = h0 + n;
-        const bool ok = live && hr < a.H;
-        const float4 *qr = reinterpret_cast<const float4 *>(
-            a.q + ((size_t)b * a.H + (ok ? hr : 0)) * kD) + 72 * half;
-#pragma unroll
-        for (int m = 0; m < 18; ++m) {
-            const float4 v = ok ? qr[4 * m + q4] : make_float4(0.f, 0.f, 0.f, 0.f);
-            qa[4 * m + 0] = v.x; qa[4 * m + 1] = v.y; qa[4 * m + 2] = v.z; qa[4 * m + 3] = v.w;
-        }
-    }
-
     // staging: thread tid moves float4s e = it * 512 + tid of the 16 x 144 tile
     constexpr int kTile4 = kKT * (kD / 4);          // 2,304
     constexpr int kPer = (kTile4 + 511) / 512;      // 5
     float4 stage[kPer];
-    auto key_row = [&](int pos) -> int {  // cache row of key position pos, -1 if none
-        if (pos >= k1) return -1;
-        if (!a.idx) return pos;
-        const int t = a.idx[(size_t)b * a.n_sel + pos];
-        return (t >= 0 && t < a.T) ? t : -1;
+    // cache row of key position pos, -1 if none.  Loads are unconditional
+    // (positions clamped into the range) so that they all stay in flight.
+    auto key_row = [&](int pos) -> int {
+        if constexpr (LIST) {
+            const int t = a.idx[(size_t)b * a.n_sel + min(pos, k1 - 1)];
+            return (pos < k1 && t >= 0 && t < a.T) ? t : -1;
+        } else {
+            return pos < k1 ? pos : -1;
+        }
     };
     auto load_tile = [&](int tile) {
         const int kk = k0 + tile * kKT;
@@ -127,8 +123,8 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
             const int e = it * 512 + tid;
             const int r = e / (kD / 4), c = e % (kD / 4);
             const int t = e < kTile4 ? key_row(kk + r) : -1;
-            stage[it] = t >= 0 ? reinterpret_cast<const float4 *>(a.kv + (size_t)t * kD)[c]
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 v = reinterpret_cast<const float4 *>(a.kv + (size_t)max(t, 0) * kD)[c];
+            stage[it] = t >= 0 ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto store_tile = [&](int buf) {
@@ -140,101 +136,114 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
         }
     };
 
-    v4f o[16];
+    v4f o[16];  // O^T tiles: o[4u + i][v] = O[head h0 + n][dim of row 4 q4 + v]
 #pragma unroll
     for (int c = 0; c < 16; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
-    float mrow[4], lpart[4];
+    float mcol = -INFINITY, lpart = 0.f;  // softmax state of head h0 + n
+
+    // the first key tile's loads go out before the query's
+    if (ntiles > 0) load_tile(0);
+    // this wave's half of the query of head h0 + n as MFMA B operands:
+    // qa[4m + i] holds dim 16 (18 half + m) + 4 q4 + i
+    float qa[72];
+    {
+        const int hr = h0 + n;
+        const bool ok = live && hr < a.H;
+        const float4 *qr = reinterpret_cast<const float4 *>(
+            a.q + ((size_t)b * a.H + (ok ? hr : 0)) * kD) + 72 * half;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        mrow[v] = -INFINITY;
-        lpart[v] = 0.f;
+        for (int m = 0; m < 18; ++m) {
+            const float4 v = qr[4 * m + q4];  // row 0 stands in for a missing head
+            qa[4 * m + 0] = ok ? v.x : 0.f; qa[4 * m + 1] = ok ? v.y : 0.f;
+            qa[4 * m + 2] = ok ? v.z : 0.f; qa[4 * m + 3] = ok ? v.w : 0.f;
+        }
     }
 
     if (ntiles > 0) {
-        load_tile(0);
         store_tile(0);
+        if (ntiles > 1) load_tile(1);
     }
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < ntiles) load_tile(tile + 1);
+        const int buf = tile % 3;
         v4f sh = {0.f, 0.f, 0.f, 0.f};
         if (live) {
-            // this half of the scores S[4 q4 + v][n] of key column n
+            // this half of S^T[key 4 q4 + v][head n]
             v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
             const float *kr = &sm.kt[buf][n][4 * q4 + 288 * half];
 #pragma unroll
             for (int m = 0; m < 18; ++m) {
                 const float4 kb = *reinterpret_cast<const float4 *>(kr + 16 * m);
                 v4f &acc = (m & 1) ? s1 : s0;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * m + 0], kb.x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * m + 1], kb.y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * m + 2], kb.z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * m + 3], kb.w, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qa[4 * m + 0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qa[4 * m + 1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qa[4 * m + 2], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qa[4 * m + 3], acc, 0, 0, 0);
             }
             sh = s0 + s1;
-            sm.sx[wave][lane] = make_float4(sh[0], sh[1], sh[2], sh[3]);
         }
+        // the next tile goes into the buffer last read two tiles ago
+        if (tile + 1 < ntiles) store_tile((tile + 1) % 3);
+        if (live) sm.sx[tile & 1][wave][lane] = make_float4(sh[0], sh[1], sh[2], sh[3]);
         __syncthreads();
+        if (tile + 2 < ntiles) load_tile(tile + 2);
         if (live) {
             // both waves of the pair form the same sum: low half + high half
-            const float4 other = sm.sx[wave ^ 1][lane];
-            const v4f ov = {other.x, other.y, other.z, other.w};
+            const float4 ot = sm.sx[tile & 1][wave ^ 1][lane];
+            const v4f ov = {ot.x, ot.y, ot.z, ot.w};
             const v4f full = half == 0 ? sh + ov : ov + sh;
-            const bool valid = key_row(k0 + tile * kKT + n) >= 0;
-            float pv[4];
+            const int kp = k0 + tile * kKT + 4 * q4;
+            float sv[4];
+            float mx = -INFINITY;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float s = valid ? full[v] * a.sl2 : -INFINITY;
-                const float mn = fmaxf(mrow[v], row_max16(s));
-                const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrow[v] - mn);
-                pv[v] = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mn);
-                lpart[v] = lpart[v] * alpha + pv[v];
-                mrow[v] = mn;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) o[c][v] *= alpha;
+                sv[v] = key_row(kp + v) >= 0 ? full[v] * a.sl2 : -INFINITY;
+                mx = fmaxf(mx, sv[v]);
             }
-            if (half == 0) {
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(mcol, mx);
+            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mcol - mn);
+            float pv[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sm.pt[hb][4 * q4 + v][n] = pv[v];
-            }
-        }
-        __syncthreads();
-        if (live) {
+            for (int v = 0; v < 4; ++v) pv[v] = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mn);
+            lpart = lpart * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+            mcol = mn;
 #pragma unroll
-            for (int s = 0; s < kKT / 4; ++s) {
-                const float pa = sm.pt[hb][n][4 * s + q4];
-                const float *vr = &sm.kt[buf][4 * s + q4][256 * half];
+            for (int c = 0; c < 16; ++c) o[c] *= alpha;
+            // O^T += V^T P^T; k-step s takes key 4k + s in k-slot k
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float *vr = &sm.kt[buf][4 * q4 + s][256 * half];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float4 vb = *reinterpret_cast<const float4 *>(vr + vseg(u, n));
-                    o[4 * u + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb.x, o[4 * u + 0], 0, 0, 0);
-                    o[4 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb.y, o[4 * u + 1], 0, 0, 0);
-                    o[4 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb.z, o[4 * u + 2], 0, 0, 0);
-                    o[4 * u + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb.w, o[4 * u + 3], 0, 0, 0);
+                    o[4 * u + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.x, pv[s], o[4 * u + 0], 0, 0, 0);
+                    o[4 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.y, pv[s], o[4 * u + 1], 0, 0, 0);
+                    o[4 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.z, pv[s], o[4 * u + 2], 0, 0, 0);
+                    o[4 * u + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.w, pv[s], o[4 * u + 3], 0, 0, 0);
                 }
             }
         }
-        if (tile + 1 < ntiles) store_tile(buf ^ 1);
-        __syncthreads();
     }
 
-    // partial record of each head row: O (this half), m and l (low half)
+    // partial record of head h0 + n: O (this half), m and l (low half)
     if (!live) return;
+    float l = lpart;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int h = h0 + n;
+    if (h >= a.H) return;
+    float *rec = a.part + (((size_t)b * a.S + split) * a.H + h) * kRec + 256 * half;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int h = h0 + 4 * q4 + v;
-        const float l = row_sum16(lpart[v]);
-        if (h >= a.H) continue;
-        float *rec = a.part + (((size_t)b * a.H + h) * a.S + split) * kRec;
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<float4 *>(rec + 256 * half + vseg(u, n)) =
+            *reinterpret_cast<float4 *>(rec + vseg(u, 4 * q4 + v)) =
                 make_float4(o[4 * u + 0][v], o[4 * u + 1][v], o[4 * u + 2][v], o[4 * u + 3][v]);
-        if (half == 0 && n == 0) {
-            rec[kDv] = mrow[v];
-            rec[kDv + 1] = l;
-        }
+    if (half == 0 && q4 == 0) {
+        rec[kDv] = mcol;
+        rec[kDv + 1] = l;
     }
 }
 
@@ -242,17 +251,19 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
 // when no range saw a key.  Block (b h, quarter): 8 groups of 32 threads,
 // group g sums the ranges s = g mod 8 for 128 output dims, then the groups
 // are added in ascending order (a fixed order: bitwise reproducible).
-__global__ __launch_bounds__(256) void mla_merge_kernel(const float *__restrict__ part, int S,
+__global__ __launch_bounds__(256) void mla_merge_kernel(const float *__restrict__ part, int S, int H,
                                                         float *__restrict__ out)
 {
     __shared__ float red[8];
     __shared__ float4 acc_g[8][32];
     const int bh = blockIdx.x >> 2, quarter = blockIdx.x & 3;
     const int tid = threadIdx.x, g = tid >> 5, t = tid & 31;
-    const float *pr = part + (size_t)bh * S * kRec;
+    const int b = bh / H, h = bh % H;
+    const size_t rs = (size_t)H * kRec;  // from one key range to the next
+    const float *pr = part + ((size_t)b * S * H + h) * kRec;
     // max and denominator over all ranges (block reductions)
     float m = -INFINITY;
-    for (int s = tid; s < S; s += 256) m = fmaxf(m, pr[(size_t)s * kRec + kDv]);
+    for (int s = tid; s < S; s += 256) m = fmaxf(m, pr[(size_t)s * rs + kDv]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     if ((tid & 63) == 0) red[tid >> 6] = m;
@@ -262,8 +273,8 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float *__restrict_
     float d = 0.f;
     if (M != -INFINITY)
         for (int s = tid; s < S; s += 256) {
-            const float ms = pr[(size_t)s * kRec + kDv];
-            if (ms != -INFINITY) d += __builtin_amdgcn_exp2f(ms - M) * pr[(size_t)s * kRec + kDv + 1];
+            const float ms = pr[(size_t)s * rs + kDv];
+            if (ms != -INFINITY) d += __builtin_amdgcn_exp2f(ms - M) * pr[(size_t)s * rs + kDv + 1];
         }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
@@ -278,8 +289,8 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float *__restrict_
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int s = s0 + 8 * j;
-                ms[j] = s < S ? pr[(size_t)s * kRec + kDv] : -INFINITY;
-                ov[j] = s < S ? reinterpret_cast<const float4 *>(pr + (size_t)s * kRec)[quarter * 32 + t]
+                ms[j] = s < S ? pr[(size_t)s * rs + kDv] : -INFINITY;
+                ov[j] = s < S ? reinterpret_cast<const float4 *>(pr + (size_t)s * rs)[quarter * 32 + t]
                               : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
@@ -359,10 +370,11 @@ int mla_impl(const float *q, int32_t B, int32_t n_heads, const float *kv, int32_
     a.sl2 = scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const unsigned grid = (unsigned)((pl.G + 7) / 8 * 8);
-    launch(mk, mla_attn_kernel, dim3(grid), dim3(512), 0, st, a);
+    if (idx) launch(mk, mla_attn_kernel<true>, dim3(grid), dim3(512), 0, st, a);
+    else launch(mk, mla_attn_kernel<false>, dim3(grid), dim3(512), 0, st, a);
     if (hipGetLastError() != hipSuccess) return COLI_E_DEVICE;
     launch(mk, mla_merge_kernel, dim3((unsigned)(B * n_heads * 4)), dim3(256), 0, st,
-           (const float *)a.part, pl.S, out);
+           (const float *)a.part, pl.S, n_heads, out);
     return hipGetLastError() == hipSuccess ? COLI_OK : COLI_E_DEVICE;
 }
 
