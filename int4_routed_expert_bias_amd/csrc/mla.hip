@@ -59,9 +59,13 @@ struct MlaLds {
 };
 
 // Output dim of tile c = 4u + i (u < 4), column n, within a half:
-// 16n + 4 sigma(u, n) + i.  The rotation sigma puts the 16 lanes of a row on
-// distinct LDS banks when they read their value segments.
-__device__ __forceinline__ int vseg(int u, int n) { return 16 * n + 4 * ((u + (n >> 2)) & 3); }
+// 16n + 4 sigma(u, n) + i.  The rotation sigma puts the lanes that read
+// their value segments in one LDS pass (8 lanes of 16 bytes on 32 banks,
+// 16 lanes on 64) on distinct banks.
+__device__ __forceinline__ int vseg(int u, int n)
+{
+    return 16 * n + 4 * ((u + (n >> 1) + (n >> 3)) & 3);
+}
 
 __device__ __forceinline__ float row_max16(float x)
 {
@@ -159,34 +163,51 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
         }
     }
 
+    // this half of S^T[key 4 q4 + v][head n] for the tile in buffer buf
+    auto scores = [&](int buf) -> v4f {
+        v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        const float *kr = &sm.kt[buf][n][4 * q4 + 288 * half];
+#pragma unroll
+        for (int m = 0; m < 18; ++m) {
+            const float4 kb = *reinterpret_cast<const float4 *>(kr + 16 * m);
+            v4f &acc = (m & 1) ? s1 : s0;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qa[4 * m + 0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qa[4 * m + 1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qa[4 * m + 2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qa[4 * m + 3], acc, 0, 0, 0);
+        }
+        // keep two operand reads in flight ahead of the matrix-core ops
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        return s0 + s1;
+    };
+
+    // Software pipeline: iteration t runs the softmax of tile t, the scores
+    // of tile t + 1 and the P x V of tile t (independent matrix-core work
+    // around the softmax), stores tile t + 2 into the buffer tile t - 1 left,
+    // and ends with the one barrier that publishes both.
     if (ntiles > 0) {
         store_tile(0);
         if (ntiles > 1) load_tile(1);
     }
     __syncthreads();
+    v4f sh = {0.f, 0.f, 0.f, 0.f};
+    if (ntiles > 0) {
+        if (live) sh = scores(0);
+        if (ntiles > 1) store_tile(1);
+        if (live) sm.sx[0][wave][lane] = make_float4(sh[0], sh[1], sh[2], sh[3]);
+        __syncthreads();
+        if (ntiles > 2) load_tile(2);
+    }
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile % 3;
-        v4f sh = {0.f, 0.f, 0.f, 0.f};
-        if (live) {
-            // this half of S^T[key 4 q4 + v][head n]
-            v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-            const float *kr = &sm.kt[buf][n][4 * q4 + 288 * half];
-#pragma unroll
-            for (int m = 0; m < 18; ++m) {
-                const float4 kb = *reinterpret_cast<const float4 *>(kr + 16 * m);
-                v4f &acc = (m & 1) ? s1 : s0;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qa[4 * m + 0], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qa[4 * m + 1], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qa[4 * m + 2], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qa[4 * m + 3], acc, 0, 0, 0);
-            }
-            sh = s0 + s1;
-        }
-        // the next tile goes into the buffer last read two tiles ago
-        if (tile + 1 < ntiles) store_tile((tile + 1) % 3);
-        if (live) sm.sx[tile & 1][wave][lane] = make_float4(sh[0], sh[1], sh[2], sh[3]);
-        __syncthreads();
-        if (tile + 2 < ntiles) load_tile(tile + 2);
+        const bool more = tile + 1 < ntiles;  // uniform
+        v4f sn = {0.f, 0.f, 0.f, 0.f};
         if (live) {
             // both waves of the pair form the same sum: low half + high half
             const float4 ot = sm.sx[tile & 1][wave ^ 1][lane];
@@ -209,8 +230,12 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
             for (int v = 0; v < 4; ++v) pv[v] = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mn);
             lpart = lpart * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
             mcol = mn;
+            if (more) sn = scores((tile + 1) % 3);
+            // the accumulators change only when some head's running max rose
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) o[c] *= alpha;
+                for (int c = 0; c < 16; ++c) o[c] *= alpha;
+            }
             // O^T += V^T P^T; k-step s takes key 4k + s in k-slot k
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -224,6 +249,20 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
                     o[4 * u + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.w, pv[s], o[4 * u + 3], 0, 0, 0);
                 }
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int g = 0; g < 14; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        if (more) {
+            if (tile + 2 < ntiles) store_tile((tile + 2) % 3);
+            if (live) sm.sx[(tile + 1) & 1][wave][lane] = make_float4(sn[0], sn[1], sn[2], sn[3]);
+            __syncthreads();
+            if (tile + 3 < ntiles) load_tile(tile + 3);
+            sh = sn;
         }
     }
 
