@@ -14,12 +14,19 @@
 //    [0, 15] of its even elements as the bytes of (q ^ 0x88888888) &
 //    0x0F0F0F0F and of its odd elements as the bytes of ((q >> 4) ^
 //    0x08080808) & 0x0F0F0F0F (one v_bitop3_b32 each, plus one shift);
-//  - v_cvt_f32_ubyte{0..3} turns a byte into fp32 and v_fmac_f32 accumulates
-//    it times x; the chunk sum starts at -K, K = 8 sum(x), which removes the
-//    bias: sum (code + 8) x - 8 sum x = sum code * x up to fp32 rounding
-//    (every product is exact; for integer x and power-of-two scales the
-//    whole sum is exact);
-//  - one fp16 group scale per chunk, applied with one more FMA;
+//  - v_cvt_pk_f32_fp8 turns two such bytes into fp32 at once (the gate/up
+//    streaming kernels; the others convert one byte at a time and run the
+//    same chains in units of 1, with bitwise the same results): read as OCP
+//    E4M3 numbers, the bytes 0..15 are exactly n * 2^-9 (the exponent-0
+//    values are the subnormals), so the chains run in units of 2^-9;
+//    v_fmac_f32 accumulates them times x and the chunk sum starts at -K,
+//    K = 8 sum(x) 2^-9, which removes the bias: sum (code + 8) x - 8 sum x =
+//    sum code * x, times 2^-9, up to fp32 rounding (every product is exact;
+//    for integer x and power-of-two scales the whole sum is exact);
+//  - one fp16 group scale per chunk, times 2^9, applied with one more FMA.
+//    Scaling by powers of two commutes with rounding, so every chain value
+//    is exactly 2^-9 times the value of the same chain over the integer
+//    codes, and the scaled product equals the unscaled one;
 //  - lane partials are combined with permlane swaps and DPP (reduce_values),
 //    one fixed pairing sequence for every value, so the sum of a given
 //    (token, row) does not depend on how many values a wave reduces.
@@ -47,13 +54,28 @@ struct GemvArgs {
     int T, k, cap, n_shared;
 };
 
-// K of an activation chunk: 8 sum(v), the sum in ascending element order.
+// U9 selects the units of a kernel's chains: 2^-9 (codes converted in pairs
+// by v_cvt_pk_f32_fp8) or 1 (one v_cvt_f32_ubyte per code).  Both give
+// bitwise the same results; the gate/up streaming kernels, where the
+// conversions are the VALU bottleneck, use 2^-9, the others (more registers
+// per code) units of 1.
+
+// K of an activation chunk: 8 sum(v) in the chain units, the sum in
+// ascending element order (the scaling is exact).
+template <bool U9 = false>
 __device__ __forceinline__ float chunk_K(const float (&v)[32])
 {
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) sum += v[i];
-    return 8.f * sum;
+    return U9 ? 0.015625f * sum : 8.f * sum;
+}
+
+// A weight group scale in the inverse chain units.
+template <bool U9 = false>
+__device__ __forceinline__ float wscale(uint16_t h)
+{
+    return U9 ? f16_to_f32(h) * 512.0f : f16_to_f32(h);
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4 &w, int d)
@@ -61,9 +83,21 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &w, int d)
     return d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w;
 }
 
+// Byte b of v as fp32 (one v_cvt_f32_ubyte{b}): chain units of 1.
 __device__ __forceinline__ float byte_f32(uint32_t v, int b)
 {
-    return (float)((v >> (8 * b)) & 0xFFu);  // v_cvt_f32_ubyte{b}
+    return (float)((v >> (8 * b)) & 0xFFu);
+}
+
+// The four bytes n of v (each in [0, 15]) as n * 2^-9: two
+// v_cvt_pk_f32_fp8 (chain units of 2^-9).
+template <bool U9>
+__device__ __forceinline__ void byte_vals(uint32_t v, float (&f)[4])
+{
+    static_assert(U9, "the pair conversion gives units of 2^-9");
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
 }
 
 // out[r][c] = sum_i code_i * x_i over 16-byte chunk w[r][c] of packed codes
@@ -71,7 +105,7 @@ __device__ __forceinline__ float byte_f32(uint32_t v, int b)
 // -K[c] and adds its 32 products in ascending element order.  The NR * NC
 // chains are interleaved so that no product waits on the previous one of
 // its own chain.
-template <int NR, int NC>
+template <int NR, int NC, bool U9 = false>
 __device__ __forceinline__ void chunk_dots(const uint4 (&w)[NR][NC], const float (&x)[NC][32],
                                            const float (&K)[NC], float (&out)[NR][NC])
 {
@@ -81,24 +115,45 @@ __device__ __forceinline__ void chunk_dots(const uint4 (&w)[NR][NC], const float
         for (int c = 0; c < NC; ++c) out[r][c] = -K[c];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        uint32_t lo[NR][NC], hi[NR][NC];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const uint32_t q = word_of(w[r][c], d);
-                lo[r][c] = (q ^ 0x88888888u) & 0x0F0F0F0Fu;         // even elements
-                hi[r][c] = ((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;  // odd elements
-            }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
+        if constexpr (U9) {
+            float lo[NR][NC][4], hi[NR][NC][4];
 #pragma unroll
             for (int r = 0; r < NR; ++r)
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    out[r][c] = fmaf(byte_f32(lo[r][c], b), x[c][8 * d + 2 * b], out[r][c]);
-                    out[r][c] = fmaf(byte_f32(hi[r][c], b), x[c][8 * d + 2 * b + 1], out[r][c]);
+                    const uint32_t q = word_of(w[r][c], d);
+                    byte_vals<true>((q ^ 0x88888888u) & 0x0F0F0F0Fu, lo[r][c]);         // even elements
+                    byte_vals<true>(((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu, hi[r][c]);  // odd elements
                 }
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        out[r][c] = fmaf(lo[r][c][b], x[c][8 * d + 2 * b], out[r][c]);
+                        out[r][c] = fmaf(hi[r][c][b], x[c][8 * d + 2 * b + 1], out[r][c]);
+                    }
+        } else {
+            uint32_t lo[NR][NC], hi[NR][NC];
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const uint32_t q = word_of(w[r][c], d);
+                    lo[r][c] = (q ^ 0x88888888u) & 0x0F0F0F0Fu;         // even elements
+                    hi[r][c] = ((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;  // odd elements
+                }
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        out[r][c] = fmaf(byte_f32(lo[r][c], b), x[c][8 * d + 2 * b], out[r][c]);
+                        out[r][c] = fmaf(byte_f32(hi[r][c], b), x[c][8 * d + 2 * b + 1], out[r][c]);
+                    }
+        }
     }
 }
 
@@ -362,7 +417,7 @@ __global__ __launch_bounds__(W * 64) void gateup_f32_kernel(GemvArgs a)
                     chunk_dots<RW, 1>(wl, xv, kc, dots);
 #pragma unroll
                     for (int r = 0; r < RW; ++r)
-                        racc[r * NT + tt] = fmaf(dots[r][0], f16_to_f32(sc[r][p]), racc[r * NT + tt]);
+                        racc[r * NT + tt] = fmaf(dots[r][0], wscale(sc[r][p]), racc[r * NT + tt]);
                 }
             }
         }
@@ -432,7 +487,7 @@ __global__ __launch_bounds__(W * 64) void down_f32_kernel(GemvArgs a)
             float dots[RW][1];
             chunk_dots<RW, 1>(wl, xv, kc, dots);
 #pragma unroll
-            for (int r = 0; r < RW; ++r) racc[r] = fmaf(dots[r][0], f16_to_f32(sc[r][p]), racc[r]);
+            for (int r = 0; r < RW; ++r) racc[r] = fmaf(dots[r][0], wscale(sc[r][p]), racc[r]);
         }
         reduce_values<V>(racc);
 #pragma unroll
@@ -531,7 +586,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
         for (int c = threadIdx.x; c < C; c += blockDim.x) {
             float v[32];
             load_chunk32(xt + c, C, v);
-            ks[c] = chunk_K(v);
+            ks[c] = chunk_K<true>(v);
         }
         __syncthreads();
     }
@@ -555,7 +610,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
             if (g0 + m < nsteps) {
                 float dots[2 * NP][P];
                 if constexpr (XREG) {
-                    chunk_dots<2 * NP, P>(wv[d], xr, kx, dots);
+                    chunk_dots<2 * NP, P, true>(wv[d], xr, kx, dots);
                 } else {
 #pragma unroll
                     for (int p = 0; p < P; ++p) {
@@ -565,7 +620,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
                         float dl[2 * NP][1];
 #pragma unroll
                         for (int r = 0; r < 2 * NP; ++r) wl[r][0] = wv[d][r][p];
-                        chunk_dots<2 * NP, 1>(wl, xl, kl, dl);
+                        chunk_dots<2 * NP, 1, true>(wl, xl, kl, dl);
 #pragma unroll
                         for (int r = 0; r < 2 * NP; ++r) dots[r][p] = dl[r][0];
                     }
@@ -574,7 +629,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
                 for (int r = 0; r < 2 * NP; ++r) {
                     float acc = 0.f;
 #pragma unroll
-                    for (int p = 0; p < P; ++p) acc = fmaf(dots[r][p], f16_to_f32(sv[d][r][p]), acc);
+                    for (int p = 0; p < P; ++p) acc = fmaf(dots[r][p], wscale<true>(sv[d][r][p]), acc);
                     racc[(r / NP) * (V / 2) + m * NP + r % NP] = acc;
                 }
             }
@@ -651,7 +706,7 @@ __global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
                 for (int r = 0; r < RD; ++r) {
                     float acc = 0.f;
 #pragma unroll
-                    for (int p = 0; p < P; ++p) acc = fmaf(dots[r][p], f16_to_f32(sv[d][r][p]), acc);
+                    for (int p = 0; p < P; ++p) acc = fmaf(dots[r][p], wscale(sv[d][r][p]), acc);
                     racc[m * RD + r] = acc;
                 }
             }
@@ -679,7 +734,7 @@ constexpr int kStreamTMax = 4;
 // once and used by every token.  out[r][j] is chain (row r, token j) with
 // exactly the arithmetic of chunk_dots (start at -K[j], products in
 // ascending element order).
-template <int NR, int CNT, int NX>
+template <int NR, int CNT, int NX, bool U9 = false>
 __device__ __forceinline__ void chunk_dots_tok(const uint4 (&w)[NR], const float (&x)[NX][32],
                                                const float (&K)[NX], float (&out)[NR][NX])
 {
@@ -689,18 +744,24 @@ __device__ __forceinline__ void chunk_dots_tok(const uint4 (&w)[NR], const float
         for (int j = 0; j < CNT; ++j) out[r][j] = -K[j];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        uint32_t lo[NR], hi[NR];
+        uint32_t lw[NR], hw[NR];
+        float lo[NR][4], hi[NR][4];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const uint32_t q = word_of(w[r], d);
-            lo[r] = (q ^ 0x88888888u) & 0x0F0F0F0Fu;
-            hi[r] = ((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
+            lw[r] = (q ^ 0x88888888u) & 0x0F0F0F0Fu;
+            hw[r] = ((q >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
+            if constexpr (U9) {
+                byte_vals<true>(lw[r], lo[r]);
+                byte_vals<true>(hw[r], hi[r]);
+            }
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                const float fl = byte_f32(lo[r], b), fh = byte_f32(hi[r], b);
+                const float fl = U9 ? lo[r][b] : byte_f32(lw[r], b);
+                const float fh = U9 ? hi[r][b] : byte_f32(hw[r], b);
 #pragma unroll
                 for (int j = 0; j < CNT; ++j) {
                     out[r][j] = fmaf(fl, x[j][8 * d + 2 * b], out[r][j]);
@@ -790,7 +851,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a)
             const int t = tc / C, c = tc - t * C;
             float v[32];
             load_chunk32(xt + 8 * t * C + c, C, v);
-            ks[tc] = chunk_K(v);
+            ks[tc] = chunk_K<true>(v);
         }
         __syncthreads();
     }
@@ -827,11 +888,11 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a)
                             kl[p] = ks[tok[0] * C + c];
                             load_chunk32(xt + 8 * tok[0] * C + c, C, xl[p]);
                         }
-                        chunk_dots<2, P>(wv[d], xl, kl, dots);
+                        chunk_dots<2, P, true>(wv[d], xl, kl, dots);
 #pragma unroll
                         for (int p = 0; p < P; ++p) {
-                            acc[0][0] = fmaf(dots[0][p], f16_to_f32(sv[d][0][p]), acc[0][0]);
-                            acc[1][0] = fmaf(dots[1][p], f16_to_f32(sv[d][1][p]), acc[1][0]);
+                            acc[0][0] = fmaf(dots[0][p], wscale<true>(sv[d][0][p]), acc[0][0]);
+                            acc[1][0] = fmaf(dots[1][p], wscale<true>(sv[d][1][p]), acc[1][0]);
                         }
                     } else {
 #pragma unroll
@@ -845,8 +906,8 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a)
                         }
                         const uint4 wl[2] = {wv[d][0][p], wv[d][1][p]};
                         float dl[2][NTOK];
-                        chunk_dots_tok<2, CNT, NTOK>(wl, xl, kl, dl);
-                        const float s0 = f16_to_f32(sv[d][0][p]), s1 = f16_to_f32(sv[d][1][p]);
+                        chunk_dots_tok<2, CNT, NTOK, true>(wl, xl, kl, dl);
+                        const float s0 = wscale<true>(sv[d][0][p]), s1 = wscale<true>(sv[d][1][p]);
 #pragma unroll
                         for (int j = 0; j < CNT; ++j) {
                             acc[0][j] = fmaf(dl[0][j], s0, acc[0][j]);
@@ -956,7 +1017,7 @@ __global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
                         chunk_dots_tok<RD, CNT, NTOK>(wl, xl, kl, dl);
 #pragma unroll
                         for (int r = 0; r < RD; ++r) {
-                            const float sc = f16_to_f32(sv[d][r][p]);
+                            const float sc = wscale(sv[d][r][p]);
 #pragma unroll
                             for (int j = 0; j < CNT; ++j) acc[r][j] = fmaf(dl[r][j], sc, acc[r][j]);
                         }
