@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the int4 routed-expert MoE layer on one MI355X.
 
-A step is one pass of the whole path -- coli_moe_route, coli_moe_union,
-coli_moe_forward -- over one batch of seeded synthetic tokens.
+A step is one pass of the whole path -- route and union
+(coli_moe_route_union: one launch for up to 4 tokens), coli_moe_forward --
+over one batch of seeded synthetic tokens.
 
 Workloads (--workload):
   decode         H6144 I2048 E256 top-8 + 1 shared, T=1, fp32 family
@@ -237,11 +238,8 @@ def main():
             x_in = xs[W + s] if not stacked else xhat
             if stacked:
                 coli.rmsnorm(resid, xhat, T, H, 1e-6)
-            if args.topp is None:
-                coli.route(lay, x_in, T, bufs.ids, bufs.w, bufs.workspace)
-            else:
-                coli.route_topp(lay, x_in, T, args.topp, bufs.ids, bufs.w, bufs.workspace)
-            coli.union(bufs.ids, T, k, E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union)
+            coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
+                             bufs.slots, bufs.n_union, bufs.workspace, top_p=args.topp)
             coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
                                   bufs.slots, bufs.n_union, mode, bufs.y, bufs.workspace, ev[i])
             union_sizes.append(bufs.n_union[:1].clone())

@@ -161,6 +161,18 @@ int coli_moe_route_topp(const coli_moe_layer *L, const float *x, int32_t T, floa
 int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                    int32_t *offsets, int32_t *slots, int32_t *n_union, void *hip_stream);
 
+/* Route and union in one call: exactly coli_moe_route_topp(L, x, T, top_p,
+ * topk_ids, topk_w, ...) (coli_moe_route when top_p >= 1) followed by
+ * coli_moe_union(topk_ids, T, L->k, L->E, union_ids, offsets, slots,
+ * n_union) -- the same outputs, bit for bit -- with both steps in one kernel
+ * launch for T <= 4 (one workgroup routes the tokens and unions their slots),
+ * so a decode or verify step launches one kernel fewer.  Argument checks of
+ * both calls; top_p must be > 0.  T == 0 only writes the empty union. */
+int coli_moe_route_union(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                         int32_t *topk_ids, float *topk_w, int32_t *union_ids, int32_t *offsets,
+                         int32_t *slots, int32_t *n_union, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
+
 /* Forward: expert compute and combine for the routed batch
  * ([Guide] "詳細解説" step 3; [Start] "토큰당 처리 경로").
  * For every union expert e and each of its slots (t, j), and for the shared

@@ -21,7 +21,7 @@ COLI_OK, COLI_E_ARG, COLI_E_SHAPE, COLI_E_ALIGN, COLI_E_WORKSPACE, COLI_E_DEVICE
 
 # every symbol declared in include/coli_moe.h
 EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
-           "coli_moe_route_topp", "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
+           "coli_moe_route_topp", "coli_moe_route_union", "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
            "coli_rmsnorm", "coli_add_inplace")
@@ -66,6 +66,8 @@ def lib():
             "coli_moe_route": ([vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "coli_moe_route_topp": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp], ctypes.c_int),
             "coli_moe_union": ([vp, i32, i32, i32, vp, vp, vp, vp, vp], ctypes.c_int),
+            "coli_moe_route_union": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz,
+                                      vp], ctypes.c_int),
             "coli_moe_forward": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp, vp],
                                  ctypes.c_int),
             "coli_moe_forward_profiled": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp,
@@ -148,6 +150,17 @@ def route_topp(layer, x, T, top_p, ids, w, workspace, workspace_nbytes=None, str
     nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
     _check(lib().coli_moe_route_topp(layer.ref, _ptr(x), T, float(top_p), _ptr(ids), _ptr(w),
                                      _ptr(workspace), nb, _stream(stream)), "coli_moe_route_topp")
+
+
+def route_union(layer, x, T, ids, w, union_ids, offsets, slots, n_union, workspace, top_p=None,
+                workspace_nbytes=None, stream=None):
+    """coli_moe_route_union: route (top-k, or top-p when top_p is given) and
+    union in one call (one launch for T <= 4)."""
+    nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    p = 1.0 if top_p is None else float(top_p)
+    _check(lib().coli_moe_route_union(layer.ref, _ptr(x), T, p, _ptr(ids), _ptr(w),
+                                      _ptr(union_ids), _ptr(offsets), _ptr(slots), _ptr(n_union),
+                                      _ptr(workspace), nb, _stream(stream)), "coli_moe_route_union")
 
 
 def union(ids, T, k, E, union_ids, offsets, slots, n_union, stream=None):
@@ -253,16 +266,21 @@ class Buffers:
             self.dump = torch.empty((max(db, 256),), dtype=torch.uint8, device=device)
 
 
-def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None, top_p=None):
+def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None, top_p=None, fused=True):
     """route -> union -> forward for x [T][H] (device fp32); top_p selects
-    the adaptive top-p router."""
+    the adaptive top-p router; fused routes and unions in one call
+    (coli_moe_route_union), else in two."""
     T = bufs.T
-    if top_p is None:
-        route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+    if fused:
+        route_union(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,
+                    bufs.n_union, bufs.workspace, top_p=top_p, stream=stream)
     else:
-        route_topp(layer, x, T, top_p, bufs.ids, bufs.w, bufs.workspace, stream=stream)
-    union(bufs.ids, T, layer.k, layer.E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union,
-          stream=stream)
+        if top_p is None:
+            route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+        else:
+            route_topp(layer, x, T, top_p, bufs.ids, bufs.w, bufs.workspace, stream=stream)
+        union(bufs.ids, T, layer.k, layer.E, bufs.union_ids, bufs.offsets, bufs.slots,
+              bufs.n_union, stream=stream)
     forward(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,
             bufs.n_union, bufs.act_mode, bufs.y, bufs.workspace, acc_dump=bufs.dump,
             stream=stream)
@@ -426,12 +444,8 @@ def run_layer_placed(layer: PlacedLayer, x, bufs: "Buffers", place_ws, stream=No
                      copy_stream=None, top_p=None):
     """route -> union -> forward_placed; returns the call's placement stats."""
     T = bufs.T
-    if top_p is None:
-        route(layer, x, T, bufs.ids, bufs.w, bufs.workspace, stream=stream)
-    else:
-        route_topp(layer, x, T, top_p, bufs.ids, bufs.w, bufs.workspace, stream=stream)
-    union(bufs.ids, T, layer.k, layer.E, bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union,
-          stream=stream)
+    route_union(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,
+                bufs.n_union, bufs.workspace, top_p=top_p, stream=stream)
     return forward_placed(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
                           bufs.slots, bufs.n_union, bufs.act_mode, bufs.y, bufs.workspace,
                           place_ws, stream=stream, copy_stream=copy_stream)

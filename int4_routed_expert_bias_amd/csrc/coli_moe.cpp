@@ -166,6 +166,34 @@ int coli_moe_route_topp(const coli_moe_layer *L, const float *x, int32_t T, floa
     return route_impl(L, x, T, top_p, topk_ids, topk_w, workspace, workspace_bytes, hip_stream);
 }
 
+int coli_moe_route_union(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                         int32_t *topk_ids, float *topk_w, int32_t *union_ids, int32_t *offsets,
+                         int32_t *slots, int32_t *n_union, void *workspace,
+                         size_t workspace_bytes, void *hip_stream)
+{
+    if (int st = check_layer(L, false)) return st;
+    if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    if (!(top_p > 0.0f)) return COLI_E_ARG;  // also rejects NaN
+    if (!n_union || !union_ids || !offsets) return COLI_E_ARG;
+    if (!aligned16(union_ids) || !aligned16(offsets) || !aligned16(n_union)) return COLI_E_ALIGN;
+    if (T == 0) {
+        if (int st = device_check()) return st;
+        return status_of(launch_union(nullptr, 0, L->k, L->E, union_ids, offsets, slots, n_union,
+                                      static_cast<hipStream_t>(hip_stream)));
+    }
+    if (!x || !topk_ids || !topk_w || !slots || !workspace) return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(slots) ||
+        !aligned16(workspace))
+        return COLI_E_ALIGN;
+    const Workspace lay = workspace_layout(L->H, L->I, L->E, L->k, T, COLI_ACT_F32, L->n_shared);
+    if (workspace_bytes < lay.route_end) return COLI_E_WORKSPACE;
+    if (int st = device_check()) return st;
+    RouteIO io{x, T, topk_ids, topk_w,
+               reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + lay.logits), top_p};
+    UnionIO un{union_ids, offsets, slots, n_union};
+    return status_of(launch_route(to_dev(L), io, static_cast<hipStream_t>(hip_stream), &un));
+}
+
 int coli_moe_union(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                    int32_t *offsets, int32_t *slots, int32_t *n_union, void *hip_stream)
 {

@@ -212,7 +212,15 @@ struct RouteIO {
 // Compute units of the current device (cached per device on first use).
 int device_cu_count();
 
-hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st);
+// Union outputs for launch_route (NULL: route only).
+struct UnionIO {
+    int32_t *union_ids, *offsets, *slots, *n_union;
+};
+
+// Route; with un, also the batch-union of the routed slots (in the top-k
+// launch itself for T <= 4, else by launch_union after it).
+hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st,
+                        const UnionIO *un = nullptr);
 
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                         int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st);

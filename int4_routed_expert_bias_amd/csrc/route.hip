@@ -10,6 +10,7 @@
 // top-k: one wave per token; lane l holds experts l, l+64, ...; k rounds of
 // a wave-wide argmax on (key desc, expert asc).
 #include "common.h"
+#include "union_wave.h"
 
 namespace coli {
 
@@ -192,13 +193,22 @@ __device__ __forceinline__ float logit_at(const float *__restrict__ logits,
     return (float)acc;
 }
 
-template <int KPL>
+// Union outputs of a routed batch, written by the top-k kernel itself when
+// the batch fits one workgroup (T <= 4, so T * k <= 64).
+struct UnionOut {
+    int32_t *union_ids, *offsets, *slots, *n_union;
+    int cap;
+};
+
+// UNION: a single workgroup also forms the batch-union of its tokens.
+template <int KPL, bool UNION = false>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    const double *__restrict__ part, int S,
                                                    const float *__restrict__ bias, int T, int E,
                                                    int k, float top_p, int32_t *__restrict__ ids,
-                                                   float *__restrict__ w)
+                                                   float *__restrict__ w, UnionOut uo = {})
 {
+    __shared__ int32_t sid[64];  // the batch's selections (UNION)
     __shared__ uint32_t sk[4][COLI_MAX_K_DEV];
     __shared__ int32_t se[4][COLI_MAX_K_DEV];
     __shared__ float ss[4][COLI_MAX_K_DEV];
@@ -283,10 +293,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         }
         ids[(size_t)t * k + rank] = rank < kp ? me : -1;
         w[(size_t)t * k + rank] = rank < kp ? sj / sum : 0.f;
+        if constexpr (UNION) sid[t * k + rank] = rank < kp ? me : -1;
+    }
+    if constexpr (UNION) {
+        __syncthreads();
+        if (wv == 0) {
+            const int n = T * k;
+            union_wave(lane, lane < n ? sid[lane] : -1, E, uo.cap, uo.union_ids, uo.offsets,
+                       uo.slots, uo.n_union);
+        }
     }
 }
 
-hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st)
+hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st, const UnionIO *un)
 {
     const int T = io.T, H = L.H, E = L.E;
     if (T <= 0) return hipSuccess;
@@ -315,9 +334,25 @@ hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int kpl = (E + 63) / 64;
+    // a batch of at most 4 tokens is one top-k workgroup: it also forms the union
+    const bool fuse = un && T <= 4;
+    UnionOut uo{};
+    if (un) {
+        uo.union_ids = un->union_ids; uo.offsets = un->offsets; uo.slots = un->slots;
+        uo.n_union = un->n_union;
+        const int n = T * L.k;
+        uo.cap = n < E ? n : E;
+    }
 #define COLI_TOPK(N) \
-    if (kpl <= N) { hipLaunchKernelGGL(topk_kernel<N>, dim3((T + 3) / 4), dim3(256), 0, st, io.logits, \
-                                       part, S, L.router_bias, T, E, L.k, io.top_p, io.ids, io.w); return hipGetLastError(); }
+    if (kpl <= N) { \
+        if (fuse) hipLaunchKernelGGL((topk_kernel<N, true>), dim3(1), dim3(256), 0, st, io.logits, part, S, \
+                                     L.router_bias, T, E, L.k, io.top_p, io.ids, io.w, uo); \
+        else hipLaunchKernelGGL((topk_kernel<N, false>), dim3((T + 3) / 4), dim3(256), 0, st, io.logits, \
+                                part, S, L.router_bias, T, E, L.k, io.top_p, io.ids, io.w, uo); \
+        err = hipGetLastError(); \
+        if (err != hipSuccess || !un || fuse) return err; \
+        return launch_union(io.ids, T, L.k, E, un->union_ids, un->offsets, un->slots, un->n_union, st); \
+    }
     COLI_TOPK(1)
     COLI_TOPK(2)
     COLI_TOPK(4)

@@ -14,6 +14,7 @@
 //      and the last lane of a run advances the cursor.
 // The result is the stable order (ascending slot) and is deterministic.
 #include "common.h"
+#include "union_wave.h"
 
 namespace coli {
 
@@ -139,8 +140,7 @@ __global__ __launch_bounds__(W * 64) void union_kernel(const int32_t *__restrict
     }
 }
 
-// Small batches (T*k <= 64): one wave sorts the 64 keys (id << 6 | slot)
-// with a bitonic network and reads the union off the sorted order.
+// Small batches (T*k <= 64): one wave (union_wave.h).
 __global__ __launch_bounds__(64) void union_small_kernel(const int32_t *__restrict__ ids, int n,
                                                          int E, int cap,
                                                          int32_t *__restrict__ union_ids,
@@ -149,40 +149,7 @@ __global__ __launch_bounds__(64) void union_small_kernel(const int32_t *__restri
                                                          int32_t *__restrict__ n_union)
 {
     const int lane = threadIdx.x;
-    int id = (lane < n) ? ids[lane] : -1;
-    const bool valid = id >= 0 && id < E;
-    uint32_t key = valid ? ((uint32_t)id << 6 | (uint32_t)lane) : 0xFFFFFFFFu;
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride >= 1; stride >>= 1) {
-            const uint32_t other = __shfl_xor(key, stride, 64);
-            const bool ascending = (lane & size) == 0 || size == 64;
-            const bool lower = (lane & stride) == 0;
-            const uint32_t lo = min(key, other), hi = max(key, other);
-            key = (lower == ascending) ? lo : hi;
-        }
-    }
-    const bool has = key != 0xFFFFFFFFu;
-    const int sid = has ? (int)(key >> 6) : -1;
-    const int prev = __shfl_up(sid, 1, 64);
-    const bool first = has && (lane == 0 || prev != sid);
-    const uint64_t fm = __ballot(first);
-    const int U = __popcll(fm);
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int upos = __popcll(fm & lt_mask);
-    if (has) slots[lane] = (int32_t)(key & 63u);
-    if (first && upos < cap) {
-        union_ids[upos] = sid;
-        offsets[upos] = lane;
-    }
-    const int kept = __popcll(__ballot(has));  // slots with an expert
-    if (lane >= U && lane < cap) union_ids[lane] = -1;
-    if (lane >= U && lane <= cap) offsets[lane] = kept;
-    if (lane == 0) {
-        n_union[0] = U;
-        if (cap == 64) offsets[64] = kept;
-    }
+    union_wave(lane, lane < n ? ids[lane] : -1, E, cap, union_ids, offsets, slots, n_union);
 }
 
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,

@@ -206,3 +206,21 @@ def test_mla_argument_errors(L):
     assert coli.mla_workspace_bytes(4, 128, 100, 2048) > 0
     assert coli.mla_workspace_bytes(0, 64, 100) == 0
     assert coli.mla_workspace_bytes(1, 64, 0) == 0
+
+
+def test_route_union_argument_errors(L):
+    def ru(lay, T=4, p=1.0, x=FAKE, u=FAKE, off=FAKE, sl=FAKE, nu=FAKE, nb=1 << 20):
+        return L.coli_moe_route_union(ctypes.byref(lay) if lay is not None else None, x, T,
+                                      ctypes.c_float(p), FAKE, FAKE, u, off, sl, nu, FAKE, nb, None)
+    assert ru(None) == coli.COLI_E_ARG
+    assert ru(layer(H=100)) == coli.COLI_E_SHAPE
+    assert ru(layer(), T=-1) == coli.COLI_E_SHAPE
+    assert ru(layer(), p=0.0) == coli.COLI_E_ARG
+    assert ru(layer(), p=float("nan")) == coli.COLI_E_ARG
+    assert ru(layer(), nu=None) == coli.COLI_E_ARG
+    assert ru(layer(), u=None) == coli.COLI_E_ARG
+    assert ru(layer(), sl=None) == coli.COLI_E_ARG
+    assert ru(layer(), x=None) == coli.COLI_E_ARG
+    assert ru(layer(), off=MIS) == coli.COLI_E_ALIGN
+    assert ru(layer(), x=MIS) == coli.COLI_E_ALIGN
+    assert ru(layer(), nb=16) == coli.COLI_E_WORKSPACE

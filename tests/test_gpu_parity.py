@@ -203,6 +203,38 @@ def test_topp_route_union_forward(name, p, mode):
     print(f"{name} p={p}: union {nu} of {plain} experts, kept slots {kept.size}/{T * k}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 9, 40])
+@pytest.mark.parametrize("top_p", [None, 0.7])
+def test_route_union_equals_route_then_union(T, top_p):
+    """coli_moe_route_union (one launch for T <= 4) gives the bits of
+    coli_moe_route[_topp] followed by coli_moe_union."""
+    import torch
+    lay = workload_layer("decode") if T <= 4 else make_layer(512, 256, 64, 8, wid=66)
+    x = torch.from_numpy(synth.activations(lay.H, T, wid=66 + T)).cuda()
+    outs = []
+    for fused in (True, False):
+        b = coli.Buffers(lay.dev, T, coli.ACT_F32)
+        for t in (b.ids, b.union_ids, b.offsets, b.slots, b.n_union):
+            t.fill_(-7)
+        b.w.fill_(-7.0)
+        if fused:
+            coli.route_union(lay.dev, x, T, b.ids, b.w, b.union_ids, b.offsets, b.slots, b.n_union,
+                             b.workspace, top_p=top_p)
+        else:
+            if top_p is None:
+                coli.route(lay.dev, x, T, b.ids, b.w, b.workspace)
+            else:
+                coli.route_topp(lay.dev, x, T, top_p, b.ids, b.w, b.workspace)
+            coli.union(b.ids, T, lay.k, lay.E, b.union_ids, b.offsets, b.slots, b.n_union)
+        torch.cuda.synchronize()
+        n_kept = int(b.offsets[int(b.n_union[0].item())].item())
+        outs.append([b.ids.cpu().numpy(), b.w.cpu().numpy().view(np.uint32),
+                     b.union_ids.cpu().numpy(), b.offsets.cpu().numpy(),
+                     b.slots[:n_kept].cpu().numpy(), b.n_union[:1].cpu().numpy()])
+    for a, c in zip(*outs):
+        assert np.array_equal(a, c)
+
+
 def test_topp_one_is_plain_topk():
     import torch
     lay = workload_layer("tiny")
