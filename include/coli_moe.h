@@ -228,8 +228,9 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
  * T tokens without acc_dump (0 if the mode is unknown), and the name of the
  * i-th one: the HIP kernel function as it appears in a profiler trace
  * (template arguments omitted).  Both depend on T: T == 1 and 2 <= T <= 4
- * run streaming kernels in the fp32 family, T <= 4 streaming kernels in the
- * int8 family (no tile schedule).  NULL if out of range. */
+ * run streaming kernels in the fp32 family (at T == 1 the down projection
+ * and the combine share one launch), T <= 4 streaming kernels in the int8
+ * family (no tile schedule).  NULL if out of range. */
 int coli_moe_forward_kernel_count(int32_t act_mode, int32_t T);
 const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
 

@@ -282,7 +282,7 @@ int coli_moe_forward_kernel_count(int32_t act_mode, int32_t T)
 
 const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
 {
-    static const char *f32_one[] = {"gateup_t1_kernel", "down_t1_kernel", "combine_kernel"};
+    static const char *f32_one[] = {"gateup_t1_kernel", "down_t1c_kernel"};
     static const char *f32_few[] = {"gateup_mt_kernel", "down_mt_kernel", "combine_kernel"};
     static const char *f32[] = {"gateup_f32_kernel", "down_f32_kernel", "combine_kernel"};
     static const char *i8_few[] = {"quant_rows_kernel", "gateup_i8v_kernel", "down_i8v_kernel",

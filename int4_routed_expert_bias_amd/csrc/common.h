@@ -242,7 +242,7 @@ struct ForwardIO {
 // (batches of at most kI8StreamTMax tokens stream without a tile schedule).
 inline int forward_kernel_count(int act_mode, int T)
 {
-    if (act_mode == 0) return 3;
+    if (act_mode == 0) return T == 1 ? 2 : 3;  // T == 1: down and combine in one launch
     if (act_mode == 1) return T <= kI8StreamTMax ? 4 : 5;
     return 0;
 }

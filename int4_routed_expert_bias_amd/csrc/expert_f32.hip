@@ -36,6 +36,7 @@
 #include "stream.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace coli {
 
@@ -647,22 +648,24 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
     }
 }
 
+// Rows of one workgroup of the fused down + combine (at most), and its
+// waves (at most): a top-8 selection plus the shared expert, one wave each.
+constexpr int kDownRowsMax = 64;
+constexpr int kDownT1cWaves = 9;
+
 // Down projection for one token.  Unit (row block) = RD rows of one entry.
 // A wave loads its entry's h chunk once and keeps it in registers
-// while it streams its row blocks.
+// while it streams its row blocks (those of sp).  Each output value is also
+// stored to so[out row][local index] when so is given (the fused combine).
 template <int P, int RD, int M, int DEPTH>
-__global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
+__device__ __forceinline__ void down_t1_rows(const GemvArgs &a, const T1Split &sp, int U, int lane,
+                                             float (*so)[kDownRowsMax])
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
     constexpr int V = next_pow2(RD * M), N = reduced_count(V);
     static_assert(V <= 64, "at most 64 values per reduction");
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32;
-    const int U = a.n_union[0];
-    const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, a.N / RD);
     const int nsteps = sp.nsteps;
-    if (nsteps == 0) return;
     const uint8_t *wb;
     const uint16_t *sb;
     int orow;
@@ -716,9 +719,62 @@ __global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             const int vi = reduced_value<V>(j, lane), m = vi / RD;
-            if (value_writer<V>(j, lane) && vi < RD * M && g0 + m < nsteps)
+            if (value_writer<V>(j, lane) && vi < RD * M && g0 + m < nsteps) {
                 orow_p[(sp.part + (g0 + m) * sp.wpe) * RD + vi % RD] = racc[j];
+                if (so) so[orow][(g0 + m) * RD + vi % RD] = racc[j];
+            }
         }
+    }
+}
+
+template <int P, int RD, int M, int DEPTH>
+__global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int U = a.n_union[0];
+    const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, a.N / RD);
+    if (sp.nsteps == 0) return;
+    down_t1_rows<P, RD, M, DEPTH>(a, sp, U, lane, nullptr);
+}
+
+// Down projection and combine for one token in one launch.  Workgroup g
+// owns row blocks g, g + G, g + 2G, ... (G workgroups, at most
+// kDownRowsMax / RD blocks each) of EVERY entry: wave v computes entries
+// v, v + NW, ... (NW waves) for those rows and leaves the values in LDS as
+// well; after a barrier the workgroup forms y of its rows with exactly the
+// combine's arithmetic (slots in order, fp32 fma chain, dropped slots
+// skipped, then the shared expert added), so y is bitwise that of the
+// two-launch form.
+template <int P, int RD, int M, int DEPTH>
+__global__ __launch_bounds__(64 * kDownT1cWaves) void down_t1c_kernel(GemvArgs a, const int32_t *__restrict__ ids,
+                                                        const float *__restrict__ w,
+                                                        float *__restrict__ y)
+{
+    __shared__ float so[COLI_MAX_K_DEV + 1][kDownRowsMax];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int NW = blockDim.x >> 6;
+    const int U = a.n_union[0];
+    const int nblocks = a.N / RD, G = gridDim.x, g = blockIdx.x;
+    T1Split sp;
+    sp.part = g;
+    sp.wpe = G;
+    sp.nsteps = g < nblocks ? (nblocks - g + G - 1) / G : 0;
+    for (int ue = wave; ue < U + a.n_shared && sp.nsteps > 0; ue += NW) {
+        sp.ue = ue;
+        down_t1_rows<P, RD, M, DEPTH>(a, sp, U, lane, so);
+    }
+    __syncthreads();
+    const int k = a.k, i = threadIdx.x;
+    if (i < sp.nsteps * RD) {
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) {
+            if (ids[j] < 0) continue;
+            acc = fmaf(w[j], so[j][i], acc);
+        }
+        if (a.n_shared) acc += so[k][i];
+        y[(g + (i / RD) * G) * RD + i % RD] = acc;
     }
 }
 
@@ -1088,6 +1144,23 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
     return err;
 }
 
+// Workgroups of NW waves of the fused down + combine kernel (variant P)
+// resident on one CU at once (at least 1), cached per device.
+static int resident_blocks(const void *kern, int P, int NW)
+{
+    static std::atomic<int> cache[8][4][16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) dev = 0;
+    std::atomic<int> &c = cache[dev][P - 1][NW - 1];
+    int n = c.load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * NW, 0) != hipSuccess || n < 1)
+            n = 1;
+        c.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // T == 1: the streaming kernels.  Launch shapes measured on MI355X with the
 // decode layer (H 6144, I 2048, 9 entries): gate/up runs one 4-wave
 // workgroup per CU (its register ring plus the x chunks allow two waves per
@@ -1121,18 +1194,37 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         a.in = h; a.in_by_slot = 1;
         a.out = o; a.out_ld = L.H;
         const int P = (L.I / 32 + 63) / 64;
+        if (io.combine) {
+#ifndef COLI_DN1C_RD
+#define COLI_DN1C_RD 4
+#define COLI_DN1C_M 4
+#define COLI_DN1C_DEPTH 2
+#endif
+            constexpr int RD = COLI_DN1C_RD, M = COLI_DN1C_M, DEPTH = COLI_DN1C_DEPTH;
+            // fused with the combine: NW waves per workgroup cover the entries;
+            // as many workgroups as are resident at once (one round), each
+            // with at most kDownRowsMax rows
+            const int nblocks = L.H / RD, NW = std::min(entries, kDownT1cWaves);
+            const dim3 block(64 * NW);
+#define COLI_DN1C(P_) \
+            if (P == P_) { \
+                const auto kern = down_t1c_kernel<P_, RD, M, DEPTH>; \
+                const int per_cu = resident_blocks(reinterpret_cast<const void *>(kern), P_, NW); \
+                const int G = std::min(nblocks, std::max(per_cu * cus, \
+                                                         (nblocks * RD + kDownRowsMax - 1) / kDownRowsMax)); \
+                launch(mk, kern, dim3(G), block, 0, st, a, io.ids, io.w, io.y); \
+            }
+            COLI_DN1C(1) COLI_DN1C(2) COLI_DN1C(3) COLI_DN1C(4)
+#undef COLI_DN1C
+            return hipGetLastError();
+        }
         const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
 #define COLI_DN1(P_) \
         if (P == P_) launch(mk, (down_t1_kernel<P_, RD, M, DEPTH>), grid, block, 0, st, a);
         COLI_DN1(1) COLI_DN1(2) COLI_DN1(3) COLI_DN1(4)
 #undef COLI_DN1
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        return hipGetLastError();
     }
-    hipError_t err = io.combine
-        ? launch_combine(o, io.ids, io.w, io.T, L.k, L.H, L.n_shared, io.y, st, mk)
-        : hipSuccess;
-    return err;
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk)

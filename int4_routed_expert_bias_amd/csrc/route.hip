@@ -10,11 +10,19 @@
 // top-k: one wave per token; lane l holds experts l, l+64, ...; k rounds of
 // a wave-wide argmax on (key desc, expert asc).
 #include "common.h"
+#include "stream.h"
 #include "union_wave.h"
 
 namespace coli {
 
 // --- small T: grid = E workgroups of 256 threads (4 waves split H) -------
+// A lane owns the float4 columns lane, lane + 64, ... of its wave's quarter
+// (at most kGemvCols of them); all of its weight loads, and then a token's
+// activation loads, are issued before the first product, so the kernel pays
+// one memory latency per token instead of one per column.  The products are
+// accumulated in ascending column order per lane, as in a plain loop.
+constexpr int kGemvCols = COLI_MAX_H_DEV / 4 / 4 / 64;  // float4 columns per lane, at most
+
 template <int NT>
 __global__ __launch_bounds__(256) void logits_gemv_kernel(const float *__restrict__ x,
                                                           const float *__restrict__ Wr,
@@ -27,20 +35,35 @@ __global__ __launch_bounds__(256) void logits_gemv_kernel(const float *__restric
     const int H4 = H >> 2;
     const int per = (H4 + 3) / 4;  // float4 columns per wave
     const int c0 = wave * per, c1 = min(H4, c0 + per);
-    const float4 *w4 = reinterpret_cast<const float4 *>(Wr + (size_t)e * H);
+    // buffer loads: columns outside the wave's quarter get an offset past
+    // the row and read 0 without touching memory
+    uint32_t off[kGemvCols];
+#pragma unroll
+    for (int i = 0; i < kGemvCols; ++i) {
+        const int c = c0 + lane + 64 * i;
+        off[i] = c < c1 ? (uint32_t)c * 16 : kOOB;
+    }
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wr + (size_t)e * H, (uint32_t)H * 4);
+    uint4 wv[kGemvCols];
+#pragma unroll
+    for (int i = 0; i < kGemvCols; ++i) wv[i] = load16(rw, off[i]);
     double acc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = 0.0;
-    for (int c = c0 + lane; c < c1; c += 64) {
-        float4 wv = w4[c];
+    for (int t = 0; t < NT; ++t) {
+        acc[t] = 0.0;
+        if (t < T) {
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t * H, (uint32_t)H * 4);
+            uint4 xv[kGemvCols];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < T) {
-                float4 xv = reinterpret_cast<const float4 *>(x + (size_t)t * H)[c];
-                acc[t] = fma((double)xv.x, (double)wv.x, acc[t]);
-                acc[t] = fma((double)xv.y, (double)wv.y, acc[t]);
-                acc[t] = fma((double)xv.z, (double)wv.z, acc[t]);
-                acc[t] = fma((double)xv.w, (double)wv.w, acc[t]);
+            for (int i = 0; i < kGemvCols; ++i) xv[i] = load16(rx, off[i]);
+            // (a column outside the quarter adds 0 * 0: acc starts at +0 and
+            // never becomes -0, so acc + 0 is acc, bit for bit)
+#pragma unroll
+            for (int i = 0; i < kGemvCols; ++i) {
+                acc[t] = fma((double)__uint_as_float(xv[i].x), (double)__uint_as_float(wv[i].x), acc[t]);
+                acc[t] = fma((double)__uint_as_float(xv[i].y), (double)__uint_as_float(wv[i].y), acc[t]);
+                acc[t] = fma((double)__uint_as_float(xv[i].z), (double)__uint_as_float(wv[i].z), acc[t]);
+                acc[t] = fma((double)__uint_as_float(xv[i].w), (double)__uint_as_float(wv[i].w), acc[t]);
             }
         }
     }
@@ -212,17 +235,45 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     __shared__ uint32_t sk[4][COLI_MAX_K_DEV];
     __shared__ int32_t se[4][COLI_MAX_K_DEV];
     __shared__ float ss[4][COLI_MAX_K_DEV];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __shared__ float sg[4][64 * KPL];  // each expert's sigmoid score, per wave
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int t = blockIdx.x * 4 + wv;
     const bool live = t < T;
     const int tr = live ? t : 0;
+    // the token's logits and the biases: every load issued before the first
+    // use (buffer loads; experts past E read 0 and are not keys)
+    float lg[KPL], bs[KPL];
+    {
+        uint32_t off[KPL];
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) off[i] = lane + 64 * i < E ? (uint32_t)(lane + 64 * i) * 4 : kOOB;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, (uint32_t)E * 4);
+        if (S == 0) {
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)tr * E, (uint32_t)E * 4);
+#pragma unroll
+            for (int i = 0; i < KPL; ++i)
+                lg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, off[i], 0, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < KPL; ++i)
+                lg[i] = lane + 64 * i < E ? logit_at(logits, part, S, T, E, tr, lane + 64 * i) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+            bs[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, off[i], 0, 0));
+        // all values present here (one wait for every load), so that no
+        // load is sunk into the conditional code below
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) asm volatile("" : "+v"(lg[i]), "+v"(bs[i]));
+    }
     uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = (live && e < E) ? order_bits(sigmoid_fp64(logit_at(logits, part, S, T, E, tr, e)) +
-                                              bias[e])
-                                 : 0u;
+        const float sgm = sigmoid_fp64(lg[i]);
+        sg[wv][e] = sgm;
+        key[i] = (live && e < E) ? order_bits(sgm + bs[i]) : 0u;
     }
     // largest tau with #{key >= tau} >= k  (valid keys are >= 1)
     uint32_t tau = 0;
@@ -269,7 +320,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     __syncthreads();
     float sj = 0.f;
     if (live && lane < k) {
-        sj = sigmoid_fp64(logit_at(logits, part, S, T, E, tr, me));
+        sj = sg[wv][me];
         ss[wv][rank] = sj;
     }
     __syncthreads();

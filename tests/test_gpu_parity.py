@@ -338,6 +338,19 @@ def test_all_experts_selected():
         assert out["n_union"] == 6
 
 
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_single_token_widest_selection(n_shared):
+    """T = 1 with k = 16: the one-launch down + combine runs 16 or 17 entries
+    (with the shared expert one wave computes two), over a ragged row count
+    and over the decode layer's 1,536 row blocks."""
+    for H, I, E, wid in ((320, 192, 40, 67), (6144, 2048, 64, 68)):
+        lay = make_layer(H, I, E, 16, wid=wid, n_shared=n_shared)
+        for t in range(2):
+            x = synth.activations(H, 1, wid=wid + 10 * t)
+            out, _, _ = full_check(lay, x, coli.ACT_F32)
+            assert out["n_union"] == 16
+
+
 def test_rmsnorm_and_add():
     import torch
     x = (np.random.default_rng(1).standard_normal((33, 640)) * 7).astype(np.float32)
