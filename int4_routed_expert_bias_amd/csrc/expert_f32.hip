@@ -1107,8 +1107,10 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
     const int cus = device_cu_count();
     {
         // one 4-wave workgroup per CU (eight waves measured slower: more
-        // concurrent streams lose DRAM locality)
-        constexpr int M = 4, DEPTH = 2, WPB = 4;
+        // concurrent streams lose DRAM locality); reductions over M = 2
+        // stages (M = 4 measured 6% slower: twice the code per token count
+        // and more live registers)
+        constexpr int M = 2, DEPTH = 2, WPB = 4;
         a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
         a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
         a.in = io.x; a.in_by_slot = 0;
