@@ -60,7 +60,7 @@ __device__ __forceinline__ int perm8_pos(int kk)
 // workspace layout (offsets in bytes, each region 256-byte aligned)
 
 struct Workspace {
-    size_t logits;   // route: [T][E] f32 logits, or [S][T][E] f64 partials
+    size_t logits;   // route: [T][E] f32 sigmoid scores, or [S][T][E] f64 logit partials
     size_t route_end;
     // forward, shared by both families
     size_t o;        // [R][H] f32 expert outputs per slot / shared row

@@ -5,17 +5,26 @@
 //
 // logits = x . Wr^T accumulated in fp64 and rounded once to fp32, so the
 // selection does not depend on summation order at fp32 precision.
-//   small T: one workgroup per expert row streams Wr once (HBM-bound);
+//   small T: one workgroup per expert row streams Wr once (HBM-bound) and
+//            writes the expert's sigmoid score;
 //   large T: fp64 MFMA GEMM split over K, partials added by the top-k kernel.
-// top-k: one wave per token; lane l holds experts l, l+64, ...; k rounds of
-// a wave-wide argmax on (key desc, expert asc).
+// top-k: one wave per token; lane l holds experts l, l+64, ...; the k-th
+// largest key by a bitwise radix select, ties by lower expert.
 #include "common.h"
 #include "stream.h"
 #include "union_wave.h"
 
 namespace coli {
 
+// Router score of a logit: sigmoid in fp64 of the fp32 logit, rounded to fp32.
+__device__ __forceinline__ float sigmoid_fp64(float l)
+{
+    return (float)(1.0 / (1.0 + exp(-(double)l)));
+}
+
 // --- small T: grid = E workgroups of 256 threads (4 waves split H) -------
+// Each workgroup writes the score of its expert (the logit rounded to fp32,
+// then its sigmoid), so the top-k kernel starts from scores.
 // A lane owns the float4 columns lane, lane + 64, ... of its wave's quarter
 // (at most kGemvCols of them); all of its weight loads, and then a token's
 // activation loads, are issued before the first product, so the kernel pays
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(256) void logits_gemv_kernel(const float *__restric
     if (threadIdx.x < NT && (int)threadIdx.x < T) {
         int t = threadIdx.x;
         double s = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
-        logits[(size_t)t * E + e] = (float)s;
+        logits[(size_t)t * E + e] = sigmoid_fp64((float)s);
     }
 }
 
@@ -183,10 +192,6 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const float *__restric
 // Radix select: the k-th largest key is found bit by bit with wave ballots
 // (32 rounds, no shuffles); keys equal to it are taken in expert order; the
 // k winners are then ordered by (key desc, expert asc) through LDS.
-__device__ __forceinline__ float sigmoid_fp64(float l)
-{
-    return (float)(1.0 / (1.0 + exp(-(double)l)));
-}
 
 // Monotone map of an fp32 key to uint32 (larger float -> larger integer);
 // -0 is folded into +0 first so that equal keys compare equal.
@@ -196,8 +201,8 @@ __device__ __forceinline__ uint32_t order_bits(float z)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Logit of (t, e): the GEMV's fp32 value, or the fp64 partials of the S
-// K-splits added in split order and rounded once to fp32.
+// Logit of (t, e) for S >= 1: the fp64 partials of the S K-splits added in
+// split order and rounded once to fp32 (S == 0: the stored value).
 __device__ __forceinline__ float logit_at(const float *__restrict__ logits,
                                           const double *__restrict__ part, int S, int T, int E,
                                           int t, int e)
@@ -241,8 +246,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     const int t = blockIdx.x * 4 + wv;
     const bool live = t < T;
     const int tr = live ? t : 0;
-    // the token's logits and the biases: every load issued before the first
-    // use (buffer loads; experts past E read 0 and are not keys)
+    // the token's scores (S == 0: written by the GEMV) or logits, and the
+    // biases: every load issued before the first use (buffer loads; experts
+    // past E read 0 and are not keys)
     float lg[KPL], bs[KPL];
     {
         uint32_t off[KPL];
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        const float sgm = sigmoid_fp64(lg[i]);
+        const float sgm = S == 0 ? lg[i] : sigmoid_fp64(lg[i]);
         sg[wv][e] = sgm;
         key[i] = (live && e < E) ? order_bits(sgm + bs[i]) : 0u;
     }
