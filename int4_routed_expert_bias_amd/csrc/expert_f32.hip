@@ -1197,12 +1197,8 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         a.out = o; a.out_ld = L.H;
         const int P = (L.I / 32 + 63) / 64;
         if (io.combine) {
-#ifndef COLI_DN1C_RD
-#define COLI_DN1C_RD 4
-#define COLI_DN1C_M 4
-#define COLI_DN1C_DEPTH 2
-#endif
-            constexpr int RD = COLI_DN1C_RD, M = COLI_DN1C_M, DEPTH = COLI_DN1C_DEPTH;
+            // (reductions over M = 2 stages: 17.6 us against 18.1 for 4 and 19.6 for 8)
+            constexpr int RD = 4, M = 2, DEPTH = 2;
             // fused with the combine: NW waves per workgroup cover the entries;
             // as many workgroups as are resident at once (one round), each
             // with at most kDownRowsMax rows
