@@ -351,6 +351,18 @@ def test_single_token_widest_selection(n_shared):
             assert out["n_union"] == 16
 
 
+@pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
+def test_maximum_hidden_sizes(mode):
+    """H = I = 8192 (the library's maximum): four activation chunks per lane
+    in the streaming kernels, the largest LDS staging of 4 tokens, the widest
+    router rows; the oracle checks every token of small batches and sampled
+    tokens of a batch that runs the grouped GEMM."""
+    lay = make_layer(8192, 8192, 4, 2, wid=69)
+    for T, rows in ((1, None), (3, None), (37, [0, 18, 36])):
+        x = synth.activations(8192, T, wid=69 + T)
+        full_check(lay, x, mode, rows=rows)
+
+
 def test_rmsnorm_and_add():
     import torch
     x = (np.random.default_rng(1).standard_normal((33, 640)) * 7).astype(np.float32)
