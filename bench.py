@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the int4 routed-expert MoE layer on one MI355X.
 
-A step is one pass of the whole path -- route and union
-(coli_moe_route_union: one launch for up to 4 tokens), coli_moe_forward --
-over one batch of seeded synthetic tokens.
+A step is one pass of the whole path -- route, union and forward -- over one
+batch of seeded synthetic tokens: one coli_moe_route_forward call for a
+single token in the fp32 family (three launches: router GEMV, gate/up that
+routes the token itself, down with the combine), else coli_moe_route_union
+(one launch for up to 4 tokens) and coli_moe_forward.
 
 Workloads (--workload):
   decode         H6144 I2048 E256 top-8 + 1 shared, T=1, fp32 family
@@ -20,8 +22,9 @@ Workloads (--workload):
 The timed steps are captured once in a HIP graph and replayed between two
 synchronisations (wall clock).  The dominant kernel's duration comes from
 HIP events that each kernel's own dispatch records at its start and end
-(coli_moe_forward_profiled launches through hipExtLaunchKernel on the
-library's stream), over the same inputs.  Prints one JSON line.
+(coli_moe_route_forward_profiled / coli_moe_forward_profiled launch through
+hipExtLaunchKernel on the library's stream), over the same inputs.  Prints
+one JSON line.
 """
 from __future__ import annotations
 
@@ -174,6 +177,8 @@ def main():
         resid = torch.empty((T, H), dtype=torch.float32, device="cuda")
         xhat = torch.empty_like(resid)
 
+    one_call = coli.route_forward_fused(layers[0], T, mode)  # coli_moe_route_forward
+
     def step(s):
         if stacked:
             resid.copy_(xs[0])
@@ -182,7 +187,8 @@ def main():
                 coli.run_layer(lay, xhat, bufs, top_p=args.topp)
                 coli.add_inplace(resid, bufs.y, T * H)
         else:
-            coli.run_layer(layers[s % NL], xs[s], bufs, top_p=args.topp)
+            coli.run_layer(layers[s % NL], xs[s], bufs, top_p=args.topp,
+                           fused="step" if one_call else True)
 
     # ---- warmup ----------------------------------------------------------
     for s in range(W):
@@ -220,7 +226,7 @@ def main():
 
     # ---- dominant kernel: per-kernel events on the library's stream ------
     hip = Hip()
-    names = coli.forward_kernel_names(mode, T)
+    names = coli.route_forward_kernel_names() if one_call else coli.forward_kernel_names(mode, T)
     nk = len(names)
     dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
     prof_steps = min(K, 64)
@@ -238,10 +244,16 @@ def main():
             x_in = xs[W + s] if not stacked else xhat
             if stacked:
                 coli.rmsnorm(resid, xhat, T, H, 1e-6)
-            coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
-                             bufs.slots, bufs.n_union, bufs.workspace, top_p=args.topp)
-            coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
-                                  bufs.slots, bufs.n_union, mode, bufs.y, bufs.workspace, ev[i])
+            if one_call:
+                coli.route_forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
+                                            bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
+                                            bufs.workspace, ev[i], top_p=args.topp)
+            else:
+                coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
+                                 bufs.slots, bufs.n_union, bufs.workspace, top_p=args.topp)
+                coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
+                                      bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
+                                      bufs.workspace, ev[i])
             union_sizes.append(bufs.n_union[:1].clone())
             if stacked:
                 coli.add_inplace(resid, bufs.y, T * H)

@@ -106,9 +106,10 @@ typedef struct coli_moe_layer {
     const uint16_t *sh_s2;     /* [H][I/64]                                 */
 } coli_moe_layer;
 
-/* Bytes of device workspace needed by coli_moe_route, coli_moe_union and
- * coli_moe_forward for this shape and arithmetic family (one buffer of this
- * size serves all three calls on one stream; its contents are scratch).
+/* Bytes of device workspace needed by coli_moe_route, coli_moe_union,
+ * coli_moe_forward and coli_moe_route_forward for this shape and arithmetic
+ * family (one buffer of this size serves all these calls on one stream; its
+ * contents are scratch).
  * Returns 0 for an invalid shape or mode. */
 size_t coli_moe_workspace_bytes(int32_t H, int32_t I, int32_t E, int32_t k, int32_t T,
                                 int32_t act_mode);
@@ -223,6 +224,37 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
                               float *y, void *workspace, size_t workspace_bytes,
                               int32_t *acc_dump, void **events, int32_t n_events,
                               void *hip_stream);
+
+/* One step of the layer: coli_moe_route_union(L, x, T, top_p, topk_ids,
+ * topk_w, union_ids, offsets, slots, n_union, ...) followed by
+ * coli_moe_forward(L, x, T, topk_ids, topk_w, union_ids, offsets, slots,
+ * n_union, act_mode, y, ...) without acc_dump -- the same outputs, bit for
+ * bit (topk_ids, topk_w, the union and y).  For one token in the fp32 family
+ * with E <= 256 it takes three launches instead of four: the router GEMV
+ * writes the sigmoid scores, and every workgroup of the gate/up kernel
+ * selects the top k and forms the union itself before streaming its share
+ * of the experts (its workgroup 0 writes them out); the down kernel also
+ * forms y.  Otherwise it runs the two calls.  Argument checks of both calls
+ * (the layer's experts must be present); top_p > 0; workspace_bytes >=
+ * coli_moe_workspace_bytes.  T == 0 only writes the empty union. */
+int coli_moe_route_forward(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                           int32_t *topk_ids, float *topk_w, int32_t *union_ids, int32_t *offsets,
+                           int32_t *slots, int32_t *n_union, int32_t act_mode, float *y,
+                           void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* coli_moe_route_forward for the three-launch case only (T == 1, fp32
+ * family, E <= 256; else COLI_E_UNSUPPORTED, nothing enqueued), recording
+ * events[2i] / events[2i + 1] at the start / end of its i-th kernel through
+ * the kernel's own dispatch (n_events >= 6, hipEvent_t values created by the
+ * caller with timing); coli_moe_route_forward_kernel_name(i) names kernel i
+ * (i < 3; NULL otherwise).  For measurement only. */
+int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
+                                    float top_p, int32_t *topk_ids, float *topk_w,
+                                    int32_t *union_ids, int32_t *offsets, int32_t *slots,
+                                    int32_t *n_union, int32_t act_mode, float *y,
+                                    void *workspace, size_t workspace_bytes, void **events,
+                                    int32_t n_events, void *hip_stream);
+const char *coli_moe_route_forward_kernel_name(int32_t i);
 
 /* Number of kernels coli_moe_forward launches for act_mode and a batch of
  * T tokens without acc_dump (0 if the mode is unknown), and the name of the

@@ -22,6 +22,7 @@ COLI_OK, COLI_E_ARG, COLI_E_SHAPE, COLI_E_ALIGN, COLI_E_WORKSPACE, COLI_E_DEVICE
 # every symbol declared in include/coli_moe.h
 EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_route_topp", "coli_moe_route_union", "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
+           "coli_moe_route_forward", "coli_moe_route_forward_profiled", "coli_moe_route_forward_kernel_name",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
            "coli_rmsnorm", "coli_add_inplace")
@@ -72,6 +73,11 @@ def lib():
                                  ctypes.c_int),
             "coli_moe_forward_profiled": ([vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp,
                                            vp, i32, vp], ctypes.c_int),
+            "coli_moe_route_forward": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, i32,
+                                        vp, vp, sz, vp], ctypes.c_int),
+            "coli_moe_route_forward_profiled": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
+                                                 vp, i32, vp, vp, sz, vp, i32, vp], ctypes.c_int),
+            "coli_moe_route_forward_kernel_name": ([i32], ctypes.c_char_p),
             "coli_moe_forward_kernel_count": ([i32, i32], ctypes.c_int),
             "coli_moe_forward_kernel_name": ([i32, i32, i32], ctypes.c_char_p),
             "coli_moe_acc_dump_bytes": ([i32, i32, i32, i32, i32], sz),
@@ -189,6 +195,40 @@ def forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, ac
            "coli_moe_forward_profiled")
 
 
+def route_forward(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y, workspace,
+                  top_p=None, workspace_nbytes=None, stream=None):
+    """coli_moe_route_forward: route, union and forward in one call (three
+    launches for one token in the fp32 family with E <= 256)."""
+    nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    p = 1.0 if top_p is None else float(top_p)
+    _check(lib().coli_moe_route_forward(layer.ref, _ptr(x), T, p, _ptr(ids), _ptr(w),
+                                        _ptr(union_ids), _ptr(offsets), _ptr(slots), _ptr(n_union),
+                                        act_mode, _ptr(y), _ptr(workspace), nb, _stream(stream)),
+           "coli_moe_route_forward")
+
+
+def route_forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y,
+                           workspace, events, top_p=None, stream=None):
+    """coli_moe_route_forward (three-launch case) recording ``events``."""
+    nb = workspace.numel() * workspace.element_size()
+    p = 1.0 if top_p is None else float(top_p)
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib().coli_moe_route_forward_profiled(layer.ref, _ptr(x), T, p, _ptr(ids), _ptr(w),
+                                                 _ptr(union_ids), _ptr(offsets), _ptr(slots),
+                                                 _ptr(n_union), act_mode, _ptr(y), _ptr(workspace),
+                                                 nb, arr, len(events), _stream(stream)),
+           "coli_moe_route_forward_profiled")
+
+
+def route_forward_kernel_names():
+    return [lib().coli_moe_route_forward_kernel_name(i).decode() for i in range(3)]
+
+
+def route_forward_fused(layer, T, act_mode):
+    """Whether coli_moe_route_forward takes its three-launch form."""
+    return T == 1 and act_mode == ACT_F32 and layer.E <= 256
+
+
 def forward_kernel_names(act_mode, T=2):
     n = lib().coli_moe_forward_kernel_count(act_mode, T)
     return [lib().coli_moe_forward_kernel_name(act_mode, T, i).decode() for i in range(n)]
@@ -269,8 +309,16 @@ class Buffers:
 def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None, top_p=None, fused=True):
     """route -> union -> forward for x [T][H] (device fp32); top_p selects
     the adaptive top-p router; fused routes and unions in one call
-    (coli_moe_route_union), else in two."""
+    (coli_moe_route_union), else in two; fused="step" runs the whole step in
+    one call (coli_moe_route_forward; not with an acc_dump buffer)."""
     T = bufs.T
+    if fused == "step":
+        if bufs.dump is not None:
+            raise ValueError("coli_moe_route_forward takes no acc_dump buffer")
+        route_forward(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,
+                      bufs.n_union, bufs.act_mode, bufs.y, bufs.workspace, top_p=top_p,
+                      stream=stream)
+        return bufs.y
     if fused:
         route_union(layer, x, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets, bufs.slots,
                     bufs.n_union, bufs.workspace, top_p=top_p, stream=stream)

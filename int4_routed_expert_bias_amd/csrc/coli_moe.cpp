@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "common.h"
@@ -273,6 +274,91 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
     mk.n = n_events;
     return forward_impl(L, x, T, topk_ids, topk_w, union_ids, offsets, slots, n_union, act_mode,
                         y, workspace, workspace_bytes, acc_dump, hip_stream, &mk);
+}
+
+// One token, fp32 family, E <= 256: router GEMV, gate/up that routes the
+// token itself, down with the combine (three launches).
+static bool route_forward_fused(const coli_moe_layer *L, int32_t T, int32_t act_mode)
+{
+    return T == 1 && act_mode == COLI_ACT_F32 && L->E <= 256;
+}
+
+static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                              int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                              int32_t *offsets, int32_t *slots, int32_t *n_union, int32_t act_mode,
+                              float *y, void *workspace, size_t workspace_bytes, void *hip_stream,
+                              Marks *mk)
+{
+    if (int st = check_layer(L, true)) return st;
+    if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
+    if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return COLI_E_UNSUPPORTED;
+    if (!(top_p > 0.0f)) return COLI_E_ARG;  // also rejects NaN
+    const bool fused = route_forward_fused(L, T, act_mode);
+    if (mk) {
+        if (!fused) return COLI_E_UNSUPPORTED;
+        if (!mk->ev || mk->n < 6) return COLI_E_ARG;
+        for (int i = 0; i < 6; ++i)
+            if (!mk->ev[i]) return COLI_E_ARG;
+    }
+    if (!n_union || !union_ids || !offsets) return COLI_E_ARG;
+    if (!aligned16(union_ids) || !aligned16(offsets) || !aligned16(n_union)) return COLI_E_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (T == 0) {
+        if (int s = device_check()) return s;
+        return status_of(launch_union(nullptr, 0, L->k, L->E, union_ids, offsets, slots, n_union, st));
+    }
+    if (!x || !topk_ids || !topk_w || !slots || !y || !workspace) return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(slots) ||
+        !aligned16(y) || !aligned16(workspace))
+        return COLI_E_ALIGN;
+    const Workspace lay = workspace_layout(L->H, L->I, L->E, L->k, T, act_mode, L->n_shared);
+    if (workspace_bytes < (fused ? lay.fused_end : std::max(lay.route_end, lay.forward_end)))
+        return COLI_E_WORKSPACE;
+    if (int s = device_check()) return s;
+    const LayerDev d = to_dev(L);
+    ForwardIO io{};
+    io.x = x; io.T = T; io.ids = topk_ids; io.w = topk_w;
+    io.union_ids = union_ids; io.offsets = offsets; io.slots = slots; io.n_union = n_union;
+    io.y = y; io.ws = static_cast<uint8_t *>(workspace); io.lay = lay;
+    if (fused) return status_of(launch_route_forward_t1(d, io, top_p, st, mk));
+    // (the forward buffers alias the route scratch: stream-ordered)
+    RouteIO rio{x, T, topk_ids, topk_w, reinterpret_cast<float *>(io.ws + lay.logits), top_p};
+    UnionIO un{union_ids, offsets, slots, n_union};
+    if (int s = status_of(launch_route(d, rio, st, &un))) return s;
+    io.dump = dump_layout(L->H, L->I, L->k, T, L->n_shared);
+    return status_of(act_mode == COLI_ACT_I8 ? launch_forward_i8(d, io, st, nullptr)
+                                             : launch_forward_f32(d, io, st, nullptr));
+}
+
+int coli_moe_route_forward(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                           int32_t *topk_ids, float *topk_w, int32_t *union_ids, int32_t *offsets,
+                           int32_t *slots, int32_t *n_union, int32_t act_mode, float *y,
+                           void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    return route_forward_impl(L, x, T, top_p, topk_ids, topk_w, union_ids, offsets, slots,
+                              n_union, act_mode, y, workspace, workspace_bytes, hip_stream,
+                              nullptr);
+}
+
+int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
+                                    float top_p, int32_t *topk_ids, float *topk_w,
+                                    int32_t *union_ids, int32_t *offsets, int32_t *slots,
+                                    int32_t *n_union, int32_t act_mode, float *y,
+                                    void *workspace, size_t workspace_bytes, void **events,
+                                    int32_t n_events, void *hip_stream)
+{
+    if (!events || n_events < 1) return COLI_E_ARG;
+    Marks mk;
+    mk.ev = events;
+    mk.n = n_events;
+    return route_forward_impl(L, x, T, top_p, topk_ids, topk_w, union_ids, offsets, slots,
+                              n_union, act_mode, y, workspace, workspace_bytes, hip_stream, &mk);
+}
+
+const char *coli_moe_route_forward_kernel_name(int32_t i)
+{
+    static const char *names[] = {"logits_gemv_kernel", "gateup_t1_kernel", "down_t1c_kernel"};
+    return i >= 0 && i < 3 ? names[i] : nullptr;
 }
 
 int coli_moe_forward_kernel_count(int32_t act_mode, int32_t T)

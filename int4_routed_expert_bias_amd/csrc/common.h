@@ -71,6 +71,10 @@ struct Workspace {
     size_t qh, sh;   // [R][I] i8 (permuted), [R][I/64] f32
     size_t tiles;    // [max_tiles] int2 (entry, first row) + [1] count
     size_t forward_end;
+    // route + forward in one call (one token): the scores stay readable
+    // while gate/up writes h, so they sit past the forward buffers
+    size_t scores;   // [E] f32
+    size_t fused_end;
     size_t total;
     int64_t R;       // rows: T*k + n_shared*T
     int64_t cap;     // min(E, T*k)
@@ -139,7 +143,9 @@ inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, in
         }
     }
     w.forward_end = p;
-    w.total = w.route_end > w.forward_end ? w.route_end : w.forward_end;
+    w.scores = p; p = align256(p + (size_t)E * 4);
+    w.fused_end = p;
+    w.total = w.route_end > w.fused_end ? w.route_end : w.fused_end;
     if (w.total == 0) w.total = 256;
     return w;
 }
@@ -222,6 +228,10 @@ struct UnionIO {
 hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st,
                         const UnionIO *un = nullptr);
 
+// Sigmoid scores of one token (the router GEMV alone) into scores [E].
+hipError_t launch_scores_t1(const LayerDev &L, const float *x, float *scores, hipStream_t st,
+                            Marks *mk = nullptr);
+
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                         int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st);
 
@@ -248,6 +258,11 @@ inline int forward_kernel_count(int act_mode, int T)
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
+// Route and forward of one token in the fp32 family (E <= 256): router GEMV
+// (scores into io.ws + io.lay.scores), gate/up that selects and unions the
+// token itself (writing io.ids / io.w / the union), down with the combine.
+hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, float top_p,
+                                   hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
                                    const float *sx, float *h, float *o, hipStream_t st, Marks *mk);

@@ -34,6 +34,7 @@
 // variant runs it: a token alone and inside a batch give identical bits.
 #include "common.h"
 #include "stream.h"
+#include "route_tokens.h"
 
 #include <algorithm>
 #include <atomic>
@@ -538,8 +539,24 @@ __device__ __forceinline__ void t1_entry(const GemvArgs &a, int ue, int U, const
 // their up rows I + i.  Each lane reads the x chunks it needs once (staged
 // through LDS) and keeps them in registers (XREG) or re-reads them from LDS
 // every stage.  h is written chunk-transposed.
-template <int P, int NP, int M, int DEPTH, bool XREG>
-__global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
+// ROUTE: the token routes itself.  Every workgroup first runs the router's
+// top-k selection and batch union (route_tokens, the code of the top-k
+// kernel) on the token's sigmoid scores, into LDS, and streams its share of
+// the selected experts from there; workgroup 0 also writes the selection and
+// the union to global memory (for the down kernel and the caller).  The
+// selection costs each workgroup a few microseconds before its first weight
+// load, against a whole launch of the top-k kernel.  E <= 256.
+struct RouteT1 {
+    const float *scores, *bias;  // [E] sigmoid scores of the token, [E] selection bias
+    int E, k, cap;
+    float top_p;
+    int32_t *ids;                // [k]
+    float *w;                    // [k]
+    int32_t *union_ids, *offsets, *slots, *n_union;
+};
+
+template <int P, int NP, int M, int DEPTH, bool XREG, bool ROUTE>
+__global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteT1 r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
     constexpr int V = next_pow2(2 * NP * M), N = reduced_count(V);
@@ -550,14 +567,58 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
-    const int U = a.n_union[0];
+    int U;
+    if constexpr (ROUTE) {
+        __shared__ int32_t l_ids[COLI_MAX_K_DEV], l_u[COLI_MAX_K_DEV], l_sl[COLI_MAX_K_DEV];
+        __shared__ int32_t l_off[COLI_MAX_K_DEV + 1], l_n[1];
+        __shared__ float l_w[COLI_MAX_K_DEV];
+        const UnionOut uo{l_u, l_off, l_sl, l_n, r.cap};
+        route_tokens<4, true>(r.scores, nullptr, 0, r.bias, 1, r.E, r.k, r.top_p, l_ids, l_w, uo,
+                              0);
+        __syncthreads();
+        const int i = threadIdx.x, nu = l_n[0];
+        if (blockIdx.x == 0) {
+            // the global contents the top-k kernel leaves (slots past the
+            // kept ones untouched)
+            const int kept = l_off[nu];
+            if (i < r.k) {
+                r.ids[i] = l_ids[i];
+                r.w[i] = l_w[i];
+            }
+            if (i < kept) r.slots[i] = l_sl[i];
+            if (i < r.cap) r.union_ids[i] = l_u[i];
+            if (i <= r.cap) r.offsets[i] = l_off[i];
+            if (i == 0) r.n_union[0] = nu;
+        }
+        a.union_ids = l_u;
+        a.offsets = l_off;
+        a.slots = l_sl;
+        a.n_union = l_n;
+        U = __builtin_amdgcn_readfirstlane(nu);
+    } else {
+        U = a.n_union[0];
+    }
     const int upe = a.I / NP;
     const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, upe);
     const int nsteps = sp.nsteps;
     const uint8_t *wb;
     const uint16_t *sb;
     int orow;
-    t1_entry(a, sp.ue, U, wb, sb, orow);
+    if constexpr (ROUTE) {
+        // (the union is in LDS, read per lane: its values made uniform)
+        if (sp.ue < U) {
+            const int e = __builtin_amdgcn_readfirstlane(a.union_ids[sp.ue]);
+            wb = a.w + (size_t)e * a.N * (a.K / 2);
+            sb = a.s + (size_t)e * a.N * (a.K / 64);
+            orow = __builtin_amdgcn_readfirstlane(a.slots[a.offsets[sp.ue]]);
+        } else {
+            wb = a.sh_w;
+            sb = a.sh_s;
+            orow = a.T * a.k;
+        }
+    } else {
+        t1_entry(a, sp.ue, U, wb, sb, orow);
+    }
     const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
     uint32_t vw[P], vs[P];
     lane_offsets<P>(lane, C, vw, vs);
@@ -1168,7 +1229,7 @@ static int resident_blocks(const void *kern, int P, int NW)
 // workgroup per CU (its register ring plus the x chunks allow two waves per
 // SIMD, and more waves lose DRAM locality), down runs four per CU.
 static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs a, float *h,
-                                float *o, hipStream_t st, Marks *mk)
+                                float *o, hipStream_t st, Marks *mk, const RouteT1 *rt = nullptr)
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
@@ -1183,7 +1244,11 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         const dim3 grid(std::min(cus, (units + 3) / 4)), block(256);
         const size_t lds = (size_t)(L.H + L.H / 32) * 4;
 #define COLI_GU1(P_) \
-        if (P == P_) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true>), grid, block, lds, st, a);
+        if (P == P_) { \
+            if (rt) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, true>), grid, block, lds, st, a, *rt); \
+            else launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, false>), grid, block, lds, st, a, \
+                        RouteT1{}); \
+        }
         COLI_GU1(1) COLI_GU1(2) COLI_GU1(3) COLI_GU1(4)
 #undef COLI_GU1
         hipError_t err = hipGetLastError();
@@ -1223,6 +1288,27 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
 #undef COLI_DN1
         return hipGetLastError();
     }
+}
+
+hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, float top_p,
+                                   hipStream_t st, Marks *mk)
+{
+    float *scores = reinterpret_cast<float *>(io.ws + io.lay.scores);
+    hipError_t err = launch_scores_t1(L, io.x, scores, st, mk);
+    if (err != hipSuccess) return err;
+    float *h = reinterpret_cast<float *>(io.ws + io.lay.h);
+    float *o = reinterpret_cast<float *>(io.ws + io.lay.o);
+    GemvArgs a{};
+    a.union_ids = io.union_ids; a.offsets = io.offsets; a.slots = io.slots; a.n_union = io.n_union;
+    a.T = 1; a.k = L.k; a.cap = (int)io.lay.cap; a.n_shared = L.n_shared;
+    a.I = L.I;
+    RouteT1 rt{};
+    rt.scores = scores; rt.bias = L.router_bias;
+    rt.E = L.E; rt.k = L.k; rt.cap = (int)io.lay.cap; rt.top_p = top_p;
+    rt.ids = const_cast<int32_t *>(io.ids); rt.w = const_cast<float *>(io.w);
+    rt.union_ids = const_cast<int32_t *>(io.union_ids); rt.offsets = const_cast<int32_t *>(io.offsets);
+    rt.slots = const_cast<int32_t *>(io.slots); rt.n_union = const_cast<int32_t *>(io.n_union);
+    return launch_f32_t1(L, io, a, h, o, st, mk, &rt);
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk)

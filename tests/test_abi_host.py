@@ -208,6 +208,41 @@ def test_mla_argument_errors(L):
     assert coli.mla_workspace_bytes(1, 64, 0) == 0
 
 
+def test_route_forward_argument_errors(L):
+    def rf(lay, T=1, p=1.0, mode=0, x=FAKE, u=FAKE, sl=FAKE, y=FAKE, nb=1 << 30):
+        return L.coli_moe_route_forward(ctypes.byref(lay) if lay is not None else None, x, T,
+                                        ctypes.c_float(p), FAKE, FAKE, u, FAKE, sl, FAKE, mode, y,
+                                        FAKE, nb, None)
+    assert rf(None) == coli.COLI_E_ARG
+    assert rf(layer(H=100)) == coli.COLI_E_SHAPE
+    assert rf(layer(), T=-1) == coli.COLI_E_SHAPE
+    assert rf(layer(), mode=5) == coli.COLI_E_UNSUPPORTED
+    assert rf(layer(), p=0.0) == coli.COLI_E_ARG
+    assert rf(layer(), u=None) == coli.COLI_E_ARG
+    assert rf(layer(), sl=None) == coli.COLI_E_ARG
+    assert rf(layer(), y=None) == coli.COLI_E_ARG
+    assert rf(layer(), x=MIS) == coli.COLI_E_ALIGN
+    assert rf(layer(), nb=16) == coli.COLI_E_WORKSPACE
+    assert rf(layer(), T=3, nb=16) == coli.COLI_E_WORKSPACE
+    noexp = layer()
+    noexp.w13 = None
+    assert rf(noexp) == coli.COLI_E_ARG
+
+    def rfp(T=1, mode=0, n=6, holes=False):
+        ev = (ctypes.c_void_p * max(n, 1))(*([FAKE] * max(n, 1)))
+        if holes:
+            ev[n - 1] = None
+        return L.coli_moe_route_forward_profiled(ctypes.byref(layer()), FAKE, T, ctypes.c_float(1.0),
+                                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode, FAKE,
+                                                 FAKE, 1 << 30, ev, n, None)
+    assert rfp(T=2) == coli.COLI_E_UNSUPPORTED      # only the three-launch case
+    assert rfp(mode=1) == coli.COLI_E_UNSUPPORTED
+    assert rfp(n=5) == coli.COLI_E_ARG
+    assert rfp(holes=True) == coli.COLI_E_ARG
+    assert [coli.lib().coli_moe_route_forward_kernel_name(i) for i in (-1, 3)] == [None, None]
+    assert coli.lib().coli_moe_route_forward_kernel_name(1) == b"gateup_t1_kernel"
+
+
 def test_route_union_argument_errors(L):
     def ru(lay, T=4, p=1.0, x=FAKE, u=FAKE, off=FAKE, sl=FAKE, nu=FAKE, nb=1 << 20):
         return L.coli_moe_route_union(ctypes.byref(lay) if lay is not None else None, x, T,

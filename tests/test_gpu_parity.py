@@ -235,6 +235,68 @@ def test_route_union_equals_route_then_union(T, top_p):
         assert np.array_equal(a, c)
 
 
+def _step_outputs(lay, x, T, mode, top_p, step):
+    import torch
+    b = coli.Buffers(lay.dev, T, mode)
+    for t in (b.ids, b.union_ids, b.offsets, b.slots, b.n_union):
+        t.fill_(-7)
+    b.w.fill_(-7.0)
+    b.y.fill_(-7.0)
+    coli.run_layer(lay.dev, x, b, top_p=top_p, fused="step" if step else True)
+    torch.cuda.synchronize()
+    n_kept = int(b.offsets[int(b.n_union[0].item())].item())
+    return [b.ids.cpu().numpy(), b.w.cpu().numpy().view(np.uint32), b.union_ids.cpu().numpy(),
+            b.offsets.cpu().numpy(), b.slots[:n_kept].cpu().numpy(), b.n_union[:1].cpu().numpy(),
+            b.y[:T].cpu().numpy().view(np.uint32)]
+
+
+@pytest.mark.parametrize("top_p", [None, 0.7])
+@pytest.mark.parametrize("case", ["decode", "wide_k", "wide_k_no_shared", "small_E", "E_70"])
+def test_route_forward_equals_route_union_then_forward(case, top_p):
+    """coli_moe_route_forward (at T = 1 in the fp32 family: the gate/up kernel
+    routes the token itself) gives the bits of coli_moe_route_union followed
+    by coli_moe_forward: selection, weights, union and y; other batches and
+    the int8 family take the two calls."""
+    import torch
+    lay = {"decode": lambda: workload_layer("decode"),
+           "wide_k": lambda: make_layer(320, 192, 40, 16, wid=70),
+           "wide_k_no_shared": lambda: make_layer(320, 192, 40, 16, wid=71, n_shared=0),
+           "small_E": lambda: make_layer(256, 128, 12, 3, wid=72),
+           "E_70": lambda: make_layer(384, 128, 70, 6, wid=73)}[case]()
+    for T, mode in ((1, coli.ACT_F32), (1, coli.ACT_I8), (3, coli.ACT_F32)):
+        for rep in range(2):
+            x = torch.from_numpy(synth.activations(lay.H, T, wid=74 + rep + 10 * T)).cuda()
+            a = _step_outputs(lay, x, T, mode, top_p, step=True)
+            c = _step_outputs(lay, x, T, mode, top_p, step=False)
+            for name, u, v in zip(("ids", "w", "union_ids", "offsets", "slots", "n_union", "y"), a, c):
+                assert np.array_equal(u, v), (case, T, mode, name)
+
+
+def test_route_forward_graph_replay():
+    """The three-launch step captured in a HIP graph: every replay (with the
+    input changed between replays) matches the eager call bit for bit."""
+    import torch
+    lay = workload_layer("decode")
+    b = coli.Buffers(lay.dev, 1, coli.ACT_F32)
+    xs = [torch.from_numpy(synth.activations(lay.H, 1, wid=80 + i)).cuda() for i in range(3)]
+    x = xs[0].clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            coli.run_layer(lay.dev, x, b, fused="step")
+    torch.cuda.synchronize()
+    for i in (1, 2, 0, 1):
+        x.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        got = (b.ids.cpu().numpy().copy(), b.y[:1].cpu().numpy().copy())
+        ref = _step_outputs(lay, xs[i], 1, coli.ACT_F32, None, step=False)
+        assert np.array_equal(got[0], ref[0])
+        assert np.array_equal(got[1].view(np.uint32), ref[6])
+
+
 def test_topp_one_is_plain_topk():
     import torch
     lay = workload_layer("tiny")
