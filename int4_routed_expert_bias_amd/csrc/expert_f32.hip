@@ -568,6 +568,18 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteT1 r)
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
     int U;
+    // ROUTE: x is loaded into registers before the selection (its latency
+    // overlaps the selection's) and staged to LDS after it
+    constexpr int XPRE = ROUTE ? COLI_MAX_H_DEV / 4 / 256 : 1;
+    uint4 xpre[XPRE];
+    if constexpr (ROUTE) {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.in, (uint32_t)K * 4);
+#pragma unroll
+        for (int j = 0; j < XPRE; ++j) {
+            const int i = (int)threadIdx.x + 256 * j;
+            xpre[j] = load16(rx, i < K / 4 ? (uint32_t)i * 16 : kOOB);
+        }
+    }
     if constexpr (ROUTE) {
         __shared__ int32_t l_ids[COLI_MAX_K_DEV], l_u[COLI_MAX_K_DEV], l_sl[COLI_MAX_K_DEV];
         __shared__ int32_t l_off[COLI_MAX_K_DEV + 1], l_n[1];
@@ -643,7 +655,18 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteT1 r)
     {
         const float4 *src = reinterpret_cast<const float4 *>(a.in);
         float4 *dst = reinterpret_cast<float4 *>(xs);
-        for (int i = threadIdx.x; i < K / 4; i += blockDim.x) dst[(i & 7) * C + (i >> 3)] = src[i];
+        if constexpr (ROUTE) {
+#pragma unroll
+            for (int jj = 0; jj < XPRE; ++jj) {
+                const int i = (int)threadIdx.x + 256 * jj;
+                if (i < K / 4)
+                    dst[(i & 7) * C + (i >> 3)] = make_float4(
+                        __uint_as_float(xpre[jj].x), __uint_as_float(xpre[jj].y),
+                        __uint_as_float(xpre[jj].z), __uint_as_float(xpre[jj].w));
+            }
+        } else {
+            for (int i = threadIdx.x; i < K / 4; i += blockDim.x) dst[(i & 7) * C + (i >> 3)] = src[i];
+        }
         __syncthreads();
         for (int c = threadIdx.x; c < C; c += blockDim.x) {
             float v[32];

@@ -189,9 +189,34 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
     if constexpr (UNION) {
         __syncthreads();
         if (wv == 0) {
-            const int n = T * k;
-            union_wave(lane, lane < n ? sid[lane] : -1, E, uo.cap, uo.union_ids, uo.offsets,
-                       uo.slots, uo.n_union);
+            if (T == 1) {
+                // one token: its kept experts are distinct, so the union is
+                // the kept slots ordered by expert (rank by counting): the
+                // lists union_wave forms, without its sorting network
+                const int id = lane < k ? sid[lane] : -1;
+                const bool valid = id >= 0 && id < E;
+                int pos = 0;
+                for (int i = 0; i < k; ++i) {
+                    const int o = sid[i];
+                    pos += (o >= 0 && o < E && o < id) ? 1 : 0;
+                }
+                const int kept = __popcll(__ballot(valid));
+                if (valid) {
+                    uo.union_ids[pos] = id;
+                    uo.offsets[pos] = pos;
+                    uo.slots[pos] = lane;
+                }
+                if (lane >= kept && lane < uo.cap) uo.union_ids[lane] = -1;
+                if (lane >= kept && lane <= uo.cap) uo.offsets[lane] = kept;
+                if (lane == 0) {
+                    uo.n_union[0] = kept;
+                    if (uo.cap == 64) uo.offsets[64] = kept;
+                }
+            } else {
+                const int n = T * k;
+                union_wave(lane, lane < n ? sid[lane] : -1, E, uo.cap, uo.union_ids, uo.offsets,
+                           uo.slots, uo.n_union);
+            }
         }
     }
 }
