@@ -831,7 +831,10 @@ __global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
 // skipped, then the shared expert added), so y is bitwise that of the
 // two-launch form.
 template <int P, int RD, int M, int DEPTH>
-__global__ __launch_bounds__(64 * kDownT1cWaves) void down_t1c_kernel(GemvArgs a, const int32_t *__restrict__ ids,
+// (one chunk per lane: registers for five waves per SIMD, two workgroups per
+// CU -- 16.4 us against 17.5 with four waves per SIMD; wider rows keep the
+// registers they need)
+__global__ __launch_bounds__(64 * kDownT1cWaves, P == 1 ? 5 : 1) void down_t1c_kernel(GemvArgs a, const int32_t *__restrict__ ids,
                                                         const float *__restrict__ w,
                                                         float *__restrict__ y)
 {
@@ -1285,8 +1288,9 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         a.out = o; a.out_ld = L.H;
         const int P = (L.I / 32 + 63) / 64;
         if (io.combine) {
-            // (reductions over M = 2 stages: 17.6 us against 18.1 for 4 and 19.6 for 8)
-            constexpr int RD = 4, M = 2, DEPTH = 2;
+            // (2 rows per stage and reductions over 2 stages: 16.4 us, against
+            // 17.5 for 4 rows and 19.9 for 2 rows over 4 stages)
+            constexpr int RD = 2, M = 2, DEPTH = 2;
             // fused with the combine: NW waves per workgroup cover the entries;
             // as many workgroups as are resident at once (one round), each
             // with at most kDownRowsMax rows
