@@ -235,6 +235,18 @@ hipError_t launch_scores_t1(const LayerDev &L, const float *x, float *scores, hi
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                         int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st);
 
+// A single token that routes itself inside its gate/up kernel (see
+// launch_route_forward_t1): the token's sigmoid scores and the selection
+// outputs the gate/up kernel's workgroup 0 writes.
+struct RouteT1 {
+    const float *scores, *bias;  // [E] sigmoid scores of the token, [E] selection bias
+    int E, k, cap;
+    float top_p;
+    int32_t *ids;                // [k]
+    float *w;                    // [k]
+    int32_t *union_ids, *offsets, *slots, *n_union;
+};
+
 struct ForwardIO {
     const float *x; int32_t T;
     const int32_t *ids; const float *w;
@@ -245,6 +257,9 @@ struct ForwardIO {
     // false: the expert outputs stay in the workspace (o) and y is not
     // written; the placed forward combines once after its last pass
     bool combine = true;
+    // set: one token whose gate/up kernel selects and unions it (the union
+    // lists above are then written by that kernel)
+    const RouteT1 *route = nullptr;
 };
 
 // Kernels one forward call launches (without acc_dump): fp32 family gate/up,
@@ -258,11 +273,11 @@ inline int forward_kernel_count(int act_mode, int T)
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
-// Route and forward of one token in the fp32 family (E <= 256): router GEMV
-// (scores into io.ws + io.lay.scores), gate/up that selects and unions the
-// token itself (writing io.ids / io.w / the union), down with the combine.
-hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, float top_p,
-                                   hipStream_t st, Marks *mk);
+// Route and forward of one token (E <= 256): router GEMV (scores into
+// io.ws + io.lay.scores), then the family's forward whose gate/up kernel
+// selects and unions the token itself (writing io.ids / io.w / the union).
+hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, int act_mode,
+                                   float top_p, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
                                    const float *sx, float *h, float *o, hipStream_t st, Marks *mk);

@@ -546,15 +546,6 @@ __device__ __forceinline__ void t1_entry(const GemvArgs &a, int ue, int U, const
 // the union to global memory (for the down kernel and the caller).  The
 // selection costs each workgroup a few microseconds before its first weight
 // load, against a whole launch of the top-k kernel.  E <= 256.
-struct RouteT1 {
-    const float *scores, *bias;  // [E] sigmoid scores of the token, [E] selection bias
-    int E, k, cap;
-    float top_p;
-    int32_t *ids;                // [k]
-    float *w;                    // [k]
-    int32_t *union_ids, *offsets, *slots, *n_union;
-};
-
 template <int P, int NP, int M, int DEPTH, bool XREG, bool ROUTE>
 __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteT1 r)
 {
@@ -581,31 +572,13 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteT1 r)
         }
     }
     if constexpr (ROUTE) {
-        __shared__ int32_t l_ids[COLI_MAX_K_DEV], l_u[COLI_MAX_K_DEV], l_sl[COLI_MAX_K_DEV];
-        __shared__ int32_t l_off[COLI_MAX_K_DEV + 1], l_n[1];
-        __shared__ float l_w[COLI_MAX_K_DEV];
-        const UnionOut uo{l_u, l_off, l_sl, l_n, r.cap};
-        route_tokens<4, true>(r.scores, nullptr, 0, r.bias, 1, r.E, r.k, r.top_p, l_ids, l_w, uo,
-                              0);
-        __syncthreads();
-        const int i = threadIdx.x, nu = l_n[0];
-        if (blockIdx.x == 0) {
-            // the global contents the top-k kernel leaves (slots past the
-            // kept ones untouched)
-            const int kept = l_off[nu];
-            if (i < r.k) {
-                r.ids[i] = l_ids[i];
-                r.w[i] = l_w[i];
-            }
-            if (i < kept) r.slots[i] = l_sl[i];
-            if (i < r.cap) r.union_ids[i] = l_u[i];
-            if (i <= r.cap) r.offsets[i] = l_off[i];
-            if (i == 0) r.n_union[0] = nu;
-        }
-        a.union_ids = l_u;
-        a.offsets = l_off;
-        a.slots = l_sl;
-        a.n_union = l_n;
+        __shared__ RouteLds rl;
+        route_self(r, rl);
+        const int nu = rl.n[0];
+        a.union_ids = rl.u;
+        a.offsets = rl.off;
+        a.slots = rl.sl;
+        a.n_union = rl.n;
         U = __builtin_amdgcn_readfirstlane(nu);
     } else {
         U = a.n_union[0];
@@ -1317,24 +1290,29 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
     }
 }
 
-hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, float top_p,
+hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, int act_mode, float top_p,
                                    hipStream_t st, Marks *mk)
 {
     float *scores = reinterpret_cast<float *>(io.ws + io.lay.scores);
     hipError_t err = launch_scores_t1(L, io.x, scores, st, mk);
     if (err != hipSuccess) return err;
-    float *h = reinterpret_cast<float *>(io.ws + io.lay.h);
-    float *o = reinterpret_cast<float *>(io.ws + io.lay.o);
-    GemvArgs a{};
-    a.union_ids = io.union_ids; a.offsets = io.offsets; a.slots = io.slots; a.n_union = io.n_union;
-    a.T = 1; a.k = L.k; a.cap = (int)io.lay.cap; a.n_shared = L.n_shared;
-    a.I = L.I;
     RouteT1 rt{};
     rt.scores = scores; rt.bias = L.router_bias;
     rt.E = L.E; rt.k = L.k; rt.cap = (int)io.lay.cap; rt.top_p = top_p;
     rt.ids = const_cast<int32_t *>(io.ids); rt.w = const_cast<float *>(io.w);
     rt.union_ids = const_cast<int32_t *>(io.union_ids); rt.offsets = const_cast<int32_t *>(io.offsets);
     rt.slots = const_cast<int32_t *>(io.slots); rt.n_union = const_cast<int32_t *>(io.n_union);
+    if (act_mode != 0) {
+        ForwardIO ri = io;
+        ri.route = &rt;
+        return launch_forward_i8(L, ri, st, mk);
+    }
+    float *h = reinterpret_cast<float *>(io.ws + io.lay.h);
+    float *o = reinterpret_cast<float *>(io.ws + io.lay.o);
+    GemvArgs a{};
+    a.union_ids = io.union_ids; a.offsets = io.offsets; a.slots = io.slots; a.n_union = io.n_union;
+    a.T = 1; a.k = L.k; a.cap = (int)io.lay.cap; a.n_shared = L.n_shared;
+    a.I = L.I;
     return launch_f32_t1(L, io, a, h, o, st, mk, &rt);
 }
 

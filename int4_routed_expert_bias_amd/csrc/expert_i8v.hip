@@ -22,6 +22,7 @@
 // weight, so these kernels are bound by the weight stream alone.
 #include "common.h"
 #include "stream.h"
+#include "route_tokens.h"
 
 namespace coli {
 
@@ -124,22 +125,73 @@ __device__ __forceinline__ float group_chain(const float *t, const float *ws, in
 // Gate/up + SwiGLU.  Unit = gate row i and up row I + i of one entry; the
 // waves of an entry take its units round-robin (t1_split).  Writes h rows
 // (natural order) for every token of the entry.
-template <int P, int M, int DEPTH, int NTOK>
-__global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a)
+// ROUTE (one token): the workgroup first selects the token's experts and
+// forms the union itself from its sigmoid scores (route_self, as the fp32
+// single-token gate/up kernel), then reads the union from LDS.
+template <int P, int M, int DEPTH, int NTOK, bool ROUTE>
+__global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteT1 r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the batch");
+    static_assert(!ROUTE || NTOK == 1, "a routing gate/up kernel serves one token");
     extern __shared__ float lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, G = K / 64;
-    const int U = a.n_union[0];
+    // this lane's activation codes and scales for every token of the entry
+    // (ROUTE: the one token's, loaded before the selection so that their
+    // latency overlaps it)
+    uint32_t xq[NTOK][P][8];
+    float xs[NTOK][P];
+    auto load_x = [&](int j, int tok) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int c = min(lane + 64 * p, C - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.qx + (size_t)tok * K + 32 * c);
+            const uint4 lo = src[0], hi = src[1];
+            xq[j][p][0] = lo.x; xq[j][p][1] = lo.y; xq[j][p][2] = lo.z; xq[j][p][3] = lo.w;
+            xq[j][p][4] = hi.x; xq[j][p][5] = hi.y; xq[j][p][6] = hi.z; xq[j][p][7] = hi.w;
+            xs[j][p] = a.sx[(size_t)tok * G + (c >> 1)];
+        }
+    };
+    if constexpr (ROUTE) load_x(0, 0);
+    int U;
+    if constexpr (ROUTE) {
+        __shared__ RouteLds rl;
+        route_self(r, rl);
+        a.union_ids = rl.u;
+        a.offsets = rl.off;
+        a.slots = rl.sl;
+        a.n_union = rl.n;
+        U = __builtin_amdgcn_readfirstlane(rl.n[0]);
+    } else {
+        U = a.n_union[0];
+    }
     const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, a.I);
     const int nsteps = sp.nsteps;
     if (nsteps == 0) return;
     const uint8_t *wb;
     const uint16_t *sb;
     const int32_t *list;
-    const int cnt = min(i8v_entry(a, sp.ue, U, wb, sb, list), NTOK);
+    int cnt;
+    if constexpr (ROUTE) {
+        // (the union is in LDS, read per lane: its values made uniform)
+        if (sp.ue < U) {
+            const int e = __builtin_amdgcn_readfirstlane(a.union_ids[sp.ue]);
+            wb = a.w + (size_t)e * a.N * (a.K / 2);
+            sb = a.s + (size_t)e * a.N * (a.K / 64);
+            const int o0 = __builtin_amdgcn_readfirstlane(a.offsets[sp.ue]);
+            list = a.slots + o0;
+            cnt = __builtin_amdgcn_readfirstlane(a.offsets[sp.ue + 1]) - o0;
+        } else {
+            wb = a.sh_w;
+            sb = a.sh_s;
+            list = nullptr;
+            cnt = a.T;
+        }
+        cnt = min(cnt, NTOK);
+    } else {
+        cnt = min(i8v_entry(a, sp.ue, U, wb, sb, list), NTOK);
+    }
     if (cnt <= 0) return;
     const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
     uint32_t vw[P], vs[P];
@@ -155,24 +207,13 @@ __global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a)
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) issue(d, d);
 
-    // this lane's activation codes and scales for every token of the entry
-    uint32_t xq[NTOK][P][8];
-    float xs[NTOK][P];
     int orow[NTOK];
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
         int tok = 0, row = 0;
         if (j < cnt) i8v_token(a, list, j, tok, row);
         orow[j] = row;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int c = min(lane + 64 * p, C - 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.qx + (size_t)tok * K + 32 * c);
-            const uint4 lo = src[0], hi = src[1];
-            xq[j][p][0] = lo.x; xq[j][p][1] = lo.y; xq[j][p][2] = lo.z; xq[j][p][3] = lo.w;
-            xq[j][p][4] = hi.x; xq[j][p][5] = hi.y; xq[j][p][6] = hi.z; xq[j][p][7] = hi.w;
-            xs[j][p] = a.sx[(size_t)tok * G + (c >> 1)];
-        }
+        if constexpr (!ROUTE) load_x(j, tok);
     }
     using Lds = TermLds<M, NTOK, 2>;
     Lds tl(lds + (size_t)wave * Lds::rows() * (G + 1), G);
@@ -369,7 +410,13 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
         const size_t lds = (size_t)4 * Lds::rows() * (L.H / 64 + 1) * 4;
         const dim3 grid(std::max((NTOK == 1 ? 2 : 1) * cus, (entries + 3) / 4)), block(256);
 #define COLI_GUV(P_) \
-        if (P == P_) launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK>), grid, block, lds, st, a);
+        if (P == P_) { \
+            if (NTOK == 1 && io.route) \
+                launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, NTOK == 1>), grid, block, lds, st, a, \
+                       *io.route); \
+            else launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, false>), grid, block, lds, st, a, \
+                        RouteT1{}); \
+        }
         COLI_GUV(1) COLI_GUV(2) COLI_GUV(3) COLI_GUV(4)
 #undef COLI_GUV
         hipError_t err = hipGetLastError();

@@ -221,4 +221,32 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
     }
 }
 
+// The selection lists of one token in LDS (cap <= COLI_MAX_K_DEV).
+struct RouteLds {
+    int32_t ids[COLI_MAX_K_DEV], u[COLI_MAX_K_DEV], sl[COLI_MAX_K_DEV];
+    int32_t off[COLI_MAX_K_DEV + 1], n[1];
+    float w[COLI_MAX_K_DEV];
+};
+
+// One token selects its top k and forms its union into l (every thread of
+// the 256-thread workgroup calls this); workgroup 0 also writes the global
+// contents the top-k kernel leaves (slots past the kept ones untouched).
+__device__ __forceinline__ void route_self(const RouteT1 &r, RouteLds &l)
+{
+    const UnionOut uo{l.u, l.off, l.sl, l.n, r.cap};
+    route_tokens<4, true>(r.scores, nullptr, 0, r.bias, 1, r.E, r.k, r.top_p, l.ids, l.w, uo, 0);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        const int i = threadIdx.x, nu = l.n[0], kept = l.off[nu];
+        if (i < r.k) {
+            r.ids[i] = l.ids[i];
+            r.w[i] = l.w[i];
+        }
+        if (i < kept) r.slots[i] = l.sl[i];
+        if (i < r.cap) r.union_ids[i] = l.u[i];
+        if (i <= r.cap) r.offsets[i] = l.off[i];
+        if (i == 0) r.n_union[0] = nu;
+    }
+}
+
 }  // namespace coli

@@ -235,12 +235,16 @@ def test_route_forward_argument_errors(L):
         return L.coli_moe_route_forward_profiled(ctypes.byref(layer()), FAKE, T, ctypes.c_float(1.0),
                                                  FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode, FAKE,
                                                  FAKE, 1 << 30, ev, n, None)
-    assert rfp(T=2) == coli.COLI_E_UNSUPPORTED      # only the three-launch case
-    assert rfp(mode=1) == coli.COLI_E_UNSUPPORTED
+    assert rfp(T=2) == coli.COLI_E_UNSUPPORTED      # only the one-token case
     assert rfp(n=5) == coli.COLI_E_ARG
     assert rfp(holes=True) == coli.COLI_E_ARG
-    assert [coli.lib().coli_moe_route_forward_kernel_name(i) for i in (-1, 3)] == [None, None]
-    assert coli.lib().coli_moe_route_forward_kernel_name(1) == b"gateup_t1_kernel"
+    assert rfp(mode=1, n=9) == coli.COLI_E_ARG       # five int8 kernels: 10 events
+    assert rfp(mode=1, n=10, holes=True) == coli.COLI_E_ARG
+    lib_ = coli.lib()
+    assert [lib_.coli_moe_route_forward_kernel_count(m) for m in (0, 1, 2)] == [3, 5, 0]
+    assert [lib_.coli_moe_route_forward_kernel_name(0, i) for i in (-1, 3)] == [None, None]
+    assert lib_.coli_moe_route_forward_kernel_name(0, 1) == b"gateup_t1_kernel"
+    assert lib_.coli_moe_route_forward_kernel_name(1, 2) == b"gateup_i8v_kernel"
 
 
 def test_route_union_argument_errors(L):

@@ -253,10 +253,10 @@ def _step_outputs(lay, x, T, mode, top_p, step):
 @pytest.mark.parametrize("top_p", [None, 0.7])
 @pytest.mark.parametrize("case", ["decode", "wide_k", "wide_k_no_shared", "small_E", "E_70"])
 def test_route_forward_equals_route_union_then_forward(case, top_p):
-    """coli_moe_route_forward (at T = 1 in the fp32 family: the gate/up kernel
+    """coli_moe_route_forward (at T = 1 the gate/up kernel of either family
     routes the token itself) gives the bits of coli_moe_route_union followed
-    by coli_moe_forward: selection, weights, union and y; other batches and
-    the int8 family take the two calls."""
+    by coli_moe_forward: selection, weights, union and y; larger batches take
+    the two calls."""
     import torch
     lay = {"decode": lambda: workload_layer("decode"),
            "wide_k": lambda: make_layer(320, 192, 40, 16, wid=70),
