@@ -67,20 +67,6 @@ __device__ __forceinline__ int vseg(int u, int n)
     return 16 * n + 4 * ((u + (n >> 1) + (n >> 3)) & 3);
 }
 
-__device__ __forceinline__ float row_max16(float x)
-{
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
-
-__device__ __forceinline__ float row_sum16(float x)
-{
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
 // LIST: the keys of a query are the rows of its key list, else its prefix.
 template <bool LIST>
 __global__ __launch_bounds__(512, 1) void mla_attn_kernel(MlaArgs a)
