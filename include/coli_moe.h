@@ -3,8 +3,9 @@
  * with int4 (group size 64) routed experts, on AMD Instinct MI355X (gfx950).
  *
  * The layer follows the per-token path the Colibri pages describe -- route,
- * union, then expert compute -- for experts that are already resident in
- * device memory (placement and streaming are outside this library):
+ * union, then expert compute -- for experts resident in device memory (the
+ * placement of experts from pinned host memory is in coli_place.h, the
+ * compressed-KV attention in coli_mla.h):
  *   [Start]  Colibri getting-started page (cti.vibequant.cc), section
  *            "토큰당 처리 경로 (The Per-Token Path)": Route picks the experts,
  *            Union de-duplicates experts shared by tokens of a batch, Place
