@@ -2,10 +2,10 @@
 """Throughput of the int4 routed-expert MoE layer on one MI355X.
 
 A step is one pass of the whole path -- route, union and forward -- over one
-batch of seeded synthetic tokens: one coli_moe_route_forward call for a
-single token (fp32 family: three launches -- router GEMV, gate/up that
-routes the token itself, down with the combine), else coli_moe_route_union
-(one launch for up to 4 tokens) and coli_moe_forward.
+batch of seeded synthetic tokens: one coli_moe_route_forward call for up to
+4 tokens (the gate/up kernel routes the tokens itself; one token in the fp32
+family: three launches -- router GEMV, gate/up, down with the combine), else
+coli_moe_route_union and coli_moe_forward.
 
 Workloads (--workload):
   decode         H6144 I2048 E256 top-8 + 1 shared, T=1, fp32 family
@@ -226,7 +226,7 @@ def main():
 
     # ---- dominant kernel: per-kernel events on the library's stream ------
     hip = Hip()
-    names = coli.route_forward_kernel_names(mode) if one_call else coli.forward_kernel_names(mode, T)
+    names = coli.route_forward_kernel_names(mode, T) if one_call else coli.forward_kernel_names(mode, T)
     nk = len(names)
     dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
     prof_steps = min(K, 64)

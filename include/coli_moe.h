@@ -230,12 +230,13 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
  * topk_w, union_ids, offsets, slots, n_union, ...) followed by
  * coli_moe_forward(L, x, T, topk_ids, topk_w, union_ids, offsets, slots,
  * n_union, act_mode, y, ...) without acc_dump -- the same outputs, bit for
- * bit (topk_ids, topk_w, the union and y).  For one token with E <= 256 the
- * top-k launch is saved: the router GEMV writes the sigmoid scores, and
- * every workgroup of the gate/up kernel selects the top k and forms the
- * union itself before streaming its share of the experts (its workgroup 0
- * writes them out) -- three launches in the fp32 family (the down kernel
- * also forms y), five in the int8 family.  Otherwise it runs the two calls.
+ * bit (topk_ids, topk_w, the union and y).  For T <= 4 tokens with E <= 256
+ * (the int8 family: T == 1) the top-k launch is saved: the router GEMV
+ * writes the sigmoid scores, and every workgroup of the gate/up kernel
+ * selects the top k and forms the union itself before streaming its share
+ * of the experts (its workgroup 0 writes them out) -- at T == 1 three
+ * launches in the fp32 family (the down kernel also forms y), five in the
+ * int8 family.  Otherwise it runs the two calls.
  * Argument checks of both calls (the layer's experts must be present);
  * top_p > 0; workspace_bytes >= coli_moe_workspace_bytes.  T == 0 only
  * writes the empty union. */
@@ -244,22 +245,22 @@ int coli_moe_route_forward(const coli_moe_layer *L, const float *x, int32_t T, f
                            int32_t *slots, int32_t *n_union, int32_t act_mode, float *y,
                            void *workspace, size_t workspace_bytes, void *hip_stream);
 
-/* coli_moe_route_forward for the one-token case only (T == 1, E <= 256;
- * else COLI_E_UNSUPPORTED, nothing enqueued), recording events[2i] /
+/* coli_moe_route_forward for the self-routing case only (see above; else
+ * COLI_E_UNSUPPORTED, nothing enqueued), recording events[2i] /
  * events[2i + 1] at the start / end of its i-th kernel through the kernel's
  * own dispatch (n_events >= 2 * coli_moe_route_forward_kernel_count(
- * act_mode), hipEvent_t values created by the caller with timing);
- * coli_moe_route_forward_kernel_name(act_mode, i) names kernel i as a
- * profiler trace shows it (template arguments omitted; NULL out of range).
- * For measurement only. */
+ * act_mode, T), hipEvent_t values created by the caller with timing);
+ * coli_moe_route_forward_kernel_name(act_mode, T, i) names kernel i as a
+ * profiler trace shows it (template arguments omitted; NULL out of range;
+ * count 0 when the case does not route itself).  For measurement only. */
 int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
                                     float top_p, int32_t *topk_ids, float *topk_w,
                                     int32_t *union_ids, int32_t *offsets, int32_t *slots,
                                     int32_t *n_union, int32_t act_mode, float *y,
                                     void *workspace, size_t workspace_bytes, void **events,
                                     int32_t n_events, void *hip_stream);
-int coli_moe_route_forward_kernel_count(int32_t act_mode);
-const char *coli_moe_route_forward_kernel_name(int32_t act_mode, int32_t i);
+int coli_moe_route_forward_kernel_count(int32_t act_mode, int32_t T);
+const char *coli_moe_route_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
 
 /* Number of kernels coli_moe_forward launches for act_mode and a batch of
  * T tokens without acc_dump (0 if the mode is unknown), and the name of the

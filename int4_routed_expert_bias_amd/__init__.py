@@ -78,8 +78,8 @@ def lib():
                                         vp, vp, sz, vp], ctypes.c_int),
             "coli_moe_route_forward_profiled": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
                                                  vp, i32, vp, vp, sz, vp, i32, vp], ctypes.c_int),
-            "coli_moe_route_forward_kernel_count": ([i32], ctypes.c_int),
-            "coli_moe_route_forward_kernel_name": ([i32, i32], ctypes.c_char_p),
+            "coli_moe_route_forward_kernel_count": ([i32, i32], ctypes.c_int),
+            "coli_moe_route_forward_kernel_name": ([i32, i32, i32], ctypes.c_char_p),
             "coli_moe_forward_kernel_count": ([i32, i32], ctypes.c_int),
             "coli_moe_forward_kernel_name": ([i32, i32, i32], ctypes.c_char_p),
             "coli_moe_acc_dump_bytes": ([i32, i32, i32, i32, i32], sz),
@@ -199,8 +199,8 @@ def forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, ac
 
 def route_forward(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y, workspace,
                   top_p=None, workspace_nbytes=None, stream=None):
-    """coli_moe_route_forward: route, union and forward in one call (for one
-    token with E <= 256 the gate/up kernel routes the token itself)."""
+    """coli_moe_route_forward: route, union and forward in one call (for up to
+    4 tokens with E <= 256 the gate/up kernel routes the tokens itself)."""
     nb = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
     p = 1.0 if top_p is None else float(top_p)
     _check(lib().coli_moe_route_forward(layer.ref, _ptr(x), T, p, _ptr(ids), _ptr(w),
@@ -211,7 +211,7 @@ def route_forward(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_m
 
 def route_forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y,
                            workspace, events, top_p=None, stream=None):
-    """coli_moe_route_forward (one-token case) recording ``events``."""
+    """coli_moe_route_forward (self-routing case) recording ``events``."""
     nb = workspace.numel() * workspace.element_size()
     p = 1.0 if top_p is None else float(top_p)
     arr = (ctypes.c_void_p * len(events))(*events)
@@ -222,14 +222,14 @@ def route_forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_uni
            "coli_moe_route_forward_profiled")
 
 
-def route_forward_kernel_names(act_mode):
-    n = lib().coli_moe_route_forward_kernel_count(act_mode)
-    return [lib().coli_moe_route_forward_kernel_name(act_mode, i).decode() for i in range(n)]
+def route_forward_kernel_names(act_mode, T=1):
+    n = lib().coli_moe_route_forward_kernel_count(act_mode, T)
+    return [lib().coli_moe_route_forward_kernel_name(act_mode, T, i).decode() for i in range(n)]
 
 
 def route_forward_fused(layer, T, act_mode):
     """Whether coli_moe_route_forward routes inside the gate/up kernel."""
-    return T == 1 and layer.E <= 256
+    return 1 <= T <= 4 and layer.E <= 256 and (act_mode == ACT_F32 or T == 1)
 
 
 def forward_kernel_names(act_mode, T=2):

@@ -276,17 +276,18 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T
                         y, workspace, workspace_bytes, acc_dump, hip_stream, &mk);
 }
 
-// One token, E <= 256: router GEMV, then the forward whose gate/up kernel
-// routes the token itself (fp32 family: three launches; int8: five).
-// Kernels of the one-token route + forward: router GEMV + the forward's.
-static int route_forward_kernels(int32_t act_mode)
+// Kernels of the self-routing route + forward: router GEMV + the forward's.
+static int route_forward_kernels(int32_t act_mode, int32_t T)
 {
-    return 1 + forward_kernel_count(act_mode, 1);
+    return 1 + forward_kernel_count(act_mode, T);
 }
 
-static bool route_forward_fused(const coli_moe_layer *L, int32_t T, int32_t /*act_mode*/)
+// T <= 4 tokens (the int8 family: one), E <= 256: router GEMV, then the
+// forward whose gate/up kernel routes the tokens itself (the top-k launch
+// is saved).
+static bool route_forward_fused(const coli_moe_layer *L, int32_t T, int32_t act_mode)
 {
-    return T == 1 && L->E <= 256;
+    return T >= 1 && T <= 4 && L->E <= 256 && (act_mode == COLI_ACT_F32 || T == 1);
 }
 
 static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
@@ -302,7 +303,7 @@ static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T
     const bool fused = route_forward_fused(L, T, act_mode);
     if (mk) {
         if (!fused) return COLI_E_UNSUPPORTED;
-        const int need = 2 * route_forward_kernels(act_mode);
+        const int need = 2 * route_forward_kernels(act_mode, T);
         if (!mk->ev || mk->n < need) return COLI_E_ARG;
         for (int i = 0; i < need; ++i)
             if (!mk->ev[i]) return COLI_E_ARG;
@@ -327,7 +328,7 @@ static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T
     io.x = x; io.T = T; io.ids = topk_ids; io.w = topk_w;
     io.union_ids = union_ids; io.offsets = offsets; io.slots = slots; io.n_union = n_union;
     io.y = y; io.ws = static_cast<uint8_t *>(workspace); io.lay = lay;
-    if (fused) return status_of(launch_route_forward_t1(d, io, act_mode, top_p, st, mk));
+    if (fused) return status_of(launch_route_forward_small(d, io, act_mode, top_p, st, mk));
     // (the forward buffers alias the route scratch: stream-ordered)
     RouteIO rio{x, T, topk_ids, topk_w, reinterpret_cast<float *>(io.ws + lay.logits), top_p};
     UnionIO un{union_ids, offsets, slots, n_union};
@@ -362,18 +363,17 @@ int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int
                               n_union, act_mode, y, workspace, workspace_bytes, hip_stream, &mk);
 }
 
-int coli_moe_route_forward_kernel_count(int32_t act_mode)
+int coli_moe_route_forward_kernel_count(int32_t act_mode, int32_t T)
 {
-    return act_mode == COLI_ACT_F32 || act_mode == COLI_ACT_I8 ? route_forward_kernels(act_mode) : 0;
+    if (act_mode != COLI_ACT_F32 && act_mode != COLI_ACT_I8) return 0;
+    if (T < 1 || T > 4 || (act_mode == COLI_ACT_I8 && T != 1)) return 0;
+    return route_forward_kernels(act_mode, T);
 }
 
-const char *coli_moe_route_forward_kernel_name(int32_t act_mode, int32_t i)
+const char *coli_moe_route_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
 {
-    static const char *f32[] = {"logits_gemv_kernel", "gateup_t1_kernel", "down_t1c_kernel"};
-    static const char *i8[] = {"logits_gemv_kernel", "quant_rows_kernel", "gateup_i8v_kernel",
-                               "down_i8v_kernel", "combine_kernel"};
-    if (i < 0 || i >= coli_moe_route_forward_kernel_count(act_mode)) return nullptr;
-    return act_mode == COLI_ACT_F32 ? f32[i] : i8[i];
+    if (i < 0 || i >= coli_moe_route_forward_kernel_count(act_mode, T)) return nullptr;
+    return i == 0 ? "logits_gemv_kernel" : coli_moe_forward_kernel_name(act_mode, T, i - 1);
 }
 
 int coli_moe_forward_kernel_count(int32_t act_mode, int32_t T)

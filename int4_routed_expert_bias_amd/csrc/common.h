@@ -143,7 +143,7 @@ inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, in
         }
     }
     w.forward_end = p;
-    w.scores = p; p = align256(p + (size_t)E * 4);
+    w.scores = p; p = align256(p + (size_t)(T <= 4 ? T : 1) * E * 4);
     w.fused_end = p;
     w.total = w.route_end > w.fused_end ? w.route_end : w.fused_end;
     if (w.total == 0) w.total = 256;
@@ -228,22 +228,22 @@ struct UnionIO {
 hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st,
                         const UnionIO *un = nullptr);
 
-// Sigmoid scores of one token (the router GEMV alone) into scores [E].
-hipError_t launch_scores_t1(const LayerDev &L, const float *x, float *scores, hipStream_t st,
-                            Marks *mk = nullptr);
+// Sigmoid scores of T <= 8 tokens (the router GEMV alone) into scores [T][E].
+hipError_t launch_scores(const LayerDev &L, const float *x, int32_t T, float *scores,
+                         hipStream_t st, Marks *mk = nullptr);
 
 hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *union_ids,
                         int32_t *offsets, int32_t *slots, int32_t *n_union, hipStream_t st);
 
-// A single token that routes itself inside its gate/up kernel (see
-// launch_route_forward_t1): the token's sigmoid scores and the selection
-// outputs the gate/up kernel's workgroup 0 writes.
-struct RouteT1 {
-    const float *scores, *bias;  // [E] sigmoid scores of the token, [E] selection bias
-    int E, k, cap;
+// A batch of at most 4 tokens that routes itself inside its gate/up kernel
+// (see launch_route_forward_small): the tokens' sigmoid scores and the
+// selection outputs the gate/up kernel's workgroup 0 writes.
+struct RouteSelf {
+    const float *scores, *bias;  // [T][E] sigmoid scores, [E] selection bias
+    int T, E, k, cap;
     float top_p;
-    int32_t *ids;                // [k]
-    float *w;                    // [k]
+    int32_t *ids;                // [T][k]
+    float *w;                    // [T][k]
     int32_t *union_ids, *offsets, *slots, *n_union;
 };
 
@@ -259,7 +259,7 @@ struct ForwardIO {
     bool combine = true;
     // set: one token whose gate/up kernel selects and unions it (the union
     // lists above are then written by that kernel)
-    const RouteT1 *route = nullptr;
+    const RouteSelf *route = nullptr;
 };
 
 // Kernels one forward call launches (without acc_dump): fp32 family gate/up,
@@ -273,11 +273,12 @@ inline int forward_kernel_count(int act_mode, int T)
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
-// Route and forward of one token (E <= 256): router GEMV (scores into
-// io.ws + io.lay.scores), then the family's forward whose gate/up kernel
-// selects and unions the token itself (writing io.ids / io.w / the union).
-hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, int act_mode,
-                                   float top_p, hipStream_t st, Marks *mk);
+// Route and forward of T <= 4 tokens (E <= 256; the int8 family T == 1):
+// router GEMV (scores into io.ws + io.lay.scores), then the family's forward
+// whose gate/up kernel selects and unions the tokens itself (writing io.ids
+// / io.w / the union).
+hipError_t launch_route_forward_small(const LayerDev &L, const ForwardIO &io, int act_mode,
+                                      float top_p, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
                                    const float *sx, float *h, float *o, hipStream_t st, Marks *mk);

@@ -547,7 +547,7 @@ __device__ __forceinline__ void t1_entry(const GemvArgs &a, int ue, int U, const
 // selection costs each workgroup a few microseconds before its first weight
 // load, against a whole launch of the top-k kernel.  E <= 256.
 template <int P, int NP, int M, int DEPTH, bool XREG, bool ROUTE>
-__global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteT1 r)
+__global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
     constexpr int V = next_pow2(2 * NP * M), N = reduced_count(V);
@@ -895,17 +895,27 @@ __device__ __forceinline__ void chunk_dots_tok(const uint4 (&w)[NR], const float
 // B(e) = e + (GW - ne) * (cost of entries before e) / (total cost), so every
 // entry has at least one wave.  Within an entry the row blocks go
 // round-robin as in t1_split.
+// UL: the union lists are in LDS (read per lane): the values read are made
+// uniform explicitly.
+template <bool UL = false>
+__device__ __forceinline__ int rd_union(const int32_t *p, int i)
+{
+    if constexpr (UL) return __builtin_amdgcn_readfirstlane(p[i]);
+    return p[i];
+}
+
+template <bool UL = false>
 __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, int U,
                                             int nblocks)
 {
     T1Split s{0, 0, 0, 0};
     const int ne = U + a.n_shared;
     if (ne <= 0 || GW < ne) return s;
-    const int total = a.offsets[U] + a.n_shared * a.T + ne;
+    const int total = rd_union<UL>(a.offsets, U) + a.n_shared * a.T + ne;
     const long spare = GW - ne;
     int before = 0;
     for (int e = 0; e < ne; ++e) {
-        const int cnt = 1 + (e < U ? a.offsets[e + 1] - a.offsets[e] : a.T);
+        const int cnt = 1 + (e < U ? rd_union<UL>(a.offsets, e + 1) - rd_union<UL>(a.offsets, e) : a.T);
         const int b0 = e + (int)(spare * before / total);
         const int b1 = e + 1 + (int)(spare * (before + cnt) / total);
         if (gw >= b0 && gw < b1) {
@@ -920,8 +930,10 @@ __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, i
     return s;
 }
 
-template <int P, int M, int DEPTH, int NTOK, int WPB>
-__global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a)
+// ROUTE: the tokens route themselves first (route_self, as the
+// single-token kernel), and the union is read from LDS.
+template <int P, int M, int DEPTH, int NTOK, int WPB, bool ROUTE>
+__global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
     constexpr int V = next_pow2(2 * M * NTOK), N = reduced_count(V);
@@ -933,13 +945,42 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
-    const int U = a.n_union[0];
-    const T1Split sp = mt_split(a, blockIdx.x * WPB + wave, gridDim.x * WPB, U, a.I);
+    int U;
+    if constexpr (ROUTE) {
+        __shared__ RouteLds rl;
+        route_self(r, rl);
+        a.union_ids = rl.u;
+        a.offsets = rl.off;
+        a.slots = rl.sl;
+        a.n_union = rl.n;
+        U = __builtin_amdgcn_readfirstlane(rl.n[0]);
+    } else {
+        U = a.n_union[0];
+    }
+    const T1Split sp = mt_split<ROUTE>(a, blockIdx.x * WPB + wave, gridDim.x * WPB, U, a.I);
     const int nsteps = sp.nsteps;
     const uint8_t *wb;
     const uint16_t *sb;
     const int32_t *list;
-    const int cnt = min(entry_info(a, sp.ue, wb, sb, list), NTOK);
+    int cnt;
+    if constexpr (ROUTE) {
+        if (sp.ue < U) {
+            const int e = rd_union<true>(a.union_ids, sp.ue);
+            wb = a.w + (size_t)e * a.N * (a.K / 2);
+            sb = a.s + (size_t)e * a.N * (a.K / 64);
+            const int o0 = rd_union<true>(a.offsets, sp.ue);
+            list = a.slots + o0;
+            cnt = rd_union<true>(a.offsets, sp.ue + 1) - o0;
+        } else {
+            wb = a.sh_w;
+            sb = a.sh_s;
+            list = nullptr;
+            cnt = a.T;
+        }
+        cnt = min(cnt, NTOK);
+    } else {
+        cnt = min(entry_info(a, sp.ue, wb, sb, list), NTOK);
+    }
     const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
     uint32_t vw[P], vs[P];
     lane_offsets<P>(lane, C, vw, vs);
@@ -1161,7 +1202,7 @@ __global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
 
 template <int NTOK>
 static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs a, float *h,
-                                float *o, hipStream_t st, Marks *mk)
+                                float *o, hipStream_t st, Marks *mk, const RouteSelf *rt = nullptr)
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
@@ -1179,7 +1220,11 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         const dim3 grid(std::max(cus, (entries + WPB - 1) / WPB)), block(WPB * 64);
         const size_t lds = (size_t)io.T * (L.H + L.H / 32) * 4;
 #define COLI_GUM(P_) \
-        if (P == P_) launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB>), grid, block, lds, st, a);
+        if (P == P_) { \
+            if (rt) launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB, true>), grid, block, lds, st, a, *rt); \
+            else launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB, false>), grid, block, lds, st, a, \
+                        RouteSelf{}); \
+        }
         COLI_GUM(1) COLI_GUM(2) COLI_GUM(3) COLI_GUM(4)
 #undef COLI_GUM
         hipError_t err = hipGetLastError();
@@ -1228,7 +1273,7 @@ static int resident_blocks(const void *kern, int P, int NW)
 // workgroup per CU (its register ring plus the x chunks allow two waves per
 // SIMD, and more waves lose DRAM locality), down runs four per CU.
 static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs a, float *h,
-                                float *o, hipStream_t st, Marks *mk, const RouteT1 *rt = nullptr)
+                                float *o, hipStream_t st, Marks *mk, const RouteSelf *rt = nullptr)
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
@@ -1246,7 +1291,7 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         if (P == P_) { \
             if (rt) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, true>), grid, block, lds, st, a, *rt); \
             else launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, false>), grid, block, lds, st, a, \
-                        RouteT1{}); \
+                        RouteSelf{}); \
         }
         COLI_GU1(1) COLI_GU1(2) COLI_GU1(3) COLI_GU1(4)
 #undef COLI_GU1
@@ -1290,15 +1335,16 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
     }
 }
 
-hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, int act_mode, float top_p,
-                                   hipStream_t st, Marks *mk)
+hipError_t launch_route_forward_small(const LayerDev &L, const ForwardIO &io, int act_mode,
+                                      float top_p, hipStream_t st, Marks *mk)
 {
+    const int T = io.T;
     float *scores = reinterpret_cast<float *>(io.ws + io.lay.scores);
-    hipError_t err = launch_scores_t1(L, io.x, scores, st, mk);
+    hipError_t err = launch_scores(L, io.x, T, scores, st, mk);
     if (err != hipSuccess) return err;
-    RouteT1 rt{};
+    RouteSelf rt{};
     rt.scores = scores; rt.bias = L.router_bias;
-    rt.E = L.E; rt.k = L.k; rt.cap = (int)io.lay.cap; rt.top_p = top_p;
+    rt.T = T; rt.E = L.E; rt.k = L.k; rt.cap = (int)io.lay.cap; rt.top_p = top_p;
     rt.ids = const_cast<int32_t *>(io.ids); rt.w = const_cast<float *>(io.w);
     rt.union_ids = const_cast<int32_t *>(io.union_ids); rt.offsets = const_cast<int32_t *>(io.offsets);
     rt.slots = const_cast<int32_t *>(io.slots); rt.n_union = const_cast<int32_t *>(io.n_union);
@@ -1311,9 +1357,11 @@ hipError_t launch_route_forward_t1(const LayerDev &L, const ForwardIO &io, int a
     float *o = reinterpret_cast<float *>(io.ws + io.lay.o);
     GemvArgs a{};
     a.union_ids = io.union_ids; a.offsets = io.offsets; a.slots = io.slots; a.n_union = io.n_union;
-    a.T = 1; a.k = L.k; a.cap = (int)io.lay.cap; a.n_shared = L.n_shared;
+    a.T = T; a.k = L.k; a.cap = (int)io.lay.cap; a.n_shared = L.n_shared;
     a.I = L.I;
-    return launch_f32_t1(L, io, a, h, o, st, mk, &rt);
+    if (T == 1) return launch_f32_t1(L, io, a, h, o, st, mk, &rt);
+    if (T == 2) return launch_f32_mt<2>(L, io, a, h, o, st, mk, &rt);
+    return launch_f32_mt<4>(L, io, a, h, o, st, mk, &rt);
 }
 
 hipError_t launch_forward_f32(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk)

@@ -129,7 +129,7 @@ __device__ __forceinline__ float group_chain(const float *t, const float *ws, in
 // forms the union itself from its sigmoid scores (route_self, as the fp32
 // single-token gate/up kernel), then reads the union from LDS.
 template <int P, int M, int DEPTH, int NTOK, bool ROUTE>
-__global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteT1 r)
+__global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the batch");
     static_assert(!ROUTE || NTOK == 1, "a routing gate/up kernel serves one token");
@@ -415,7 +415,7 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
                 launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, NTOK == 1>), grid, block, lds, st, a, \
                        *io.route); \
             else launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, false>), grid, block, lds, st, a, \
-                        RouteT1{}); \
+                        RouteSelf{}); \
         }
         COLI_GUV(1) COLI_GUV(2) COLI_GUV(3) COLI_GUV(4)
 #undef COLI_GUV

@@ -193,11 +193,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     route_tokens<KPL, UNION>(logits, part, S, bias, T, E, k, top_p, ids, w, uo, blockIdx.x * 4);
 }
 
-hipError_t launch_scores_t1(const LayerDev &L, const float *x, float *scores, hipStream_t st,
-                            Marks *mk)
+hipError_t launch_scores(const LayerDev &L, const float *x, int32_t T, float *scores,
+                         hipStream_t st, Marks *mk)
 {
-    launch(mk, logits_gemv_kernel<1>, dim3(L.E), dim3(256), 0, st, x, L.router_w, 1, L.H, L.E,
-           scores);
+    const dim3 grid(L.E), block(256);
+    if (T <= 1) launch(mk, logits_gemv_kernel<1>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
+    else if (T <= 2) launch(mk, logits_gemv_kernel<2>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
+    else if (T <= 4) launch(mk, logits_gemv_kernel<4>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
+    else launch(mk, logits_gemv_kernel<8>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
     return hipGetLastError();
 }
 

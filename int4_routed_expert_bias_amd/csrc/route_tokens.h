@@ -221,24 +221,25 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
     }
 }
 
-// The selection lists of one token in LDS (cap <= COLI_MAX_K_DEV).
+// The selection lists of at most 4 tokens in LDS (T * k <= 64).
 struct RouteLds {
-    int32_t ids[COLI_MAX_K_DEV], u[COLI_MAX_K_DEV], sl[COLI_MAX_K_DEV];
-    int32_t off[COLI_MAX_K_DEV + 1], n[1];
-    float w[COLI_MAX_K_DEV];
+    int32_t ids[64], u[64], sl[64];
+    int32_t off[65], n[1];
+    float w[64];
 };
 
-// One token selects its top k and forms its union into l (every thread of
-// the 256-thread workgroup calls this); workgroup 0 also writes the global
-// contents the top-k kernel leaves (slots past the kept ones untouched).
-__device__ __forceinline__ void route_self(const RouteT1 &r, RouteLds &l)
+// The tokens (r.T <= 4, one per wave) select their top k and form their
+// union into l (every thread of the 256-thread workgroup calls this);
+// workgroup 0 also writes the global contents the top-k kernel leaves
+// (slots past the kept ones untouched).
+__device__ __forceinline__ void route_self(const RouteSelf &r, RouteLds &l)
 {
     const UnionOut uo{l.u, l.off, l.sl, l.n, r.cap};
-    route_tokens<4, true>(r.scores, nullptr, 0, r.bias, 1, r.E, r.k, r.top_p, l.ids, l.w, uo, 0);
+    route_tokens<4, true>(r.scores, nullptr, 0, r.bias, r.T, r.E, r.k, r.top_p, l.ids, l.w, uo, 0);
     __syncthreads();
     if (blockIdx.x == 0) {
         const int i = threadIdx.x, nu = l.n[0], kept = l.off[nu];
-        if (i < r.k) {
+        if (i < r.T * r.k) {
             r.ids[i] = l.ids[i];
             r.w[i] = l.w[i];
         }

@@ -235,16 +235,21 @@ def test_route_forward_argument_errors(L):
         return L.coli_moe_route_forward_profiled(ctypes.byref(layer()), FAKE, T, ctypes.c_float(1.0),
                                                  FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode, FAKE,
                                                  FAKE, 1 << 30, ev, n, None)
-    assert rfp(T=2) == coli.COLI_E_UNSUPPORTED      # only the one-token case
+    assert rfp(T=5) == coli.COLI_E_UNSUPPORTED      # only the self-routing cases
+    assert rfp(T=2, mode=1, n=12) == coli.COLI_E_UNSUPPORTED
     assert rfp(n=5) == coli.COLI_E_ARG
     assert rfp(holes=True) == coli.COLI_E_ARG
+    assert rfp(T=4, n=7) == coli.COLI_E_ARG          # four kernels: 8 events
     assert rfp(mode=1, n=9) == coli.COLI_E_ARG       # five int8 kernels: 10 events
     assert rfp(mode=1, n=10, holes=True) == coli.COLI_E_ARG
     lib_ = coli.lib()
-    assert [lib_.coli_moe_route_forward_kernel_count(m) for m in (0, 1, 2)] == [3, 5, 0]
-    assert [lib_.coli_moe_route_forward_kernel_name(0, i) for i in (-1, 3)] == [None, None]
-    assert lib_.coli_moe_route_forward_kernel_name(0, 1) == b"gateup_t1_kernel"
-    assert lib_.coli_moe_route_forward_kernel_name(1, 2) == b"gateup_i8v_kernel"
+    cnt = lib_.coli_moe_route_forward_kernel_count
+    assert [cnt(0, 1), cnt(0, 2), cnt(0, 4), cnt(0, 5), cnt(1, 1), cnt(1, 2), cnt(2, 1)] == \
+        [3, 4, 4, 0, 5, 0, 0]
+    name = lib_.coli_moe_route_forward_kernel_name
+    assert [name(0, 1, i) for i in (-1, 3)] == [None, None]
+    assert name(0, 1, 1) == b"gateup_t1_kernel" and name(0, 4, 1) == b"gateup_mt_kernel"
+    assert name(0, 4, 3) == b"combine_kernel" and name(1, 1, 2) == b"gateup_i8v_kernel"
 
 
 def test_route_union_argument_errors(L):

@@ -253,17 +253,18 @@ def _step_outputs(lay, x, T, mode, top_p, step):
 @pytest.mark.parametrize("top_p", [None, 0.7])
 @pytest.mark.parametrize("case", ["decode", "wide_k", "wide_k_no_shared", "small_E", "E_70"])
 def test_route_forward_equals_route_union_then_forward(case, top_p):
-    """coli_moe_route_forward (at T = 1 the gate/up kernel of either family
-    routes the token itself) gives the bits of coli_moe_route_union followed
-    by coli_moe_forward: selection, weights, union and y; larger batches take
-    the two calls."""
+    """coli_moe_route_forward (up to 4 tokens in the fp32 family and one in the
+    int8 family: the gate/up kernel routes the tokens itself) gives the bits
+    of coli_moe_route_union followed by coli_moe_forward: selection, weights,
+    union and y; other batches take the two calls."""
     import torch
     lay = {"decode": lambda: workload_layer("decode"),
            "wide_k": lambda: make_layer(320, 192, 40, 16, wid=70),
            "wide_k_no_shared": lambda: make_layer(320, 192, 40, 16, wid=71, n_shared=0),
            "small_E": lambda: make_layer(256, 128, 12, 3, wid=72),
            "E_70": lambda: make_layer(384, 128, 70, 6, wid=73)}[case]()
-    for T, mode in ((1, coli.ACT_F32), (1, coli.ACT_I8), (3, coli.ACT_F32)):
+    for T, mode in ((1, coli.ACT_F32), (1, coli.ACT_I8), (2, coli.ACT_F32), (3, coli.ACT_F32),
+                    (4, coli.ACT_F32), (4, coli.ACT_I8), (5, coli.ACT_F32)):
         for rep in range(2):
             x = torch.from_numpy(synth.activations(lay.H, T, wid=74 + rep + 10 * T)).cuda()
             a = _step_outputs(lay, x, T, mode, top_p, step=True)
