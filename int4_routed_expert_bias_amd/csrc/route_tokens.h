@@ -4,7 +4,8 @@
 // table "コア技術のハイライト"), the top k per token ("colibri解説", section
 // "なぜ25GBで動くのか"), optionally the adaptive top-p prefix, and for a
 // batch that fits the workgroup the batch union.  Used by the router's top-k
-// kernel and by the single-token gate/up kernel that routes for itself.
+// kernel and by the streaming gate/up kernels of batches of at most 4 tokens
+// that route their tokens themselves (route_self).
 #pragma once
 
 #include "common.h"

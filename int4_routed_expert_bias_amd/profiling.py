@@ -33,7 +33,8 @@ COPY_KERNEL = "copyBuffer"  # the runtime blit kernel behind a device-to-device 
 
 
 def source_hash(files=("expert_f32.hip", "expert_i8.hip", "expert_i8v.hip", "stream.h",
-                       "common.h", "route.hip", "union.hip", "combine.hip")) -> str:
+                       "common.h", "route.hip", "route_tokens.h", "union_wave.h", "union.hip",
+                       "combine.hip")) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(HERE, "csrc", f), "rb") as fp:
