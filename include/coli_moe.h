@@ -128,7 +128,7 @@ size_t coli_moe_workspace_bytes(int32_t H, int32_t I, int32_t E, int32_t k, int3
 int coli_moe_route(const coli_moe_layer *L, const float *x, int32_t T, int32_t *topk_ids,
                    float *topk_w, void *workspace, size_t workspace_bytes, void *hip_stream);
 
-/* Route with adaptive expert top-p ([Heart] "使えるかどうかの判定材料", knob
+/* Route with adaptive expert top-p ([Heart] "速度を稼ぐ実用ノブ", knob
  * list: an adaptive expert top-p, `--topp 0.7`, reading 30-40% fewer expert
  * bytes; the pages give no formula, this is the library's reading).  The
  * top-k selection of coli_moe_route, then per token: with the routing
@@ -202,8 +202,11 @@ int coli_moe_route_union(const coli_moe_layer *L, const float *x, int32_t T, flo
  *   int32  acc2  [R][H][I/64]    down group accumulators,
  *   int8   qh    [R][I]          int8 codes of h (natural element order),
  *   fp32   sh    [R][I/64]       their scales,
+ *   int8   qx    [T][H]          int8 codes of x (natural element order),
+ *   fp32   sx    [T][H/64]       their scales,
  * each region starting at a 256-byte aligned offset; coli_moe_acc_dump_bytes
- * gives the total size. */
+ * gives the total size.  Every batch size fills it from the kernels that
+ * serve that batch size in production. */
 int coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
                      const int32_t *topk_ids, const float *topk_w, const int32_t *union_ids,
                      const int32_t *offsets, const int32_t *slots, const int32_t *n_union,
@@ -284,6 +287,17 @@ int coli_moe_abi_version(void);
 /* COLI_OK when the current HIP device is a gfx950, else COLI_E_UNSUPPORTED
  * (or COLI_E_DEVICE when no device can be queried). */
 int coli_moe_device_check(void);
+
+/* ---- Measurement ---------------------------------------------------------
+ * For measurement only (not part of the layer): reads bytes (a multiple of
+ * 1024, at most 1 GiB) of device memory at buf with the load pattern of the
+ * streaming expert kernels -- 16-byte buffer loads per lane, 1 KB per wave
+ * instruction, 8 loads in flight per wave -- on n_groups workgroups of 4
+ * waves (1..65536), and writes one XOR checksum per workgroup to
+ * out[n_groups] (uint32).  Timing it gives the practical HBM read rate the
+ * streaming kernels' GB/s are compared against. */
+int coli_stream_read(const void *buf, size_t bytes, uint32_t *out, int32_t n_groups,
+                     void *hip_stream);
 
 /* ---- Glue for stacking layers (outside the MoE layer itself) ------------
  * The pages do not describe the blocks around the MoE layer.  To run a

@@ -26,7 +26,7 @@ EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_route_forward_kernel_count", "coli_moe_route_forward_kernel_name",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
-           "coli_rmsnorm", "coli_add_inplace")
+           "coli_rmsnorm", "coli_add_inplace", "coli_stream_read")
 # every symbol declared in include/coli_mla.h
 MLA_EXPORTS = ("coli_mla_workspace_bytes", "coli_mla_decode", "coli_mla_decode_profiled")
 # every symbol declared in include/coli_place.h
@@ -87,6 +87,7 @@ def lib():
             "coli_moe_device_check": ([], ctypes.c_int),
             "coli_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
             "coli_add_inplace": ([vp, vp, i64, vp], ctypes.c_int),
+            "coli_stream_read": ([vp, sz, vp, i32, vp], ctypes.c_int),
             "coli_moe_placer_create": ([i32, i32, i32, i32, i32, i32, i32, vp], ctypes.c_int),
             "coli_moe_placer_destroy": ([vp], None),
             "coli_moe_placer_reset": ([vp], ctypes.c_int),
@@ -245,6 +246,14 @@ def add_inplace(x, y, n, stream=None):
     _check(lib().coli_add_inplace(_ptr(x), _ptr(y), n, _stream(stream)), "coli_add_inplace")
 
 
+def stream_read(buf, out, n_groups, nbytes=None, stream=None):
+    """coli_stream_read (measurement only): read ``buf`` with the streaming
+    kernels' load pattern; one checksum per workgroup into ``out``."""
+    nb = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(lib().coli_stream_read(_ptr(buf), nb, _ptr(out), n_groups, _stream(stream)),
+           "coli_stream_read")
+
+
 class DeviceLayer:
     """One layer's tensors in device memory plus the C descriptor.
 
@@ -338,24 +347,32 @@ def run_layer(layer: DeviceLayer, x, bufs: Buffers, stream=None, top_p=None, fus
     return bufs.y
 
 
-def dump_views(dump_host, H, I, k, T, n_shared):
-    """Split a host copy (numpy uint8) of the acc_dump buffer into its
-    documented regions: acc13 [R][2I][H/64], acc2 [R][H][I/64], qh [R][I],
-    sh [R][I/64]."""
+def dump_regions(H, I, k, T, n_shared):
+    """Byte offset, dtype and shape of each region of the acc_dump buffer
+    (include/coli_moe.h): acc13 [R][2I][H/64], acc2 [R][H][I/64], qh [R][I],
+    sh [R][I/64], qx [T][H], sx [T][H/64], each 256-byte aligned."""
     import numpy as np
     R = T * k + n_shared * T
-    a256 = lambda v: (v + 255) & ~255
-    off = 0
-    n13 = R * 2 * I * (H // 64) * 4
-    acc13 = dump_host[off:off + n13].view(np.int32).reshape(R, 2 * I, H // 64)
-    off = a256(off + n13)
-    n2 = R * H * (I // 64) * 4
-    acc2 = dump_host[off:off + n2].view(np.int32).reshape(R, H, I // 64)
-    off = a256(off + n2)
-    qh = dump_host[off:off + R * I].view(np.int8).reshape(R, I)
-    off = a256(off + R * I)
-    sh = dump_host[off:off + R * (I // 64) * 4].view(np.float32).reshape(R, I // 64)
-    return dict(acc13=acc13, acc2=acc2, qh=qh, sh=sh)
+    regs = [("acc13", np.int32, (R, 2 * I, H // 64)), ("acc2", np.int32, (R, H, I // 64)),
+            ("qh", np.int8, (R, I)), ("sh", np.float32, (R, I // 64)),
+            ("qx", np.int8, (T, H)), ("sx", np.float32, (T, H // 64))]
+    out, off = {}, 0
+    for name, dt, shape in regs:
+        out[name] = (off, dt, shape)
+        n = int(np.prod(shape)) * np.dtype(dt).itemsize
+        off = (off + n + 255) & ~255
+    return out
+
+
+def dump_views(dump_host, H, I, k, T, n_shared):
+    """Split a host copy (numpy uint8) of the acc_dump buffer into its
+    documented regions (see dump_regions)."""
+    import numpy as np
+    out = {}
+    for name, (off, dt, shape) in dump_regions(H, I, k, T, n_shared).items():
+        n = int(np.prod(shape)) * np.dtype(dt).itemsize
+        out[name] = dump_host[off:off + n].view(dt).reshape(shape)
+    return out
 
 
 # ---- placement across pinned host memory and device slots (coli_place.h) ----

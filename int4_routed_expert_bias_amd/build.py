@@ -12,7 +12,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcoli_moe.so")
 
 SOURCES = ["coli_moe.cpp", "route.hip", "union.hip", "expert_f32.hip", "expert_i8.hip", "place.hip",
-           "expert_i8v.hip", "combine.hip", "mla.hip"]
+           "expert_i8v.hip", "combine.hip", "mla.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -23,8 +23,14 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 # Per-file flags.  The router's fp64 MFMA accumulators stay in VGPRs (the
-# default AGPR form copies them across the loop every iteration).
-EXTRA = {"route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# default AGPR form copies them across the loop every iteration).  The
+# streaming kernels' register rings are indexed by unrolled loop counters:
+# the unroll limit for loops marked "#pragma unroll" is raised so that the
+# largest instantiations (four tokens, the accumulator-dump variants) are
+# still fully unrolled.
+_UNROLL = ["-mllvm", "-pragma-unroll-threshold=100000"]
+EXTRA = {"route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "expert_i8v.hip": _UNROLL, "expert_f32.hip": _UNROLL}
 
 
 def _compile(src: str) -> str:

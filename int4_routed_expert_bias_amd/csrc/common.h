@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/coli_moe.h"
+
 namespace coli {
 
 constexpr int kWave = 64;
@@ -152,7 +154,7 @@ inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, in
 
 // acc_dump regions (see coli_moe.h)
 struct DumpLayout {
-    size_t acc13, acc2, qh, sh, total;
+    size_t acc13, acc2, qh, sh, qx, sx, total;
 };
 
 inline DumpLayout dump_layout(int64_t H, int64_t I, int64_t k, int64_t T, int64_t n_shared)
@@ -164,6 +166,8 @@ inline DumpLayout dump_layout(int64_t H, int64_t I, int64_t k, int64_t T, int64_
     d.acc2 = p;  p = align256(p + (size_t)R * H * (I / 64) * 4);
     d.qh = p;    p = align256(p + (size_t)R * I);
     d.sh = p;    p = align256(p + (size_t)R * (I / 64) * 4);
+    d.qx = p;    p = align256(p + (size_t)T * H);
+    d.sx = p;    p = align256(p + (size_t)T * (H / 64) * 4);
     d.total = p;
     return d;
 }

@@ -33,10 +33,13 @@ namespace coli {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // --- activation quantisation ---------------------------------------------
-// rows [nrows][K] fp32 -> q [nrows][K] int8 (permuted), s [nrows][K/64]
+// rows [nrows][K] fp32 -> q [nrows][K] int8 (permuted), s [nrows][K/64];
+// dq / ds (tests only, else null): the same codes in natural order and the
+// scales
 __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict__ x, int64_t ngroups,
                                                          int K, int8_t *__restrict__ q,
-                                                         float *__restrict__ s)
+                                                         float *__restrict__ s, int8_t *dq,
+                                                         float *ds)
 {
     const int lane = threadIdx.x & 63;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -56,6 +59,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict
     }
     q[row * K + perm8_pos(gi * 64 + lane)] = code;
     if (lane == 0) s[row * G + gi] = sc;
+    if (dq) {
+        dq[row * K + gi * 64 + lane] = code;
+        if (lane == 0) ds[row * G + gi] = sc;
+    }
 }
 
 // --- tile schedule ---------------------------------------------------------
@@ -524,13 +531,16 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     int2 *tiles = reinterpret_cast<int2 *>(io.ws + lay.tiles);
 
     const int64_t ng = (int64_t)T * (L.H / 64);
+    int32_t *dump = io.acc_dump;
+    uint8_t *dump_b = reinterpret_cast<uint8_t *>(dump);
     launch(mk, quant_rows_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, st, io.x, ng,
-                       L.H, qx, sx);
+           L.H, qx, sx, dump ? reinterpret_cast<int8_t *>(dump_b + io.dump.qx) : nullptr,
+           dump ? reinterpret_cast<float *>(dump_b + io.dump.sx) : nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // small batches: streaming kernels with the same arithmetic (the test-only
-    // accumulator dump is written by the GEMM path)
-    if (T <= kI8StreamTMax && !io.acc_dump)
+    // small batches: streaming kernels with the same arithmetic (they write
+    // the test-only accumulator dump themselves)
+    if (T <= kI8StreamTMax)
         return launch_forward_i8_small(L, io, qx, sx, reinterpret_cast<float *>(io.ws + lay.h), o,
                                        st, mk);
     // 64-row tiles: measured on MI355X they beat 128-row tiles even for dense
@@ -547,8 +557,6 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.tiles = tiles; a.max_tiles = (int)lay.max_tiles;
     a.T = T; a.k = L.k; a.cap = (int)lay.cap; a.I = L.I; a.H = L.H;
     a.qh = qh; a.sh = sh; a.o = o;
-    int32_t *dump = io.acc_dump;
-    uint8_t *dump_b = reinterpret_cast<uint8_t *>(dump);
     a.qin = qx; a.sin = sx; a.in_by_slot = 0;
     a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
     a.N = 2 * L.I; a.K = L.H;

@@ -2,7 +2,7 @@
 // (1 <= T <= kI8StreamTMax: decode, draft and verify steps).  The pages run
 // decode in f32 and batches on the integer kernel ("Colibri 完全ガイド",
 // walk-through "詳細解説" step 3) and note that the two round differently
-// ("colibri解説", "精度は落としていない"); this path gives small batches the
+// ("colibri解説", "使えるかどうかの判定材料"); this path gives small batches the
 // integer family's function, so a token's output is the same whether it is
 // decoded alone, verified with a few others or prefilled in a large batch.
 //
@@ -19,7 +19,8 @@
 // add the two halves of a group (exact), and the group terms go through LDS
 // to one lane per output that adds them in group order.  The dequantising
 // FMAs of the fp32 family are replaced by 0.6 integer instructions per
-// weight, so these kernels are bound by the weight stream alone.
+// weight; the serial group chain per output through LDS is the part that
+// keeps these kernels from the weight stream's rate.
 #include "common.h"
 #include "stream.h"
 #include "route_tokens.h"
@@ -35,6 +36,12 @@ struct I8vArgs {
     float *out; int out_ld;      // gate/up: h [R][I]; down: o [R][H]
     const int32_t *union_ids, *offsets, *slots, *n_union;
     int T, k, n_shared;
+    // tests only (DUMP kernels): exact group accumulators [R][N][K/64]
+    // (gate/up: acc13, down: acc2) and the down kernel's int8 codes of h
+    // [R][I] (natural order) and their scales [R][I/64]
+    int32_t *dump_acc;
+    int8_t *dump_qh;
+    float *dump_sh;
 };
 
 // Entry ue (union experts in union order, then the shared expert): weight
@@ -128,7 +135,7 @@ __device__ __forceinline__ float group_chain(const float *t, const float *ws, in
 // ROUTE (one token): the workgroup first selects the token's experts and
 // forms the union itself from its sigmoid scores (route_self, as the fp32
 // single-token gate/up kernel), then reads the union from LDS.
-template <int P, int M, int DEPTH, int NTOK, bool ROUTE>
+template <int P, int M, int DEPTH, int NTOK, bool ROUTE, bool DUMP = false>
 __global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the batch");
@@ -243,8 +250,14 @@ __global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteSelf r)
                                 int acc = dot_chunk_i8(wv[d][r][p], xq[j][p]);
                                 acc += pair_lane(acc);
                                 const int c = lane + 64 * p, g = c >> 1;
-                                if (writer && c < C)
+                                if (writer && c < C) {
                                     tl.t[((m * NTOK + j) * 2 + r) * tl.gs + g] = (float)acc * xs[j][p];
+                                    if constexpr (DUMP) {
+                                        const int blk = sp.part + (g0 + m) * sp.wpe;
+                                        const int row = r == 0 ? blk : a.I + blk;
+                                        a.dump_acc[((size_t)orow[j] * a.N + row) * G + g] = acc >> 4;
+                                    }
+                                }
                             }
                 };
                 dispatch_count<NTOK>(cnt, stage);
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteSelf r)
 // Down.  Unit = RD rows of one entry.  Each wave quantises the h rows of its
 // entry's tokens itself (per 64-group, the gate/up GEMM epilogue's
 // arithmetic) into registers, then streams its rows.
-template <int P, int RD, int M, int DEPTH, int NTOK>
+template <int P, int RD, int M, int DEPTH, int NTOK, bool DUMP = false>
 __global__ __launch_bounds__(256) void down_i8v_kernel(I8vArgs a)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the batch");
@@ -340,6 +353,20 @@ __global__ __launch_bounds__(256) void down_i8v_kernel(I8vArgs a)
                 }
                 xq[j][p][2 * blk] = ev;
                 xq[j][p][2 * blk + 1] = od;
+                if constexpr (DUMP) {
+                    // every wave of the entry holds the same codes: the one
+                    // with the first row block writes them in natural order
+                    if (sp.part == 0 && j < cnt && lane + 64 * p < C) {
+                        uint32_t *dq = reinterpret_cast<uint32_t *>(
+                            a.dump_qh + (size_t)row * K + 32 * (lane + 64 * p) + 8 * blk);
+                        dq[0] = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // e0 o0 e1 o1
+                        dq[1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // e2 o2 e3 o3
+                    }
+                }
+            }
+            if constexpr (DUMP) {
+                if (sp.part == 0 && j < cnt && (lane & 1) == 0 && lane + 64 * p < C)
+                    a.dump_sh[(size_t)row * G + ((lane + 64 * p) >> 1)] = sc;
             }
         }
     }
@@ -371,8 +398,13 @@ __global__ __launch_bounds__(256) void down_i8v_kernel(I8vArgs a)
                                 int acc = dot_chunk_i8(wv[d][r][p], xq[j][p]);
                                 acc += pair_lane(acc);
                                 const int c = lane + 64 * p, g = c >> 1;
-                                if (writer && c < C)
+                                if (writer && c < C) {
                                     tl.t[((m * NTOK + j) * RD + r) * tl.gs + g] = (float)acc * xs[j][p];
+                                    if constexpr (DUMP) {
+                                        const int row = (sp.part + (g0 + m) * sp.wpe) * RD + r;
+                                        a.dump_acc[((size_t)orow[j] * a.N + row) * G + g] = acc >> 4;
+                                    }
+                                }
                             }
                 };
                 dispatch_count<NTOK>(cnt, stage);
@@ -396,6 +428,7 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
 {
     const int cus = device_cu_count();
     const int entries = (int)io.lay.cap + L.n_shared;
+    uint8_t *dump = reinterpret_cast<uint8_t *>(io.acc_dump);  // tests only
     {
         // measured on MI355X with the decode layer: one token streams best with
         // two workgroups per CU and a three-stage ring (28.6 us vs 32.2 for one
@@ -406,6 +439,7 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
         a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
         a.N = 2 * L.I; a.K = L.H;
         a.out = h; a.out_ld = L.I;
+        a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump + io.dump.acc13) : nullptr;
         const int P = (L.H / 32 + 63) / 64;
         const size_t lds = (size_t)4 * Lds::rows() * (L.H / 64 + 1) * 4;
         const dim3 grid(std::max((NTOK == 1 ? 2 : 1) * cus, (entries + 3) / 4)), block(256);
@@ -414,6 +448,9 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
             if (NTOK == 1 && io.route) \
                 launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, NTOK == 1>), grid, block, lds, st, a, \
                        *io.route); \
+            else if (dump) \
+                launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, false, true>), grid, block, lds, st, \
+                       a, RouteSelf{}); \
             else launch(mk, (gateup_i8v_kernel<P_, M, DEPTH, NTOK, false>), grid, block, lds, st, a, \
                         RouteSelf{}); \
         }
@@ -431,11 +468,17 @@ static hipError_t launch_i8v(const LayerDev &L, const ForwardIO &io, I8vArgs a, 
         a.N = L.H; a.K = L.I;
         a.h = h;
         a.out = o; a.out_ld = L.H;
+        a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump + io.dump.acc2) : nullptr;
+        a.dump_qh = dump ? reinterpret_cast<int8_t *>(dump + io.dump.qh) : nullptr;
+        a.dump_sh = dump ? reinterpret_cast<float *>(dump + io.dump.sh) : nullptr;
         const int P = (L.I / 32 + 63) / 64;
         const size_t lds = (size_t)4 * Lds::rows() * (L.I / 64 + 1) * 4;
         const dim3 grid(std::max((NTOK == 1 ? 2 : 4) * cus, (entries + 3) / 4)), block(256);
 #define COLI_DNV(P_) \
-        if (P == P_) launch(mk, (down_i8v_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, lds, st, a);
+        if (P == P_) { \
+            if (dump) launch(mk, (down_i8v_kernel<P_, RD, M, DEPTH, NTOK, true>), grid, block, lds, st, a); \
+            else launch(mk, (down_i8v_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, lds, st, a); \
+        }
         COLI_DNV(1) COLI_DNV(2) COLI_DNV(3) COLI_DNV(4)
 #undef COLI_DNV
         hipError_t err = hipGetLastError();

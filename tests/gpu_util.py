@@ -2,6 +2,8 @@
 ABI on seeded synthetic layers and compare with the CPU oracle."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import int4_routed_expert_bias_amd as coli
@@ -24,34 +26,90 @@ def assert_close(got, ref, what, tol=TOL):
     return e
 
 
-def f32_ulp_diff(a, b):
-    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
-    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
-    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
-    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
-    return np.abs(ai - bi)
+def pool_map(fn, items, workers=None):
+    """fn over items on a thread pool (the oracle's C calls release the GIL);
+    results in item order.  At most 16 workers (one GPU's CPU share)."""
+    from concurrent.futures import ThreadPoolExecutor
+    items = list(items)
+    n = workers or max(1, min(16, os.cpu_count() or 1, len(items)))
+    with ThreadPoolExecutor(n) as ex:
+        return list(ex.map(fn, items))
 
 
-def check_route(gpu_ids, gpu_w, orc_ids, orc_w, orc_scores, bias):
-    """Ids must equal the oracle's.  A token may differ only at a near-tie of
-    the selection keys (within 4 ulps at the k-th position), where both
-    orders are correct; such tokens are counted and returned."""
+def orc_route_all(orc, lay_orc, x, chunk=64):
+    """The oracle's routing of every row of x (ids, w, logits, scores), rows
+    split over threads."""
+    x = np.ascontiguousarray(x, np.float32)
+    parts = pool_map(lambda a: orc.route(lay_orc, x[a:a + chunk]), range(0, x.shape[0], chunk))
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))
+
+
+def check_route(gpu_ids, gpu_w, orc_ids, orc_w):
+    """Router selections must equal the oracle's bit for bit, every token and
+    every position (the selection order included); the routing weights agree
+    within the tolerance."""
     gpu_ids = np.asarray(gpu_ids)
-    near = 0
-    for t in range(orc_ids.shape[0]):
-        if np.array_equal(gpu_ids[t], orc_ids[t]):
-            continue
-        key = (orc_scores[t] + bias).astype(np.float32)
-        kth = key[orc_ids[t, -1]]
-        diff = set(gpu_ids[t].tolist()) ^ set(orc_ids[t].tolist())
-        order_only = not diff
-        cands = diff if diff else set(orc_ids[t].tolist())
-        ok = all(f32_ulp_diff(key[e], kth) <= 4 for e in cands) or order_only and all(
-            f32_ulp_diff(key[gpu_ids[t, j]], key[orc_ids[t, j]]) <= 4 for j in range(len(gpu_ids[t])))
-        assert ok, f"token {t}: gpu ids {gpu_ids[t]} != oracle {orc_ids[t]} (not a near tie)"
-        near += 1
+    bad = np.nonzero(~np.all(gpu_ids == orc_ids, axis=1))[0]
+    assert bad.size == 0, (f"{bad.size} token(s) routed differently from the oracle, first "
+                           f"{bad[0]}: gpu {gpu_ids[bad[0]]} vs oracle {orc_ids[bad[0]]}")
     assert_close(gpu_w, orc_w, "topk_w")
-    return near
+
+
+def tile_rows(ids, union_ids, offsets, slots, n_union, T, k, n_shared, tile=64):
+    """Rows of the expert outputs o to check so that the first and the last
+    tile of every union entry's row list hold a checked row (its first
+    row, the last row of its first full tile, its last row): a list of
+    (o row, token, expert) with o row = slot t*k+j for a routed expert and
+    T*k+t for the shared expert (expert -1)."""
+    rows = []
+    for u in range(n_union):
+        a, b = int(offsets[u]), int(offsets[u + 1])
+        for p in sorted({a, min(a + tile - 1, b - 1), b - 1}):
+            sl = int(slots[p])
+            t, j = sl // k, sl % k
+            assert ids[t, j] == union_ids[u]
+            rows.append((sl, t, int(union_ids[u])))
+    if n_shared:
+        for t in sorted({0, min(tile - 1, T - 1), T - 1}):
+            rows.append((T * k + t, t, -1))
+    return rows
+
+
+def workspace_o(bufs, R, H):
+    """The expert outputs o [R][H] fp32 that the forward leaves at offset 0
+    of its workspace (the library's workspace layout, both families)."""
+    import torch
+    return bufs.workspace[:R * H * 4].view(torch.float32).view(R, H)
+
+
+def check_expert_rows(orc, arrays, x, o_rows, rows, mode, what):
+    """Each listed o row (o row, token, expert) against the oracle's output
+    of that expert for that token (the token's input row of x), within the
+    tolerance per row; rows run on a thread pool."""
+    import oracle as oracle_mod
+
+    def ref(r):
+        _, t, e = r
+        if e >= 0:
+            w = (arrays["w13"][e], arrays["s13"][e], arrays["w2"][e], arrays["s2"][e])
+        else:
+            w = (arrays["sh_w13"], arrays["sh_s13"], arrays["sh_w2"], arrays["sh_s2"])
+        f = orc.expert_i8 if mode == oracle_mod.ACT_I8 else orc.expert_f32
+        return f(*w, x[t])["o"]
+
+    refs = pool_map(ref, rows)
+    for i, (r, ro) in enumerate(zip(rows, refs)):
+        assert_close(o_rows[i], ro, f"{what}: o row {r[0]} (token {r[1]}, expert {r[2]})")
+
+
+def orc_y_rows(orc, lay_orc, x_rows, ids_rows, w_rows, mode):
+    """The oracle's layer output for each given token (its input row, ids
+    and weights), one token per thread."""
+    x_rows = np.ascontiguousarray(x_rows, np.float32)
+    ys = pool_map(lambda i: orc.forward_rows(lay_orc, x_rows[i:i + 1], ids_rows[i:i + 1],
+                                             w_rows[i:i + 1], np.zeros(1, np.int32), mode)[0],
+                  range(x_rows.shape[0]))
+    return np.stack(ys)
 
 
 class GpuLayer:
