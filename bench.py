@@ -19,12 +19,22 @@ Workloads (--workload):
                  int8 family; a step is the whole stack.
   tiny           H256 I128 E16 top-2, T=4 (parity-size workload).
 
-The timed steps are captured once in a HIP graph and replayed between two
-synchronisations (wall clock).  The dominant kernel's duration comes from
-HIP events that each kernel's own dispatch records at its start and end
-(coli_moe_route_forward_profiled / coli_moe_forward_profiled launch through
-hipExtLaunchKernel on the library's stream), over the same inputs.  Prints
-one JSON line.
+Without --workload the run reports decode as the headline line (value,
+roofline, cpu_baseline) and verify, prefill512 and prefill4096x8 beside it
+under "workloads", each with its own tokens/s, roofline (int8 TOP/s for the
+prefill GEMM when it is matrix-core bound) and oracle baseline; plus the
+plain HBM read rate with the streaming kernels' load pattern
+("hbm_read_ceiling"), the GPU clocks and the host CPU.
+
+Per workload, the timed steps are captured once in a HIP graph and replayed
+between two synchronisations (wall clock): value = tokens / that time.  The
+dominant kernel's duration comes from HIP events that each kernel's own
+dispatch records at its start and end (coli_moe_route_forward_profiled /
+coli_moe_forward_profiled launch through hipExtLaunchKernel on the library's
+stream), over the same inputs; the same events give the median and p10/p90
+of a layer call, warm and cold (after a 1 GiB write that flushes L2 and the
+Infinity Cache).  The oracle baseline runs single-threaded on one pinned host
+CPU.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -34,6 +44,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -58,11 +70,17 @@ class Hip:
                                                ctypes.c_void_p]
         self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def event(self):
         e = ctypes.c_void_p()
         assert self.L.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
+
+    def record(self, e, stream=None):
+        import torch
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        assert self.L.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(st)) == 0
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -77,90 +95,176 @@ def expert_bytes(H, I):
     return 3 * I * H // 2 + 3 * I * (H // 64) * 2
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "verify", "prefill512", "prefill4096x8", "tiny",
-                             "mla", "mla_verify", "mla_dsa"])
-    ap.add_argument("--layers", type=int, default=None, help="resident layer copies cycled (decode/verify)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
-    ap.add_argument("--act-mode", choices=["f32", "i8"], default=None,
-                    help="arithmetic family (default: the workload's own)")
-    ap.add_argument("--topp", type=float, default=None,
-                    help="adaptive expert top-p router (coli_moe_route_topp) instead of top-k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (the reference for HBM counters)")
-    ap.add_argument("--place-slots", type=int, default=None,
-                    help="Place + Overlap: routed experts in pinned host memory, this many "
-                         "device slots per layer (coli_moe_forward_placed)")
-    ap.add_argument("--place-chunk", type=int, default=1, help="loaded experts per compute pass")
-    ap.add_argument("--no-overlap", action="store_true",
-                    help="placed mode: copies on the compute stream (no copy/compute overlap)")
-    args = ap.parse_args()
+DEFAULT_STEPS = {"decode": (256, 32), "verify": (128, 16), "prefill512": (20, 4),
+                 "prefill4096x8": (4, 1), "tiny": (256, 32)}
+# the workloads reported beside the headline (decode) in a default run
+EXTRA_WORKLOADS = ("verify", "prefill512", "prefill4096x8")
 
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU sharding "
-                                   "of the layer is a design (see the design notes), not built",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
 
-    import numpy as np
+def host_info():
+    """CPU model and counts of the host the oracle baseline runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_allowed": aff}
+
+
+def gpu_clocks():
+    """Current shader and memory clocks (MHz) of GPU 0: the level marked '*'
+    in the driver's DPM tables, else rocm-smi's report; None if neither."""
+    import glob
+    import re
+    import subprocess
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            for key, fn in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+                with open(os.path.join(card, fn)) as f:
+                    for line in f:
+                        if "*" in line:
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                out[key] = int(m.group(1))
+            if out:
+                out["source"] = card + "/pp_dpm_*"
+                return out
+        except OSError:
+            continue
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+        for line in r.stdout.splitlines():
+            m = re.search(r"\b(sclk|mclk)\b.*?\((\d+)\s*Mhz\)", line, re.I)
+            if m and m.group(1).lower() not in out:
+                out[m.group(1).lower()] = int(m.group(2))
+        if out:
+            out["source"] = "rocm-smi --showclocks"
+            return out
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return None
+
+
+def stream_read_rate(hip, n_bufs=8, nbytes=188 << 20, reps=3):
+    """Plain HBM read rate with the streaming kernels' load pattern
+    (coli_stream_read) over n_bufs distinct buffers of the decode step's
+    size (so that no read is served by the 256 MB Infinity Cache), for a
+    range of workgroup counts; GB/s of the best count and all counts."""
     import torch
-
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+    import int4_routed_expert_bias_amd as coli
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(n_bufs)]
+    out = torch.empty((64 * cus,), dtype=torch.int32, device="cuda")
+    res = {}
+    for mult in (1, 2, 4, 8):
+        g = mult * cus
+        for b in bufs:  # warm
+            coli.stream_read(b, out, g)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
-        return
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0)
+        for _ in range(reps):
+            for b in bufs:
+                coli.stream_read(b, out, g)
+        hip.record(e1)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(e0, e1)
+        hip.destroy(e0)
+        hip.destroy(e1)
+        res[f"{mult}x_cus"] = round(reps * n_bufs * nbytes / (ms * 1e-3) / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    best = max(res, key=res.get)
+    return {"gbs": res[best], "workgroups": best, "by_workgroups": res,
+            "bytes_per_read": nbytes, "buffers": n_bufs,
+            "kernel": "stream_read_kernel (coli_stream_read)"}
 
+
+def percentiles(v):
+    v = np.asarray(v, np.float64)
+    return {"median": round(float(np.median(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
+            "p90": round(float(np.percentile(v, 90)), 2), "n": int(v.size)}
+
+
+def oracle_baseline(w, host0, mode, topp, cpu_seconds):
+    """The oracle, single-threaded and pinned to one host CPU, on tokens of
+    the workload one at a time (route, union and forward) for about
+    cpu_seconds."""
+    import oracle
+    import synth
+    import int4_routed_expert_bias_amd as coli
+    orc = oracle.default()
+    olay = oracle.Layer(host0, k=w.k, n_shared=w.n_shared)
+    stacked = w.layers > 1
+    xh = synth.workload_x(w, layer=0) if (stacked or w.x_kind == "overlap") else \
+        synth.activations(w.H, w.T, wid=w.wid)
+    omode = oracle.ACT_I8 if mode == coli.ACT_I8 else oracle.ACT_F32
+    pinned = None
+    old_aff = None
+    if hasattr(os, "sched_setaffinity"):
+        old_aff = os.sched_getaffinity(0)
+        pinned = min(old_aff)
+        os.sched_setaffinity(0, {pinned})
+    try:
+        done, t0 = 0, time.perf_counter()
+        while True:
+            xt = xh[done % w.T:done % w.T + 1]
+            ids, wt, _, _ = orc.route(olay, xt) if topp is None else orc.route_topp(olay, xt, topp)
+            orc.union(ids, w.E)
+            orc.forward(olay, xt, ids, wt, omode)
+            done += 1
+            if time.perf_counter() - t0 >= cpu_seconds or done >= 1000:
+                break
+        t_cpu = time.perf_counter() - t0
+    finally:
+        if old_aff is not None:
+            os.sched_setaffinity(0, old_aff)
+    return {"value": round(done / t_cpu, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "pinned_cpu": pinned,
+            "sample": f"{done} token(s) of the {w.name} workload, one at a time through route, "
+                      f"union and forward on layer 0 ({t_cpu:.1f} s, single-threaded C oracle "
+                      f"pinned to one CPU)"}
+
+
+def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_graph=True,
+                   cpu_seconds=12.0, with_cpu=True, prof_steps=None):
+    """One resident-layer workload: K graph-replayed steps after W warmup
+    steps, then the per-kernel and per-step times from dispatch-recorded
+    events (warm, and cold after a 1 GiB write that flushes the caches), the
+    roofline of the dominant kernel and the oracle baseline."""
+    import torch
     import int4_routed_expert_bias_amd as coli
     from int4_routed_expert_bias_amd import profiling
     import synth
 
-    assert torch.cuda.is_available(), "needs a GPU"
-    torch.cuda.set_device(0)
-    if coli.device_check() != coli.COLI_OK:
-        raise SystemExit("device is not gfx950: " + coli.strerror(coli.device_check()))
-
-    if args.workload.startswith("mla"):
-        return bench_mla(args)
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[name]
     H, I, E, k, T = w.H, w.I, w.E, w.k, w.T
-    fam = args.act_mode or w.act_mode
+    fam = act_mode or w.act_mode
     mode = coli.ACT_I8 if fam == "i8" else coli.ACT_F32
-    if args.place_slots is not None:
-        return bench_placed(args, w, mode)
     stacked = w.layers > 1
-    defaults = {"decode": (256, 32), "verify": (128, 16), "prefill512": (20, 4),
-                "prefill4096x8": (4, 1), "tiny": (256, 32)}
-    K = args.steps if args.steps is not None else defaults[w.name][0]
-    W = args.warmup if args.warmup is not None else defaults[w.name][1]
-    if stacked:
-        NL = w.layers
-    else:
-        NL = args.layers if args.layers is not None else (8 if w.name in ("decode", "verify") else 1)
+    NL = w.layers if stacked else (layers if layers is not None else
+                                   (8 if name in ("decode", "verify") else 1))
 
     # ---- resident layers -------------------------------------------------
     t0 = time.time()
-    layers = []
+    devl = []
     host0 = None
     for l in range(NL):
         A = synth.workload_layer(w, layer=l)
         if l == 0:
             host0 = A
-        layers.append(coli.DeviceLayer(A, k=k, n_shared=w.n_shared))
+        devl.append(coli.DeviceLayer(A, k=k, n_shared=w.n_shared))
         if l > 0:
             del A
-    log(f"[bench] {NL} layer(s) resident ({NL * (w.E + 1) * expert_bytes(H, I) / 1e9:.1f} GB experts) "
-        f"in {time.time() - t0:.1f}s")
+    log(f"[bench] {name}: {NL} layer(s) resident ({NL * (E + 1) * expert_bytes(H, I) / 1e9:.1f} GB "
+        f"experts) in {time.time() - t0:.1f}s")
 
     # ---- inputs and buffers ----------------------------------------------
     nsteps_in = W + K
@@ -172,31 +276,29 @@ def main():
     else:
         xall = torch.from_numpy(synth.activations(H, T * nsteps_in, wid=w.wid)).cuda()
         xs = [xall[s * T:(s + 1) * T] for s in range(nsteps_in)]
-    bufs = coli.Buffers(layers[0], T, mode)
+    bufs = coli.Buffers(devl[0], T, mode)
     if stacked:
         resid = torch.empty((T, H), dtype=torch.float32, device="cuda")
         xhat = torch.empty_like(resid)
 
-    one_call = coli.route_forward_fused(layers[0], T, mode)  # coli_moe_route_forward
+    one_call = coli.route_forward_fused(devl[0], T, mode)  # coli_moe_route_forward
 
     def step(s):
         if stacked:
             resid.copy_(xs[0])
-            for l, lay in enumerate(layers):
+            for lay in devl:
                 coli.rmsnorm(resid, xhat, T, H, 1e-6)
-                coli.run_layer(lay, xhat, bufs, top_p=args.topp)
+                coli.run_layer(lay, xhat, bufs, top_p=topp)
                 coli.add_inplace(resid, bufs.y, T * H)
         else:
-            coli.run_layer(layers[s % NL], xs[s], bufs, top_p=args.topp,
+            coli.run_layer(devl[s % NL], xs[s], bufs, top_p=topp,
                            fused="step" if one_call else True)
 
-    # ---- warmup ----------------------------------------------------------
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
 
-    # ---- timed region ----------------------------------------------------
-    use_graph = not args.no_graph
+    # ---- timed region: K steps in one HIP graph, replayed ------------------
     if use_graph:
         g = torch.cuda.CUDAGraph()
         cap_stream = torch.cuda.Stream()
@@ -212,6 +314,7 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         t_end = time.perf_counter()
+        del g
     else:
         torch.cuda.synchronize()
         t_start = time.perf_counter()
@@ -224,49 +327,63 @@ def main():
     value = layer_passes * T / elapsed
     ms_per_step = elapsed * 1e3 / K
 
-    # ---- dominant kernel: per-kernel events on the library's stream ------
+    # ---- per-kernel and per-layer-call times: dispatch-recorded events ------
     hip = Hip()
     names = coli.route_forward_kernel_names(mode, T) if one_call else coli.forward_kernel_names(mode, T)
     nk = len(names)
     dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
-    prof_steps = min(K, 64)
-    ev = [[hip.event() for _ in range(2 * nk)] for _ in range(prof_steps * (w.layers if stacked else 1))]
+    flush = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")  # 1 GiB
+    if prof_steps is None:
+        prof_steps = 8 if stacked else 64
     union_sizes = []
-    torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
-    i = 0
-    for s in range(prof_steps):
-        if stacked:
-            resid.copy_(xs[0])
-            lays = list(enumerate(layers))
-        else:
-            lays = [(0, layers[(W + s) % NL])]
-        for _, lay in lays:
-            x_in = xs[W + s] if not stacked else xhat
-            if stacked:
-                coli.rmsnorm(resid, xhat, T, H, 1e-6)
-            if one_call:
-                coli.route_forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
-                                            bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
-                                            bufs.workspace, ev[i], top_p=args.topp)
-            else:
-                coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
-                                 bufs.slots, bufs.n_union, bufs.workspace, top_p=args.topp)
-                coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
-                                      bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
-                                      bufs.workspace, ev[i])
-            union_sizes.append(bufs.n_union[:1].clone())
-            if stacked:
-                coli.add_inplace(resid, bufs.y, T * H)
-            i += 1
-    torch.cuda.synchronize()
     per_kernel = np.zeros(nk)
-    for e in ev:
-        for j in range(nk):
-            per_kernel[j] += hip.elapsed_ms(e[2 * j], e[2 * j + 1])
-    per_kernel /= len(ev)
-    for e in ev:
-        for x_ in e:
-            hip.destroy(x_)
+    calls = {"warm": [], "cold": []}
+    for phase in ("warm", "cold"):
+        # per layer call: 2 marks per kernel, then one event recorded on the
+        # stream just before the call (the start of its routing launches)
+        ev = [[hip.event() for _ in range(2 * nk + 1)] for _ in range(prof_steps * (w.layers if stacked else 1))]
+        torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
+        i = 0
+        for s in range(prof_steps):
+            if stacked:
+                resid.copy_(xs[0])
+                lays = devl
+            else:
+                lays = [devl[(W + s) % NL]]
+            for lay in lays:
+                x_in = xs[(W + s) % len(xs)] if not stacked else xhat
+                if stacked:
+                    coli.rmsnorm(resid, xhat, T, H, 1e-6)
+                if phase == "cold":
+                    flush.zero_()  # evicts the L2 and Infinity Cache contents
+                hip.record(ev[i][2 * nk])
+                if one_call:
+                    coli.route_forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
+                                                bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
+                                                bufs.workspace, ev[i][:2 * nk], top_p=topp)
+                else:
+                    coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
+                                     bufs.slots, bufs.n_union, bufs.workspace, top_p=topp)
+                    coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
+                                          bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
+                                          bufs.workspace, ev[i][:2 * nk])
+                if phase == "warm":
+                    union_sizes.append(bufs.n_union[:1].clone())
+                if stacked:
+                    coli.add_inplace(resid, bufs.y, T * H)
+                i += 1
+        torch.cuda.synchronize()
+        for e in ev:
+            # one layer call: from the event before it to its last kernel's end
+            calls[phase].append(hip.elapsed_ms(e[2 * nk], e[2 * nk - 1]) * 1e3)
+            if phase == "warm":
+                for j in range(nk):
+                    per_kernel[j] += hip.elapsed_ms(e[2 * j], e[2 * j + 1])
+            for x_ in e:
+                hip.destroy(x_)
+        if phase == "warm":
+            per_kernel /= len(ev)
+    del flush
     U = np.array([int(u.item()) for u in union_sizes])
     dur_s = per_kernel[dom] * 1e-3
     n_exp = U.mean() + w.n_shared
@@ -289,59 +406,134 @@ def main():
         ach = algo_bytes / dur_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    traffic = None
+    # HBM bytes per launch from the committed counter record (profiles/):
+    # reported only while the kernel sources are those the counters were
+    # taken on, and labelled as that stored record
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tpath):
+    if os.path.exists(tpath) and topp is None:
         with open(tpath) as fp:
             rec = json.load(fp).get(f"{w.name}:{names[dom]}")
-        # the counters were taken with plain top-k routing
-        if rec and rec.get("source_hash") == profiling.source_hash() and args.topp is None:
-            traffic = rec["hbm_bytes_per_launch"]
-    roof["traffic"] = traffic
+        if rec and rec.get("source_hash") == profiling.source_hash():
+            roof["traffic"] = rec["hbm_bytes_per_launch"]
+            roof["traffic_source"] = ("profiles/traffic.json (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
+                                      "copy-calibrated; same kernel sources)")
     roof["kernel"] = names[dom]
     roof["kernel_us"] = round(per_kernel[dom] * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = int(algo_bytes)
     roof["algorithmic_ops_per_launch"] = int(algo_ops)
+    if mode == coli.ACT_I8:
+        roof["hbm_gbs_of_kernel"] = round(algo_bytes / dur_s / 1e9, 1)
+        roof["int8_tops_of_kernel"] = round(algo_ops / dur_s / 1e12, 2)
     kernels_us = {names[j]: round(per_kernel[j] * 1e3, 2) for j in range(nk)}
 
-    # ---- CPU baseline: the oracle on a bounded sample ---------------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        orc = oracle.default()
-        olay = oracle.Layer(host0, k=k, n_shared=w.n_shared)
-        xh = synth.workload_x(w, layer=0) if (stacked or w.x_kind == "overlap") else \
-            synth.activations(H, T, wid=w.wid)
-        done, t_cpu0 = 0, time.perf_counter()
-        omode = oracle.ACT_I8 if mode == coli.ACT_I8 else oracle.ACT_F32
-        while True:
-            xt = xh[done % T:done % T + 1]
-            ids, wt, _, _ = (orc.route(olay, xt) if args.topp is None
-                             else orc.route_topp(olay, xt, args.topp))
-            orc.union(ids, E)
-            orc.forward(olay, xt, ids, wt, omode)
-            done += 1
-            if time.perf_counter() - t_cpu0 >= args.cpu_seconds or done >= 1000:
-                break
-        t_cpu = time.perf_counter() - t_cpu0
-        cpu = {"value": round(done / t_cpu, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} token(s) of the {w.name} workload through route, union and "
-                         f"forward on layer 0 ({t_cpu:.1f} s, single-threaded C oracle)"}
-
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8" if mode == coli.ACT_I8 else "f32",
-        "data": "synthetic",
+    cpu = oracle_baseline(w, host0, mode, topp, cpu_seconds) if with_cpu else None
+    res = {
+        "value": round(value, 2), "unit": "tokens/s", "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5), "dtype": "i8" if mode == coli.ACT_I8 else "f32",
         "config": {"workload": w.name, "description": w.note, "H": H, "I": I, "E": E, "k": k,
                    "T": T, "n_shared": w.n_shared, "layers": NL,
-                   "act_mode": "i8" if mode == coli.ACT_I8 else "f32", "top_p": args.topp,
+                   "act_mode": "i8" if mode == coli.ACT_I8 else "f32", "top_p": topp,
                    "graph": use_graph, "union_size_mean": round(float(U.mean()), 2),
                    "union_size_minmax": [int(U.min()), int(U.max())],
                    "kernels_us": kernels_us},
+        # per layer call (route + union + forward), eager with the queue kept
+        # full; cold: after a 1 GiB write that flushes L2 and Infinity Cache
+        "layer_call_us": {"warm": percentiles(calls["warm"]), "cold": percentiles(calls["cold"])},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    del devl, bufs, xs
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=None,
+                    choices=["decode", "verify", "prefill512", "prefill4096x8", "tiny",
+                             "mla", "mla_verify", "mla_dsa"],
+                    help="run only this workload (default: decode as the headline, with verify, "
+                         "prefill512 and prefill4096x8 reported beside it)")
+    ap.add_argument("--layers", type=int, default=None, help="resident layer copies cycled (decode/verify)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--act-mode", choices=["f32", "i8"], default=None,
+                    help="arithmetic family (default: the workload's own)")
+    ap.add_argument("--topp", type=float, default=None,
+                    help="adaptive expert top-p router (coli_moe_route_topp) instead of top-k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    ap.add_argument("--prof-steps", type=int, default=None,
+                    help="event-timed steps per phase (default 64; 8 for the 8-layer stack)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (the reference for HBM counters)")
+    ap.add_argument("--place-slots", type=int, default=None,
+                    help="Place + Overlap: routed experts in pinned host memory, this many "
+                         "device slots per layer (coli_moe_forward_placed)")
+    ap.add_argument("--place-chunk", type=int, default=1, help="loaded experts per compute pass")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="placed mode: copies on the compute stream (no copy/compute overlap)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU sharding "
+                                   "of the layer is a design (see the design notes), not built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
+        return
+
+    import int4_routed_expert_bias_amd as coli
+    import synth
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+    if coli.device_check() != coli.COLI_OK:
+        raise SystemExit("device is not gfx950: " + coli.strerror(coli.device_check()))
+
+    if args.workload is not None and args.workload.startswith("mla"):
+        return bench_mla(args)
+    name = args.workload or "decode"
+    w = synth.WORKLOADS[name]
+    if args.place_slots is not None:
+        fam = args.act_mode or w.act_mode
+        return bench_placed(args, w, coli.ACT_I8 if fam == "i8" else coli.ACT_F32)
+    K = args.steps if args.steps is not None else DEFAULT_STEPS[name][0]
+    W = args.warmup if args.warmup is not None else DEFAULT_STEPS[name][1]
+    head = bench_resident(name, K, W, act_mode=args.act_mode, topp=args.topp, layers=args.layers,
+                          use_graph=not args.no_graph, cpu_seconds=args.cpu_seconds,
+                          with_cpu=not args.no_cpu_baseline, prof_steps=args.prof_steps)
+    clocks = gpu_clocks()
+    out = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": K, "warmup": W, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic"}
+    for key in ("config", "layer_call_us", "roofline", "cpu_baseline"):
+        out[key] = head[key]
+    if args.workload is None:
+        # the other workloads of the metric, each with its own default steps
+        extra = {}
+        for nm in EXTRA_WORKLOADS:
+            kk, ww = DEFAULT_STEPS[nm]
+            r = bench_resident(nm, kk, ww, cpu_seconds=args.cpu_seconds,
+                               with_cpu=not args.no_cpu_baseline)
+            extra[nm] = r
+            log(f"[bench] {nm}: {r['value']:.0f} tokens/s, {r['roofline']['kernel']} "
+                f"{r['roofline']['kernel_us']} us = {r['roofline']['frac']:.3f} of its roofline")
+        out["workloads"] = extra
+        out["hbm_read_ceiling"] = stream_read_rate(Hip())
+    out["clocks_mhz"] = clocks
+    out["host"] = host_info()
     print(json.dumps(out), flush=True)
 
 

@@ -5,6 +5,11 @@ Used on the measurement side only (never by the compute path):
   python -m int4_routed_expert_bias_amd.profiling trace <run_kernel_trace.csv> --command "..."
       markdown table of per-kernel durations (avg / min / max, grid, registers)
 
+  python -m int4_routed_expert_bias_amd.profiling counters <pmc dir> [<pmc dir> ...] \
+      --match <kernel name substring> [--match ...]
+      markdown table of the per-dispatch mean of every counter collected
+      for the matching kernels, with the ratios derived from them
+
   python -m int4_routed_expert_bias_amd.profiling traffic \
       --fetch <pmc dir> --write <pmc dir> --copy-fetch <pmc dir> --copy-write <pmc dir> \
       --kernel <label> --match <trace name substring> --workload <name> \
@@ -85,12 +90,56 @@ def pmc_avg(pmc_dir: str, counter: str, kernel_sub: str) -> float:
     return statistics.mean(vals)
 
 
+def counter_table(dirs, matches) -> str:
+    """Per-dispatch means of every counter in the counter-collection CSVs
+    under dirs, for the kernels whose names contain one of matches."""
+    per = {}
+    for d in dirs:
+        for r in _rows(d, "*counter_collection.csv"):
+            m = next((mm for mm in matches if mm in r["Kernel_Name"]), None)
+            if m is None:
+                continue
+            per.setdefault(m, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    out = ["| counter | " + " | ".join(f"`{m}`" for m in matches) + " |",
+           "|---|" + "---|" * len(matches)]
+    for c in names:
+        cells = []
+        for m in matches:
+            v = per.get(m, {}).get(c)
+            cells.append(f"{statistics.mean(v):,.0f} (n={len(v)})" if v else "-")
+        out.append(f"| {c} | " + " | ".join(cells) + " |")
+
+    def mean(m, c):
+        v = per.get(m, {}).get(c)
+        return statistics.mean(v) if v else None
+    derived = []
+    for m in matches:
+        valu, mfma = mean(m, "SQ_INSTS_VALU"), mean(m, "SQ_INSTS_MFMA")
+        busy, gui = mean(m, "SQ_VALU_MFMA_BUSY_CYCLES"), mean(m, "GRBM_GUI_ACTIVE")
+        conf, lds = mean(m, "SQ_LDS_BANK_CONFLICT"), mean(m, "SQ_ACTIVE_INST_LDS")
+        row = []
+        if valu and mfma:
+            row.append(f"VALU instructions per MFMA {valu / mfma:.2f}")
+        if conf is not None and lds:
+            row.append(f"LDS bank-conflict cycles per LDS-active cycle {conf / lds:.3f}")
+        if busy and gui:
+            row.append(f"SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE {busy / gui:.1f}")
+        if row:
+            derived.append(f"- `{m}`: " + "; ".join(row))
+    return "\n".join(out) + ("\n\nDerived:\n\n" + "\n".join(derived) if derived else "")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("trace_csv")
     t.add_argument("--command", default="")
+    cn = sub.add_parser("counters")
+    cn.add_argument("dirs", nargs="+")
+    cn.add_argument("--match", action="append", required=True)
+    cn.add_argument("--command", action="append", default=[])
     tr = sub.add_parser("traffic")
     for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "match", "workload", "out"):
         tr.add_argument("--" + a.replace("_", "-"), required=True)
@@ -101,6 +150,11 @@ def main(argv=None):
         if args.command:
             print("Command:\n\n```\n" + args.command + "\n```\n")
         print(trace_table(args.trace_csv))
+        return
+    if args.cmd == "counters":
+        if args.command:
+            print("Commands:\n\n```\n" + "\n".join(args.command) + "\n```\n")
+        print(counter_table(args.dirs, args.match))
         return
     f_kib = pmc_avg(args.fetch, "FETCH_SIZE", args.match)
     w_kib = pmc_avg(args.write, "WRITE_SIZE", args.match)
