@@ -140,7 +140,7 @@ void orc_select(int32_t E, int32_t k, int32_t T, const float *logits, const floa
     free(c);
 }
 
-/* Adaptive expert top-p ([Heart] "使えるかどうかの判定材料" knob list: an
+/* Adaptive expert top-p ([Heart] "速度を稼ぐ実用ノブ" knob list: an
  * adaptive expert top-p, `--topp 0.7`, that reads 30-40% fewer expert bytes;
  * the pages give no formula).  Reading: after the top-k selection above,
  * keep the shortest prefix of the selection order whose routing weights add
