@@ -28,7 +28,8 @@
  * Conventions for every entry point
  *  - Memory: every tensor pointer is DEVICE memory owned by the caller; the
  *    library never allocates or frees device memory, keeps no state between
- *    calls and never synchronises.  Work is enqueued on `hip_stream` (a
+ *    calls (coli_moe_route_forward_noalloc's static scratch array aside) and
+ *    never synchronises.  Work is enqueued on `hip_stream` (a
  *    hipStream_t; NULL = the null stream) and buffers must stay valid until
  *    the caller synchronises that stream.  The layer descriptor itself is
  *    host memory and may be reused or freed when the call returns.
@@ -68,7 +69,9 @@ enum coli_status {
     COLI_E_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned        */
     COLI_E_WORKSPACE = 4,   /* workspace smaller than coli_moe_workspace_bytes */
     COLI_E_DEVICE = 5,      /* a HIP call or kernel launch failed             */
-    COLI_E_UNSUPPORTED = 6  /* current device is not gfx950, or unknown mode  */
+    COLI_E_UNSUPPORTED = 6, /* current device is not gfx950, or unknown mode  */
+    COLI_E_SCRATCH = 7      /* shape needs more scratch than the static array
+                               of coli_moe_route_forward_noalloc holds      */
 };
 
 /* Arithmetic family of the expert matmuls ([Guide] "詳細解説" step 3; the
@@ -264,6 +267,34 @@ int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int
                                     int32_t n_events, void *hip_stream);
 int coli_moe_route_forward_kernel_count(int32_t act_mode, int32_t T);
 const char *coli_moe_route_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
+
+/* coli_moe_route_forward for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same call, arguments and outputs (bit for bit) without the
+ * workspace: its scratch is one static device array of
+ * COLI_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held
+ * from the library's load until the process ends.  The caller still owns x,
+ * the routing and union outputs and y.  Nothing is allocated or freed: the
+ * array's device address is looked up once per device (hipGetSymbolAddress,
+ * on the first call with that device current).
+ *  - Size limit: a shape whose coli_moe_workspace_bytes(H, I, E, k, T,
+ *    act_mode) exceeds COLI_NOALLOC_SCRATCH_BYTES returns COLI_E_SCRATCH
+ *    and enqueues nothing.  On the H 6144 / I 2048 / E 256 / top-8 layer
+ *    this admits up to 113 tokens in the fp32 family and 135 in the int8
+ *    family (decode, verify and small batches).
+ *  - Every call on one GPU shares that GPU's array, and nothing in it must
+ *    start at zero (its contents are scratch, as in coli_moe_route_forward).
+ *    Calls that overlap on one GPU (concurrent streams, or threads without
+ *    ordering between their streams) race on the array: the caller orders
+ *    them, e.g. on one stream.
+ *  - Errors as in coli_moe_route_forward; COLI_E_DEVICE if the symbol lookup
+ *    fails. */
+#define COLI_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int coli_moe_route_forward_noalloc(const coli_moe_layer *L, const float *x, int32_t T,
+                                   float top_p, int32_t *topk_ids, float *topk_w,
+                                   int32_t *union_ids, int32_t *offsets, int32_t *slots,
+                                   int32_t *n_union, int32_t act_mode, float *y,
+                                   void *hip_stream);
 
 /* Number of kernels coli_moe_forward launches for act_mode and a batch of
  * T tokens without acc_dump (0 if the mode is unknown), and the name of the

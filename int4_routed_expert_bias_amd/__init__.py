@@ -17,12 +17,14 @@ LIB_PATH = os.path.join(_HERE, "libcoli_moe.so")
 
 ACT_F32, ACT_I8 = 0, 1
 COLI_OK, COLI_E_ARG, COLI_E_SHAPE, COLI_E_ALIGN, COLI_E_WORKSPACE, COLI_E_DEVICE, \
-    COLI_E_UNSUPPORTED = range(7)
+    COLI_E_UNSUPPORTED, COLI_E_SCRATCH = range(8)
+NOALLOC_SCRATCH_BYTES = 32 << 20  # COLI_NOALLOC_SCRATCH_BYTES
 
 # every symbol declared in include/coli_moe.h
 EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_route_topp", "coli_moe_route_union", "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
            "coli_moe_route_forward", "coli_moe_route_forward_profiled",
+           "coli_moe_route_forward_noalloc",
            "coli_moe_route_forward_kernel_count", "coli_moe_route_forward_kernel_name",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
@@ -78,6 +80,8 @@ def lib():
                                         vp, vp, sz, vp], ctypes.c_int),
             "coli_moe_route_forward_profiled": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
                                                  vp, i32, vp, vp, sz, vp, i32, vp], ctypes.c_int),
+            "coli_moe_route_forward_noalloc": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
+                                                vp, i32, vp, vp], ctypes.c_int),
             "coli_moe_route_forward_kernel_count": ([i32, i32], ctypes.c_int),
             "coli_moe_route_forward_kernel_name": ([i32, i32, i32], ctypes.c_char_p),
             "coli_moe_forward_kernel_count": ([i32, i32], ctypes.c_int),
@@ -208,6 +212,18 @@ def route_forward(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_m
                                         _ptr(union_ids), _ptr(offsets), _ptr(slots), _ptr(n_union),
                                         act_mode, _ptr(y), _ptr(workspace), nb, _stream(stream)),
            "coli_moe_route_forward")
+
+
+def route_forward_noalloc(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y,
+                          top_p=None, stream=None):
+    """coli_moe_route_forward_noalloc: coli_moe_route_forward with the
+    library's static scratch array instead of a workspace (no allocation)."""
+    p = 1.0 if top_p is None else float(top_p)
+    _check(lib().coli_moe_route_forward_noalloc(layer.ref, _ptr(x), T, p, _ptr(ids), _ptr(w),
+                                                _ptr(union_ids), _ptr(offsets), _ptr(slots),
+                                                _ptr(n_union), act_mode, _ptr(y),
+                                                _stream(stream)),
+           "coli_moe_route_forward_noalloc")
 
 
 def route_forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y,

@@ -129,6 +129,9 @@ const char *coli_moe_strerror(int status)
     case COLI_E_WORKSPACE: return "COLI_E_WORKSPACE: workspace too small";
     case COLI_E_DEVICE: return "COLI_E_DEVICE: HIP call or kernel launch failed";
     case COLI_E_UNSUPPORTED: return "COLI_E_UNSUPPORTED: device is not gfx950 or mode unknown";
+    case COLI_E_SCRATCH:
+        return "COLI_E_SCRATCH: shape needs more than the static scratch of the no-allocation "
+               "entry point";
     default: return "unknown coli status";
     }
 }
@@ -290,11 +293,15 @@ static bool route_forward_fused(const coli_moe_layer *L, int32_t T, int32_t act_
     return T >= 1 && T <= 4 && L->E <= 256 && (act_mode == COLI_ACT_F32 || T == 1);
 }
 
+// scratch (the no-allocation entry point): the workspace arguments are
+// ignored; after every host check the call takes its scratch from
+// scratch() (COLI_E_SCRATCH first if the shape needs more than
+// COLI_NOALLOC_SCRATCH_BYTES).
 static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
                               int32_t *topk_ids, float *topk_w, int32_t *union_ids,
                               int32_t *offsets, int32_t *slots, int32_t *n_union, int32_t act_mode,
                               float *y, void *workspace, size_t workspace_bytes, void *hip_stream,
-                              Marks *mk)
+                              Marks *mk, ScratchFn scratch = nullptr)
 {
     if (int st = check_layer(L, true)) return st;
     if (T < 0 || T > COLI_MAX_T) return COLI_E_SHAPE;
@@ -315,14 +322,23 @@ static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T
         if (int s = device_check()) return s;
         return status_of(launch_union(nullptr, 0, L->k, L->E, union_ids, offsets, slots, n_union, st));
     }
-    if (!x || !topk_ids || !topk_w || !slots || !y || !workspace) return COLI_E_ARG;
+    if (!x || !topk_ids || !topk_w || !slots || !y || (!workspace && !scratch)) return COLI_E_ARG;
     if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(slots) ||
-        !aligned16(y) || !aligned16(workspace))
+        !aligned16(y) || (!scratch && !aligned16(workspace)))
         return COLI_E_ALIGN;
     const Workspace lay = workspace_layout(L->H, L->I, L->E, L->k, T, act_mode, L->n_shared);
-    if (workspace_bytes < (fused ? lay.fused_end : std::max(lay.route_end, lay.forward_end)))
+    if (scratch) {
+        if (coli_moe_workspace_bytes(L->H, L->I, L->E, L->k, T, act_mode) >
+            COLI_NOALLOC_SCRATCH_BYTES)
+            return COLI_E_SCRATCH;
+    } else if (workspace_bytes < (fused ? lay.fused_end : std::max(lay.route_end, lay.forward_end))) {
         return COLI_E_WORKSPACE;
+    }
     if (int s = device_check()) return s;
+    if (scratch) {
+        if (int s = scratch(&workspace)) return s;
+        workspace_bytes = COLI_NOALLOC_SCRATCH_BYTES;
+    }
     const LayerDev d = to_dev(L);
     ForwardIO io{};
     io.x = x; io.T = T; io.ids = topk_ids; io.w = topk_w;
@@ -347,6 +363,19 @@ int coli_moe_route_forward(const coli_moe_layer *L, const float *x, int32_t T, f
                               n_union, act_mode, y, workspace, workspace_bytes, hip_stream,
                               nullptr);
 }
+
+}  // extern "C"
+
+int coli::route_forward_scratch(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                                int32_t *topk_ids, float *topk_w, int32_t *union_ids,
+                                int32_t *offsets, int32_t *slots, int32_t *n_union,
+                                int32_t act_mode, float *y, void *hip_stream, ScratchFn scratch)
+{
+    return route_forward_impl(L, x, T, top_p, topk_ids, topk_w, union_ids, offsets, slots,
+                              n_union, act_mode, y, nullptr, 0, hip_stream, nullptr, scratch);
+}
+
+extern "C" {
 
 int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
                                     float top_p, int32_t *topk_ids, float *topk_w,

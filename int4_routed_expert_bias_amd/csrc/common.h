@@ -286,6 +286,15 @@ hipError_t launch_route_forward_small(const LayerDev &L, const ForwardIO &io, in
 hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t st, Marks *mk);
 hipError_t launch_forward_i8_small(const LayerDev &L, const ForwardIO &io, const int8_t *qx,
                                    const float *sx, float *h, float *o, hipStream_t st, Marks *mk);
+// The one-call layer step of coli_moe_route_forward with its scratch from
+// scratch() instead of a caller workspace (coli_moe_route_forward_noalloc):
+// scratch() runs after every host check and returns a COLI_* status and
+// the device address of COLI_NOALLOC_SCRATCH_BYTES of scratch.
+typedef int (*ScratchFn)(void **ws);
+int route_forward_scratch(const coli_moe_layer *L, const float *x, int32_t T, float top_p,
+                          int32_t *topk_ids, float *topk_w, int32_t *union_ids, int32_t *offsets,
+                          int32_t *slots, int32_t *n_union, int32_t act_mode, float *y,
+                          void *hip_stream, ScratchFn scratch);
 hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, int32_t T, int32_t k,
                           int32_t H, int32_t n_shared, float *y, hipStream_t st,
                           Marks *mk = nullptr);

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_strerror(L):
-    for s in range(7):
+    for s in range(8):
         assert coli.strerror(s).startswith("COLI_")
     assert "unknown" in coli.strerror(99)
 
@@ -268,3 +268,23 @@ def test_route_union_argument_errors(L):
     assert ru(layer(), off=MIS) == coli.COLI_E_ALIGN
     assert ru(layer(), x=MIS) == coli.COLI_E_ALIGN
     assert ru(layer(), nb=16) == coli.COLI_E_WORKSPACE
+
+
+def test_route_forward_noalloc_argument_errors(L):
+    """The no-allocation step runs every host check of coli_moe_route_forward
+    and rejects a shape beyond its static scratch before any HIP call."""
+    def rf(lay, T=4, mode=0, p=1.0, x=FAKE, y=FAKE):
+        return L.coli_moe_route_forward_noalloc(
+            ctypes.byref(lay) if lay is not None else None, x, T, ctypes.c_float(p), FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, mode, y, None)
+    assert rf(None) == coli.COLI_E_ARG
+    assert rf(layer(H=100)) == coli.COLI_E_SHAPE
+    assert rf(layer(), mode=2) == coli.COLI_E_UNSUPPORTED
+    assert rf(layer(), p=0.0) == coli.COLI_E_ARG
+    assert rf(layer(), y=0) == coli.COLI_E_ARG
+    assert rf(layer(), x=MIS) == coli.COLI_E_ALIGN
+    big = layer(H=6144, I=2048, E=256, k=8)
+    for mode, t_max in ((0, 113), (1, 135)):
+        assert coli.workspace_bytes(6144, 2048, 256, 8, t_max, mode) <= coli.NOALLOC_SCRATCH_BYTES
+        assert rf(big, T=t_max + 1, mode=mode) == coli.COLI_E_SCRATCH
+        assert rf(big, T=4096, mode=mode) == coli.COLI_E_SCRATCH
