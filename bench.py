@@ -31,10 +31,11 @@ between two synchronisations (wall clock): value = tokens / that time.  The
 dominant kernel's duration comes from HIP events that each kernel's own
 dispatch records at its start and end (coli_moe_route_forward_profiled /
 coli_moe_forward_profiled launch through hipExtLaunchKernel on the library's
-stream), over the same inputs; the same events give the median and p10/p90
-of a layer call, warm and cold (after a 1 GiB write that flushes L2 and the
-Infinity Cache).  The oracle baseline runs single-threaded on one pinned host
-CPU.  Prints one JSON line.
+stream), over the same inputs.  The step time's median and p10/p90 come
+from 50 further replays of the timed graph (warm) and from 64 replays of a
+one-step graph, each after a 1 GiB read of other memory that evicts L2 and
+the Infinity Cache (cold).  The oracle baseline runs single-threaded on one
+pinned host CPU.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -150,6 +151,42 @@ def gpu_clocks():
     except (OSError, subprocess.SubprocessError):
         pass
     return None
+
+
+class ClockSampler:
+    """Samples gpu_clocks() every `period` seconds on a thread while the GPU
+    works, so that the reported clocks are the ones under load."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period, self.samples = period, []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            c = gpu_clocks()
+            if c:
+                self.samples.append(c)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        out = {"samples": len(self.samples), "source": self.samples[0].get("source")}
+        for key in ("sclk", "mclk"):
+            v = [c[key] for c in self.samples if key in c]
+            if v:
+                out[key] = {"median": float(np.median(v)), "min": min(v), "max": max(v)}
+        return out
 
 
 def stream_read_rate(hip, n_bufs=8, nbytes=188 << 20, reps=3):
@@ -314,7 +351,46 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
         g.replay()
         torch.cuda.synchronize()
         t_end = time.perf_counter()
+        # distribution of the step time: more replays of the same graph, each
+        # bracketed by events (per-step time = replay time / K)
+        hip = Hip()
+        reps = 12 if stacked else 50
+        evs = [(hip.event(), hip.event()) for _ in range(reps)]
+        for e0, e1 in evs:
+            hip.record(e0)
+            g.replay()
+            hip.record(e1)
+        torch.cuda.synchronize()
+        step_warm = [hip.elapsed_ms(e0, e1) * 1e3 / K for e0, e1 in evs]
+        for e in evs:
+            hip.destroy(e[0])
+            hip.destroy(e[1])
         del g
+        # cold steps: one step per replay, after a read of 1 GiB of other
+        # memory that evicts L2 and the Infinity Cache without dirtying them
+        g1 = torch.cuda.CUDAGraph()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(g1, stream=cap_stream):
+                step(W if not stacked else 0)
+        torch.cuda.synchronize()
+        sweep = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
+        sweep_out = torch.empty((4096,), dtype=torch.int32, device="cuda")
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        g1.replay()
+        reps = 16 if stacked else 64
+        evs = [(hip.event(), hip.event()) for _ in range(reps)]
+        for e0, e1 in evs:
+            coli.stream_read(sweep, sweep_out, cus)
+            hip.record(e0)
+            g1.replay()
+            hip.record(e1)
+        torch.cuda.synchronize()
+        step_cold = [hip.elapsed_ms(e0, e1) * 1e3 for e0, e1 in evs]
+        for e in evs:
+            hip.destroy(e[0])
+            hip.destroy(e[1])
+        del g1, sweep, sweep_out
     else:
         torch.cuda.synchronize()
         t_start = time.perf_counter()
@@ -322,68 +398,55 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
             step(W + s if not stacked else s)
         torch.cuda.synchronize()
         t_end = time.perf_counter()
+        step_warm = step_cold = None
     elapsed = t_end - t_start
     layer_passes = K * (w.layers if stacked else 1)
     value = layer_passes * T / elapsed
     ms_per_step = elapsed * 1e3 / K
 
-    # ---- per-kernel and per-layer-call times: dispatch-recorded events ------
+    # ---- per-kernel times: dispatch-recorded events ------------------------
     hip = Hip()
     names = coli.route_forward_kernel_names(mode, T) if one_call else coli.forward_kernel_names(mode, T)
     nk = len(names)
     dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
-    flush = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")  # 1 GiB
     if prof_steps is None:
         prof_steps = 8 if stacked else 64
     union_sizes = []
-    per_kernel = np.zeros(nk)
-    calls = {"warm": [], "cold": []}
-    for phase in ("warm", "cold"):
-        # per layer call: 2 marks per kernel, then one event recorded on the
-        # stream just before the call (the start of its routing launches)
-        ev = [[hip.event() for _ in range(2 * nk + 1)] for _ in range(prof_steps * (w.layers if stacked else 1))]
-        torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
-        i = 0
-        for s in range(prof_steps):
+    ev = [[hip.event() for _ in range(2 * nk)] for _ in range(prof_steps * (w.layers if stacked else 1))]
+    torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
+    i = 0
+    for s in range(prof_steps):
+        if stacked:
+            resid.copy_(xs[0])
+            lays = devl
+        else:
+            lays = [devl[(W + s) % NL]]
+        for lay in lays:
+            x_in = xs[(W + s) % len(xs)] if not stacked else xhat
             if stacked:
-                resid.copy_(xs[0])
-                lays = devl
+                coli.rmsnorm(resid, xhat, T, H, 1e-6)
+            if one_call:
+                coli.route_forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
+                                            bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
+                                            bufs.workspace, ev[i], top_p=topp)
             else:
-                lays = [devl[(W + s) % NL]]
-            for lay in lays:
-                x_in = xs[(W + s) % len(xs)] if not stacked else xhat
-                if stacked:
-                    coli.rmsnorm(resid, xhat, T, H, 1e-6)
-                if phase == "cold":
-                    flush.zero_()  # evicts the L2 and Infinity Cache contents
-                hip.record(ev[i][2 * nk])
-                if one_call:
-                    coli.route_forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
-                                                bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
-                                                bufs.workspace, ev[i][:2 * nk], top_p=topp)
-                else:
-                    coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
-                                     bufs.slots, bufs.n_union, bufs.workspace, top_p=topp)
-                    coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
-                                          bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
-                                          bufs.workspace, ev[i][:2 * nk])
-                if phase == "warm":
-                    union_sizes.append(bufs.n_union[:1].clone())
-                if stacked:
-                    coli.add_inplace(resid, bufs.y, T * H)
-                i += 1
-        torch.cuda.synchronize()
-        for e in ev:
-            # one layer call: from the event before it to its last kernel's end
-            calls[phase].append(hip.elapsed_ms(e[2 * nk], e[2 * nk - 1]) * 1e3)
-            if phase == "warm":
-                for j in range(nk):
-                    per_kernel[j] += hip.elapsed_ms(e[2 * j], e[2 * j + 1])
-            for x_ in e:
-                hip.destroy(x_)
-        if phase == "warm":
-            per_kernel /= len(ev)
-    del flush
+                coli.route_union(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids, bufs.offsets,
+                                 bufs.slots, bufs.n_union, bufs.workspace, top_p=topp)
+                coli.forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
+                                      bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
+                                      bufs.workspace, ev[i])
+            union_sizes.append(bufs.n_union[:1].clone())
+            if stacked:
+                coli.add_inplace(resid, bufs.y, T * H)
+            i += 1
+    torch.cuda.synchronize()
+    per_kernel = np.zeros(nk)
+    for e in ev:
+        for j in range(nk):
+            per_kernel[j] += hip.elapsed_ms(e[2 * j], e[2 * j + 1])
+        for x_ in e:
+            hip.destroy(x_)
+    per_kernel /= len(ev)
     U = np.array([int(u.item()) for u in union_sizes])
     dur_s = per_kernel[dom] * 1e-3
     n_exp = U.mean() + w.n_shared
@@ -436,9 +499,11 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
                    "graph": use_graph, "union_size_mean": round(float(U.mean()), 2),
                    "union_size_minmax": [int(U.min()), int(U.max())],
                    "kernels_us": kernels_us},
-        # per layer call (route + union + forward), eager with the queue kept
-        # full; cold: after a 1 GiB write that flushes L2 and Infinity Cache
-        "layer_call_us": {"warm": percentiles(calls["warm"]), "cold": percentiles(calls["cold"])},
+        # step time (us): warm = graph replays of the K timed steps (replay
+        # time / K); cold = single-step graph replays, each after a 1 GiB read
+        # of other memory (evicts L2 and Infinity Cache), graph launch included
+        "step_us": ({"warm": percentiles(step_warm), "cold": percentiles(step_cold)}
+                    if step_warm is not None else None),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -511,14 +576,20 @@ def main():
         return bench_placed(args, w, coli.ACT_I8 if fam == "i8" else coli.ACT_F32)
     K = args.steps if args.steps is not None else DEFAULT_STEPS[name][0]
     W = args.warmup if args.warmup is not None else DEFAULT_STEPS[name][1]
-    head = bench_resident(name, K, W, act_mode=args.act_mode, topp=args.topp, layers=args.layers,
-                          use_graph=not args.no_graph, cpu_seconds=args.cpu_seconds,
-                          with_cpu=not args.no_cpu_baseline, prof_steps=args.prof_steps)
-    clocks = gpu_clocks()
+    with ClockSampler() as clk:
+        head = bench_resident(name, K, W, act_mode=args.act_mode, topp=args.topp,
+                              layers=args.layers, use_graph=not args.no_graph,
+                              cpu_seconds=0.0, with_cpu=False, prof_steps=args.prof_steps)
+    if not args.no_cpu_baseline:  # after the GPU work, outside the clock sampling
+        import synth as _s
+        hw = _s.WORKLOADS[name]
+        head["cpu_baseline"] = oracle_baseline(hw, _s.workload_layer(hw, layer=0),
+                                               coli.ACT_I8 if head["dtype"] == "i8" else coli.ACT_F32,
+                                               args.topp, args.cpu_seconds)
     out = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
            "steps": K, "warmup": W, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic"}
-    for key in ("config", "layer_call_us", "roofline", "cpu_baseline"):
+    for key in ("config", "step_us", "roofline", "cpu_baseline"):
         out[key] = head[key]
     if args.workload is None:
         # the other workloads of the metric, each with its own default steps
@@ -532,7 +603,8 @@ def main():
                 f"{r['roofline']['kernel_us']} us = {r['roofline']['frac']:.3f} of its roofline")
         out["workloads"] = extra
         out["hbm_read_ceiling"] = stream_read_rate(Hip())
-    out["clocks_mhz"] = clocks
+    # clocks sampled every 20 ms while the headline workload ran on the GPU
+    out["clocks_mhz"] = clk.summary()
     out["host"] = host_info()
     print(json.dumps(out), flush=True)
 
