@@ -270,8 +270,81 @@ def oracle_baseline(w, host0, mode, topp, cpu_seconds):
                       f"pinned to one CPU)"}
 
 
+TL_CAP = 8192      # waves recorded per kernel by the timeline entry point
+TL_TICK_US = 0.01  # the real-time counter runs at 100 MHz
+
+
+def timeline_summary(rec, names, per_kernel_us):
+    """Markdown summary of per-wave timeline marks rec[step, kernel, wave,
+    mark] (counter ticks, 0 = not reached): per kernel, the spread of wave
+    entries and exits relative to the step's first wave entry, each wave's
+    time to its marks, and the gap to the previous kernel; medians over the
+    steps."""
+    steps, nk = rec.shape[0], rec.shape[1]
+    rows = {}
+    for s in range(steps):
+        base = None
+        for i in range(nk):
+            m0 = rec[s, i, :, 0]
+            if (m0 > 0).any():
+                b = m0[m0 > 0].min()
+                base = b if base is None else min(base, b)
+        prev_exit = None
+        for i in range(nk):
+            r = rec[s, i].astype(np.int64)
+            live = r[:, 0] > 0
+            if not live.any():
+                continue
+            e0 = (r[live, 0] - base) * TL_TICK_US
+            ex = r[live, 7]
+            ex = (ex[ex > 0] - base) * TL_TICK_US
+            d = rows.setdefault(i, {})
+            d.setdefault("waves", []).append(int(live.sum()))
+            # most waves of the kernel resident at once (entry +1, exit -1)
+            done = r[live, 7] > 0
+            ev = np.concatenate([np.stack([r[live, 0][done], np.ones(done.sum(), np.int64)], 1),
+                                 np.stack([r[live, 7][done], -np.ones(done.sum(), np.int64)], 1)])
+            ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]
+            d.setdefault("peak", []).append(int(np.cumsum(ev[:, 1]).max()) if len(ev) else 0)
+            d.setdefault("entry_first", []).append(e0.min())
+            d.setdefault("entry_med", []).append(np.median(e0))
+            d.setdefault("entry_last", []).append(e0.max())
+            if len(ex):
+                d.setdefault("exit_first", []).append(ex.min())
+                d.setdefault("exit_med", []).append(np.median(ex))
+                d.setdefault("exit_last", []).append(ex.max())
+            if prev_exit is not None:
+                d.setdefault("gap", []).append(e0.min() - prev_exit)
+            if len(ex):
+                prev_exit = ex.max()
+            for j in (1, 2, 3, 4, 5, 6):
+                mj = r[live, j]
+                ok = mj > 0
+                if ok.any():
+                    dt = (mj[ok] - r[live, 0][ok]) * TL_TICK_US
+                    d.setdefault(f"m{j}_med", []).append(np.median(dt))
+                    d.setdefault(f"m{j}_max", []).append(dt.max())
+    med = lambda v: f"{np.median(v):.2f}" if v else "-"
+    marks = [j for j in (1, 2, 3, 4, 5, 6) if any(f"m{j}_med" in d for d in rows.values())]
+    out = ["| kernel | event us | waves | most resident at once | gap after previous | "
+           "entries first / median / last | "
+           "exits first / median / last | " + " | ".join(f"wave to mark {j} (median / max)" for j in marks) + " |",
+           "|---|---|---|---|---|---|---|" + "---|" * len(marks)]
+    for i in range(nk):
+        d = rows.get(i)
+        if not d:
+            continue
+        out.append(f"| `{names[i]}` | {per_kernel_us[i]:.2f} | {int(np.median(d['waves']))} | "
+                   f"{int(np.median(d['peak']))} | "
+                   f"{med(d.get('gap'))} | {med(d['entry_first'])} / {med(d['entry_med'])} / "
+                   f"{med(d['entry_last'])} | {med(d.get('exit_first'))} / {med(d.get('exit_med'))} / "
+                   f"{med(d.get('exit_last'))} | " +
+                   " | ".join(f"{med(d.get(f'm{j}_med'))} / {med(d.get(f'm{j}_max'))}" for j in marks) + " |")
+    return "\n".join(out)
+
+
 def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_graph=True,
-                   cpu_seconds=12.0, with_cpu=True, prof_steps=None):
+                   cpu_seconds=12.0, with_cpu=True, prof_steps=None, timeline=None):
     """One resident-layer workload: K graph-replayed steps after W warmup
     steps, then the per-kernel and per-step times from dispatch-recorded
     events (warm, and cold after a 1 GiB write that flushes the caches), the
@@ -489,6 +562,32 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
         roof["int8_tops_of_kernel"] = round(algo_ops / dur_s / 1e12, 2)
     kernels_us = {names[j]: round(per_kernel[j] * 1e3, 2) for j in range(nk)}
 
+    if timeline:
+        # per-wave phase marks of the same kernels (coli_moe_route_forward_timeline)
+        if not (one_call and mode == coli.ACT_F32 and not stacked):
+            raise SystemExit("--timeline: the self-routing fp32 workloads (decode, verify) only")
+        n_tl = 32
+        rec = torch.zeros((n_tl, nk, TL_CAP, 8), dtype=torch.int64, device="cuda")
+        torch.cuda._sleep(200_000_000)
+        for s in range(n_tl):
+            lay = devl[(W + s) % NL]
+            coli.route_forward_timeline(lay, xs[(W + s) % len(xs)], T, bufs.ids, bufs.w,
+                                        bufs.union_ids, bufs.offsets, bufs.slots, bufs.n_union,
+                                        mode, bufs.y, bufs.workspace, rec[s], TL_CAP, top_p=topp)
+        torch.cuda.synchronize()
+        table = timeline_summary(rec.cpu().numpy(), names, [per_kernel[j] * 1e3 for j in range(nk)])
+        with open(timeline, "w") as fp:
+            fp.write(f"# Timeline of the {w.name} step ({n_tl} eager steps, one layer call each)\n\n"
+                     "Times in us from the step's first wave entry; medians over the steps.  "
+                     "'event us' is the kernel's dispatch-event duration from the same run.  "
+                     "Marks (coli_moe_route_forward_timeline): self-routing gate/up 1 routing done, "
+                     "2 activations staged, 3 first reduction batch written, 4 router keys loaded, "
+                     "5 top-k threshold found, 6 selection and union written; fused down + combine "
+                     "1 first entry's rows done, 2 / 3 before / after the workgroup barrier.\n\n")
+            fp.write(table + "\n")
+        log(table)
+        del rec
+
     cpu = oracle_baseline(w, host0, mode, topp, cpu_seconds) if with_cpu else None
     res = {
         "value": round(value, 2), "unit": "tokens/s", "steps": K, "warmup": W,
@@ -532,6 +631,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--prof-steps", type=int, default=None,
                     help="event-timed steps per phase (default 64; 8 for the 8-layer stack)")
+    ap.add_argument("--timeline", default=None, metavar="PATH",
+                    help="decode/verify: also write per-wave kernel phase marks "
+                         "(coli_moe_route_forward_timeline), summarised as markdown, to PATH")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (the reference for HBM counters)")
     ap.add_argument("--place-slots", type=int, default=None,
@@ -579,7 +681,8 @@ def main():
     with ClockSampler() as clk:
         head = bench_resident(name, K, W, act_mode=args.act_mode, topp=args.topp,
                               layers=args.layers, use_graph=not args.no_graph,
-                              cpu_seconds=0.0, with_cpu=False, prof_steps=args.prof_steps)
+                              cpu_seconds=0.0, with_cpu=False, prof_steps=args.prof_steps,
+                              timeline=args.timeline)
     if not args.no_cpu_baseline:  # after the GPU work, outside the clock sampling
         import synth as _s
         hw = _s.WORKLOADS[name]

@@ -268,6 +268,26 @@ int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int
 int coli_moe_route_forward_kernel_count(int32_t act_mode, int32_t T);
 const char *coli_moe_route_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i);
 
+/* coli_moe_route_forward for the self-routing fp32 family (T <= 4; else
+ * COLI_E_UNSUPPORTED, nothing enqueued), where the waves of its kernels also
+ * write a timeline: timeline is device memory of
+ * coli_moe_route_forward_kernel_count(act_mode, T) * waves_cap * 8 uint64_t,
+ * zeroed by the caller; wave w (its workgroup index times the waves per
+ * workgroup plus its wave index, recorded for w < waves_cap) of kernel i
+ * writes mark j to timeline[(i * waves_cap + w) * 8 + j]: the chip's
+ * 100 MHz real-time counter (s_memrealtime) at the kernel's points j:
+ * 0 entry, 7 exit; the self-routing gate/up kernels 1 routing done, 2
+ * activations staged, 3 first reduction batch written; the fused down +
+ * combine 1 first entry's rows done, 2 / 3 before / after the workgroup
+ * barrier.  Marks a kernel does not reach stay 0.  waves_cap >= 1.  The
+ * outputs are those of coli_moe_route_forward.  For measurement only. */
+int coli_moe_route_forward_timeline(const coli_moe_layer *L, const float *x, int32_t T,
+                                    float top_p, int32_t *topk_ids, float *topk_w,
+                                    int32_t *union_ids, int32_t *offsets, int32_t *slots,
+                                    int32_t *n_union, int32_t act_mode, float *y,
+                                    void *workspace, size_t workspace_bytes, uint64_t *timeline,
+                                    int32_t waves_cap, void *hip_stream);
+
 /* coli_moe_route_forward for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  The same call, arguments and outputs (bit for bit) without the

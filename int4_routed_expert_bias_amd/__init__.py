@@ -24,7 +24,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # COLI_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_route_topp", "coli_moe_route_union", "coli_moe_union", "coli_moe_forward", "coli_moe_forward_profiled",
            "coli_moe_route_forward", "coli_moe_route_forward_profiled",
-           "coli_moe_route_forward_noalloc",
+           "coli_moe_route_forward_noalloc", "coli_moe_route_forward_timeline",
            "coli_moe_route_forward_kernel_count", "coli_moe_route_forward_kernel_name",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
@@ -79,6 +79,8 @@ def lib():
             "coli_moe_route_forward": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, i32,
                                         vp, vp, sz, vp], ctypes.c_int),
             "coli_moe_route_forward_profiled": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
+                                                 vp, i32, vp, vp, sz, vp, i32, vp], ctypes.c_int),
+            "coli_moe_route_forward_timeline": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
                                                  vp, i32, vp, vp, sz, vp, i32, vp], ctypes.c_int),
             "coli_moe_route_forward_noalloc": ([vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
                                                 vp, i32, vp, vp], ctypes.c_int),
@@ -237,6 +239,22 @@ def route_forward_profiled(layer, x, T, ids, w, union_ids, offsets, slots, n_uni
                                                  _ptr(n_union), act_mode, _ptr(y), _ptr(workspace),
                                                  nb, arr, len(events), _stream(stream)),
            "coli_moe_route_forward_profiled")
+
+
+def route_forward_timeline(layer, x, T, ids, w, union_ids, offsets, slots, n_union, act_mode, y,
+                           workspace, timeline, waves_cap, top_p=None, stream=None):
+    """coli_moe_route_forward (self-routing fp32 case) writing per-wave
+    timeline marks into ``timeline`` (uint64/int64 device tensor of
+    kernels x waves_cap x 8, zeroed by the caller)."""
+    nb = workspace.numel() * workspace.element_size()
+    p = 1.0 if top_p is None else float(top_p)
+    if timeline.numel() < len(route_forward_kernel_names(act_mode, T)) * waves_cap * 8:
+        raise ValueError("timeline holds fewer than kernels x waves_cap x 8 marks")
+    _check(lib().coli_moe_route_forward_timeline(layer.ref, _ptr(x), T, p, _ptr(ids), _ptr(w),
+                                                 _ptr(union_ids), _ptr(offsets), _ptr(slots),
+                                                 _ptr(n_union), act_mode, _ptr(y), _ptr(workspace),
+                                                 nb, _ptr(timeline), waves_cap, _stream(stream)),
+           "coli_moe_route_forward_timeline")
 
 
 def route_forward_kernel_names(act_mode, T=1):

@@ -310,10 +310,15 @@ static int route_forward_impl(const coli_moe_layer *L, const float *x, int32_t T
     const bool fused = route_forward_fused(L, T, act_mode);
     if (mk) {
         if (!fused) return COLI_E_UNSUPPORTED;
-        const int need = 2 * route_forward_kernels(act_mode, T);
-        if (!mk->ev || mk->n < need) return COLI_E_ARG;
-        for (int i = 0; i < need; ++i)
-            if (!mk->ev[i]) return COLI_E_ARG;
+        if (mk->tl) {  // timeline: the fp32 family's kernels write it
+            if (act_mode != COLI_ACT_F32) return COLI_E_UNSUPPORTED;
+            if (mk->tl_cap < 1 || ((uintptr_t)mk->tl & 7u)) return COLI_E_ARG;
+        } else {
+            const int need = 2 * route_forward_kernels(act_mode, T);
+            if (!mk->ev || mk->n < need) return COLI_E_ARG;
+            for (int i = 0; i < need; ++i)
+                if (!mk->ev[i]) return COLI_E_ARG;
+        }
     }
     if (!n_union || !union_ids || !offsets) return COLI_E_ARG;
     if (!aligned16(union_ids) || !aligned16(offsets) || !aligned16(n_union)) return COLI_E_ALIGN;
@@ -388,6 +393,21 @@ int coli_moe_route_forward_profiled(const coli_moe_layer *L, const float *x, int
     Marks mk;
     mk.ev = events;
     mk.n = n_events;
+    return route_forward_impl(L, x, T, top_p, topk_ids, topk_w, union_ids, offsets, slots,
+                              n_union, act_mode, y, workspace, workspace_bytes, hip_stream, &mk);
+}
+
+int coli_moe_route_forward_timeline(const coli_moe_layer *L, const float *x, int32_t T,
+                                    float top_p, int32_t *topk_ids, float *topk_w,
+                                    int32_t *union_ids, int32_t *offsets, int32_t *slots,
+                                    int32_t *n_union, int32_t act_mode, float *y,
+                                    void *workspace, size_t workspace_bytes, uint64_t *timeline,
+                                    int32_t waves_cap, void *hip_stream)
+{
+    if (!timeline || waves_cap < 1) return COLI_E_ARG;
+    Marks mk;
+    mk.tl = timeline;
+    mk.tl_cap = waves_cap;
     return route_forward_impl(L, x, T, top_p, topk_ids, topk_w, union_ids, offsets, slots,
                               n_union, act_mode, y, workspace, workspace_bytes, hip_stream, &mk);
 }

@@ -178,10 +178,16 @@ inline DumpLayout dump_layout(int64_t H, int64_t I, int64_t k, int64_t T, int64_
 // Optional profiling marks: caller-created events, two per kernel of a call
 // (ev[2i], ev[2i + 1]), set to the start and the end of kernel i by its own
 // dispatch (hipExtLaunchKernel), i.e. the durations a kernel trace reports.
+// Optional timeline (coli_moe_route_forward_timeline): per kernel of the
+// call, 8 real-time-counter marks per wave (see tl_mark).
 struct Marks {
     void **ev = nullptr;
     int n = 0;  // events available
     int i = 0;  // kernels launched so far
+    uint64_t *tl = nullptr;
+    int tl_cap = 0;  // waves recorded per kernel
+    // timeline records of the kernel launched next (null: none)
+    uint64_t *tl_next() const { return tl ? tl + (size_t)i * tl_cap * 8 : nullptr; }
     bool next(hipEvent_t &start, hipEvent_t &end)
     {
         const int j = 2 * i++;

@@ -54,6 +54,8 @@ struct GemvArgs {
     int out_ld;
     const int32_t *union_ids, *offsets, *slots, *n_union;
     int T, k, cap, n_shared;
+    uint64_t *tl;          // timeline marks (measurement only; null: none)
+    int tl_cap;
 };
 
 // U9 selects the units of a kernel's chains: 2^-9 (codes converted in pairs
@@ -546,7 +548,7 @@ __device__ __forceinline__ void t1_entry(const GemvArgs &a, int ue, int U, const
 // the union to global memory (for the down kernel and the caller).  The
 // selection costs each workgroup a few microseconds before its first weight
 // load, against a whole launch of the top-k kernel.  E <= 256.
-template <int P, int NP, int M, int DEPTH, bool XREG, bool ROUTE>
+template <int P, int NP, int M, int DEPTH, bool XREG, bool ROUTE, bool TL = false>
 __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
@@ -558,6 +560,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
+    tl_mark<TL>(a.tl, a.tl_cap, 0);
     int U;
     // ROUTE: x is loaded into registers before the selection (its latency
     // overlaps the selection's) and staged to LDS after it
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
     }
     if constexpr (ROUTE) {
         __shared__ RouteLds rl;
-        route_self(r, rl);
+        route_self<TL>(r, rl, a.tl, a.tl_cap);
         const int nu = rl.n[0];
         a.union_ids = rl.u;
         a.offsets = rl.off;
@@ -583,6 +586,7 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
     } else {
         U = a.n_union[0];
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 1);
     const int upe = a.I / NP;
     const T1Split sp = t1_split(blockIdx.x * 4 + wave, gridDim.x * 4, U + a.n_shared, upe);
     const int nsteps = sp.nsteps;
@@ -648,7 +652,11 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
         }
         __syncthreads();
     }
-    if (nsteps == 0) return;
+    tl_mark<TL>(a.tl, a.tl_cap, 2);
+    if (nsteps == 0) {
+        tl_mark<TL>(a.tl, a.tl_cap, 7);
+        return;
+    }
     float *hrow = a.out + (size_t)orow * a.out_ld;
     float xr[XREG ? P : 1][32], kx[P];
 #pragma unroll
@@ -702,7 +710,9 @@ __global__ __launch_bounds__(256) void gateup_t1_kernel(GemvArgs a, RouteSelf r)
             if (value_writer<V>(j, lane) && vi < NP * M && g0 + m < nsteps)
                 hrow[ht_pos(i, CI)] = swiglu(racc[j], up);
         }
+        if (g0 == 0) tl_mark<TL>(a.tl, a.tl_cap, 3);
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 7);
 }
 
 // Rows of one workgroup of the fused down + combine (at most), and its
@@ -803,7 +813,7 @@ __global__ __launch_bounds__(256) void down_t1_kernel(GemvArgs a)
 // combine's arithmetic (slots in order, fp32 fma chain, dropped slots
 // skipped, then the shared expert added), so y is bitwise that of the
 // two-launch form.
-template <int P, int RD, int M, int DEPTH>
+template <int P, int RD, int M, int DEPTH, bool TL = false>
 // (one chunk per lane: registers for five waves per SIMD, two workgroups per
 // CU -- 16.4 us against 17.5 with four waves per SIMD; wider rows keep the
 // registers they need)
@@ -815,6 +825,7 @@ __global__ __launch_bounds__(64 * kDownT1cWaves, P == 1 ? 5 : 1) void down_t1c_k
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int NW = blockDim.x >> 6;
+    tl_mark<TL>(a.tl, a.tl_cap, 0);
     const int U = a.n_union[0];
     const int nblocks = a.N / RD, G = gridDim.x, g = blockIdx.x;
     T1Split sp;
@@ -824,8 +835,11 @@ __global__ __launch_bounds__(64 * kDownT1cWaves, P == 1 ? 5 : 1) void down_t1c_k
     for (int ue = wave; ue < U + a.n_shared && sp.nsteps > 0; ue += NW) {
         sp.ue = ue;
         down_t1_rows<P, RD, M, DEPTH>(a, sp, U, lane, so);
+        if (ue == wave) tl_mark<TL>(a.tl, a.tl_cap, 1);
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 2);
     __syncthreads();
+    tl_mark<TL>(a.tl, a.tl_cap, 3);
     const int k = a.k, i = threadIdx.x;
     if (i < sp.nsteps * RD) {
         float acc = 0.f;
@@ -836,6 +850,7 @@ __global__ __launch_bounds__(64 * kDownT1cWaves, P == 1 ? 5 : 1) void down_t1c_k
         if (a.n_shared) acc += so[k][i];
         y[(g + (i / RD) * G) * RD + i % RD] = acc;
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 7);
 }
 
 // Small batches (2 <= T <= kStreamTMax, the verify step): the same streams,
@@ -932,7 +947,7 @@ __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, i
 
 // ROUTE: the tokens route themselves first (route_self, as the
 // single-token kernel), and the union is read from LDS.
-template <int P, int M, int DEPTH, int NTOK, int WPB, bool ROUTE>
+template <int P, int M, int DEPTH, int NTOK, int WPB, bool ROUTE, bool TL = false>
 __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
@@ -945,10 +960,11 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
+    tl_mark<TL>(a.tl, a.tl_cap, 0);
     int U;
     if constexpr (ROUTE) {
         __shared__ RouteLds rl;
-        route_self(r, rl);
+        route_self<TL>(r, rl, a.tl, a.tl_cap);
         a.union_ids = rl.u;
         a.offsets = rl.off;
         a.slots = rl.sl;
@@ -957,6 +973,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
     } else {
         U = a.n_union[0];
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 1);
     const T1Split sp = mt_split<ROUTE>(a, blockIdx.x * WPB + wave, gridDim.x * WPB, U, a.I);
     const int nsteps = sp.nsteps;
     const uint8_t *wb;
@@ -1012,7 +1029,11 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
         }
         __syncthreads();
     }
-    if (nsteps == 0 || cnt <= 0) return;
+    tl_mark<TL>(a.tl, a.tl_cap, 2);
+    if (nsteps == 0 || cnt <= 0) {
+        tl_mark<TL>(a.tl, a.tl_cap, 7);
+        return;
+    }
     int tok[NTOK], orow[NTOK];
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
@@ -1092,10 +1113,12 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
             if (value_writer<V>(jj, lane) && vi < NTOK * M && j < cnt && g0 + m < nsteps)
                 a.out[(size_t)orow[j] * a.out_ld + ht_pos(i, CI)] = swiglu(racc[jj], up);
         }
+        if (g0 == 0) tl_mark<TL>(a.tl, a.tl_cap, 3);
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 7);
 }
 
-template <int P, int RD, int M, int DEPTH, int NTOK>
+template <int P, int RD, int M, int DEPTH, int NTOK, bool TL = false>
 __global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
@@ -1104,15 +1127,22 @@ __global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32;
+    tl_mark<TL>(a.tl, a.tl_cap, 0);
     const int U = a.n_union[0];
     const T1Split sp = mt_split(a, blockIdx.x * 4 + wave, gridDim.x * 4, U, a.N / RD);
     const int nsteps = sp.nsteps;
-    if (nsteps == 0) return;
+    if (nsteps == 0) {
+        tl_mark<TL>(a.tl, a.tl_cap, 7);
+        return;
+    }
     const uint8_t *wb;
     const uint16_t *sb;
     const int32_t *list;
     const int cnt = min(entry_info(a, sp.ue, wb, sb, list), NTOK);
-    if (cnt <= 0) return;
+    if (cnt <= 0) {
+        tl_mark<TL>(a.tl, a.tl_cap, 7);
+        return;
+    }
     const StageRsrc R = stage_rsrc(wb, sb, a.N, rb, sbs);
     uint32_t vw[P], vs[P];
     lane_offsets<P>(lane, C, vw, vs);
@@ -1198,6 +1228,7 @@ __global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
                     racc[jj];
         }
     }
+    tl_mark<TL>(a.tl, a.tl_cap, 7);
 }
 
 template <int NTOK>
@@ -1206,7 +1237,9 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
+    a.tl_cap = mk ? mk->tl_cap : 0;
     {
+        a.tl = mk ? mk->tl_next() : nullptr;
         // one 4-wave workgroup per CU (eight waves measured slower: more
         // concurrent streams lose DRAM locality); reductions over M = 2
         // stages (M = 4 measured 6% slower: twice the code per token count
@@ -1221,7 +1254,8 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         const size_t lds = (size_t)io.T * (L.H + L.H / 32) * 4;
 #define COLI_GUM(P_) \
         if (P == P_) { \
-            if (rt) launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB, true>), grid, block, lds, st, a, *rt); \
+            if (rt && a.tl) launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB, true, true>), grid, block, lds, st, a, *rt); \
+            else if (rt) launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB, true>), grid, block, lds, st, a, *rt); \
             else launch(mk, (gateup_mt_kernel<P_, M, DEPTH, NTOK, WPB, false>), grid, block, lds, st, a, \
                         RouteSelf{}); \
         }
@@ -1232,6 +1266,7 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
     }
     {
         constexpr int RD = 4, M = (NTOK >= 4 ? 2 : 4), DEPTH = 2;
+        a.tl = mk ? mk->tl_next() : nullptr;
         a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
         a.N = L.H; a.K = L.I; a.upe = L.H;
         a.in = h; a.in_by_slot = 1;
@@ -1239,7 +1274,10 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         const int P = (L.I / 32 + 63) / 64;
         const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
 #define COLI_DNM(P_) \
-        if (P == P_) launch(mk, (down_mt_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, 0, st, a);
+        if (P == P_) { \
+            if (a.tl) launch(mk, (down_mt_kernel<P_, RD, M, DEPTH, NTOK, true>), grid, block, 0, st, a); \
+            else launch(mk, (down_mt_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, 0, st, a); \
+        }
         COLI_DNM(1) COLI_DNM(2) COLI_DNM(3) COLI_DNM(4)
 #undef COLI_DNM
         hipError_t err = hipGetLastError();
@@ -1277,7 +1315,9 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
 {
     const int entries = a.cap + a.n_shared;
     const int cus = device_cu_count();
+    a.tl_cap = mk ? mk->tl_cap : 0;
     {
+        a.tl = mk ? mk->tl_next() : nullptr;
         constexpr int NP = 1, M = 8, DEPTH = 2;
         a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
         a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
@@ -1289,7 +1329,8 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         const size_t lds = (size_t)(L.H + L.H / 32) * 4;
 #define COLI_GU1(P_) \
         if (P == P_) { \
-            if (rt) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, true>), grid, block, lds, st, a, *rt); \
+            if (rt && a.tl) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, true, true>), grid, block, lds, st, a, *rt); \
+            else if (rt) launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, true>), grid, block, lds, st, a, *rt); \
             else launch(mk, (gateup_t1_kernel<P_, NP, M, DEPTH, true, false>), grid, block, lds, st, a, \
                         RouteSelf{}); \
         }
@@ -1304,6 +1345,7 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
         a.N = L.H; a.K = L.I; a.upe = L.H;
         a.in = h; a.in_by_slot = 1;
         a.out = o; a.out_ld = L.H;
+        a.tl = mk ? mk->tl_next() : nullptr;
         const int P = (L.I / 32 + 63) / 64;
         if (io.combine) {
             // (2 rows per stage and reductions over 2 stages: 16.4 us, against
@@ -1320,7 +1362,9 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
                 const int per_cu = resident_blocks(reinterpret_cast<const void *>(kern), P_, NW); \
                 const int G = std::min(nblocks, std::max(per_cu * cus, \
                                                          (nblocks * RD + kDownRowsMax - 1) / kDownRowsMax)); \
-                launch(mk, kern, dim3(G), block, 0, st, a, io.ids, io.w, io.y); \
+                if (a.tl) launch(mk, (down_t1c_kernel<P_, RD, M, DEPTH, true>), dim3(G), block, 0, st, a, \
+                                 io.ids, io.w, io.y); \
+                else launch(mk, kern, dim3(G), block, 0, st, a, io.ids, io.w, io.y); \
             }
             COLI_DN1C(1) COLI_DN1C(2) COLI_DN1C(3) COLI_DN1C(4)
 #undef COLI_DN1C

@@ -25,12 +25,14 @@ namespace coli {
 // accumulated in ascending column order per lane, as in a plain loop.
 constexpr int kGemvCols = COLI_MAX_H_DEV / 4 / 4 / 64;  // float4 columns per lane, at most
 
-template <int NT>
+template <int NT, bool TL = false>
 __global__ __launch_bounds__(256) void logits_gemv_kernel(const float *__restrict__ x,
                                                           const float *__restrict__ Wr,
                                                           int T, int H, int E,
-                                                          float *__restrict__ logits)
+                                                          float *__restrict__ logits,
+                                                          uint64_t *tl, int tl_cap)
 {
+    tl_mark<TL>(tl, tl_cap, 0);
     const int e = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __shared__ double part[4][NT];
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(256) void logits_gemv_kernel(const float *__restric
         double s = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
         logits[(size_t)t * E + e] = sigmoid_fp64((float)s);
     }
+    tl_mark<TL>(tl, tl_cap, 7);
 }
 
 // --- large T: fp64 MFMA GEMM, split over K -------------------------------
@@ -197,10 +200,16 @@ hipError_t launch_scores(const LayerDev &L, const float *x, int32_t T, float *sc
                          hipStream_t st, Marks *mk)
 {
     const dim3 grid(L.E), block(256);
-    if (T <= 1) launch(mk, logits_gemv_kernel<1>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
-    else if (T <= 2) launch(mk, logits_gemv_kernel<2>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
-    else if (T <= 4) launch(mk, logits_gemv_kernel<4>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
-    else launch(mk, logits_gemv_kernel<8>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores);
+    uint64_t *tl = mk ? mk->tl_next() : nullptr;
+    const int cap = mk ? mk->tl_cap : 0;
+#define COLI_SC(NT_) \
+    (tl ? launch(mk, logits_gemv_kernel<NT_, true>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores, tl, cap) \
+        : launch(mk, logits_gemv_kernel<NT_, false>, grid, block, 0, st, x, L.router_w, T, L.H, L.E, scores, tl, cap))
+    if (T <= 1) COLI_SC(1);
+    else if (T <= 2) COLI_SC(2);
+    else if (T <= 4) COLI_SC(4);
+    else COLI_SC(8);
+#undef COLI_SC
     return hipGetLastError();
 }
 
@@ -214,7 +223,8 @@ hipError_t launch_route(const LayerDev &L, const RouteIO &io, hipStream_t st, co
     if (S == 0) {
         dim3 grid(E), block(256);
 #define COLI_GEMV_CASE(N) \
-    case N: hipLaunchKernelGGL(logits_gemv_kernel<N>, grid, block, 0, st, io.x, L.router_w, T, H, E, io.logits); break;
+    case N: hipLaunchKernelGGL(logits_gemv_kernel<N>, grid, block, 0, st, io.x, L.router_w, T, H, E, io.logits, \
+                               nullptr, 0); break;
         switch (T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8) {
             COLI_GEMV_CASE(1)
             COLI_GEMV_CASE(2)

@@ -21,8 +21,8 @@ __device__ __forceinline__ float sigmoid_fp64(float l)
 }
 
 // --- top-k: one wave per token, 4 tokens per workgroup -------------------
-// Radix select: the k-th largest key is found bit by bit with wave ballots
-// (32 rounds, no shuffles); keys equal to it are taken in expert order; the
+// Radix select: the k-th largest key is found two bits at a time with wave
+// ballots (16 rounds, no shuffles); keys equal to it are taken in expert order; the
 // k winners are then ordered by (key desc, expert asc) through LDS.
 
 // Monotone map of an fp32 key to uint32 (larger float -> larger integer);
@@ -64,12 +64,15 @@ struct UnionOut {
 // barriers, so every wave of the 256-thread workgroup must call this).
 // ids / w are indexed by token (t * k + rank); with UNION the workgroup's
 // tokens (T <= 4, t0 = 0) also form the batch union into uo.
-template <int KPL, bool UNION>
+// TL: timeline marks 4 (keys loaded), 5 (threshold found), 6 (selection
+// and union written) into tl (measurement variants only).
+template <int KPL, bool UNION, bool TL = false>
 __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
                                              const double *__restrict__ part, int S,
                                              const float *__restrict__ bias, int T, int E, int k,
                                              float top_p, int32_t *__restrict__ ids,
-                                             float *__restrict__ w, const UnionOut &uo, int t0)
+                                             float *__restrict__ w, const UnionOut &uo, int t0,
+                                             uint64_t *tl = nullptr, int tl_cap = 0)
 {
     __shared__ int32_t sid[64];  // the batch's selections (UNION)
     __shared__ uint32_t sk[4][COLI_MAX_K_DEV];
@@ -108,6 +111,7 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
 #pragma unroll
         for (int i = 0; i < KPL; ++i) asm volatile("" : "+v"(lg[i]), "+v"(bs[i]));
     }
+    tl_mark<TL>(tl, tl_cap, 4);
     uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
@@ -116,15 +120,23 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
         sg[wv][e] = sgm;
         key[i] = (live && e < E) ? order_bits(sgm + bs[i]) : 0u;
     }
-    // largest tau with #{key >= tau} >= k  (valid keys are >= 1)
+    // largest tau with #{key >= tau} >= k  (valid keys are >= 1), two bits
+    // per round: the counts of the three candidates of a round are
+    // independent (their ballots overlap, where one bit per round would wait
+    // for each count before the next compare)
     uint32_t tau = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = tau | (1u << b);
-        int c = 0;
+    for (int b = 30; b >= 0; b -= 2) {
+        const uint32_t c1 = tau | (1u << b), c2 = tau | (2u << b), c3 = tau | (3u << b);
+        int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) c += __popcll(__ballot(key[i] >= cand));
-        if (c >= k) tau = cand;
+        for (int i = 0; i < KPL; ++i) {
+            n1 += __popcll(__ballot(key[i] >= c1));
+            n2 += __popcll(__ballot(key[i] >= c2));
+            n3 += __popcll(__ballot(key[i] >= c3));
+        }
+        tau = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : tau;
     }
+    tl_mark<TL>(tl, tl_cap, 5);
     int gt = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) gt += __popcll(__ballot(key[i] > tau));
@@ -152,10 +164,13 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
     if (live && lane < k) {
         mk = sk[wv][lane];
         me = se[wv][lane];
-        for (int j = 0; j < k; ++j) {
+        // all COLI_MAX_K_DEV entries read at once (one LDS round trip; the
+        // ones past k are not counted)
+#pragma unroll
+        for (int j = 0; j < COLI_MAX_K_DEV; ++j) {
             const uint32_t ok = sk[wv][j];
             const int oe = se[wv][j];
-            rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+            rank += (j < k && (ok > mk || (ok == mk && oe < me))) ? 1 : 0;
         }
     }
     __syncthreads();
@@ -166,8 +181,13 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
     }
     __syncthreads();
     if (live && lane < k) {
+        float sv[COLI_MAX_K_DEV];
+#pragma unroll
+        for (int j = 0; j < COLI_MAX_K_DEV; ++j) sv[j] = ss[wv][j];
         float sum = 0.f;
-        for (int j = 0; j < k; ++j) sum += ss[wv][j];  // fp32, selection order
+#pragma unroll
+        for (int j = 0; j < COLI_MAX_K_DEV; ++j)
+            if (j < k) sum += sv[j];  // fp32, selection order
         // adaptive top-p: keep the shortest prefix of the selection whose
         // weights reach top_p (fp32, in order), renormalised over the kept
         int kp = k;
@@ -197,9 +217,10 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
                 const int id = lane < k ? sid[lane] : -1;
                 const bool valid = id >= 0 && id < E;
                 int pos = 0;
-                for (int i = 0; i < k; ++i) {
+#pragma unroll
+                for (int i = 0; i < COLI_MAX_K_DEV; ++i) {
                     const int o = sid[i];
-                    pos += (o >= 0 && o < E && o < id) ? 1 : 0;
+                    pos += (i < k && o >= 0 && o < E && o < id) ? 1 : 0;
                 }
                 const int kept = __popcll(__ballot(valid));
                 if (valid) {
@@ -220,6 +241,7 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
             }
         }
     }
+    tl_mark<TL>(tl, tl_cap, 6);
 }
 
 // The selection lists of at most 4 tokens in LDS (T * k <= 64).
@@ -233,10 +255,13 @@ struct RouteLds {
 // union into l (every thread of the 256-thread workgroup calls this);
 // workgroup 0 also writes the global contents the top-k kernel leaves
 // (slots past the kept ones untouched).
-__device__ __forceinline__ void route_self(const RouteSelf &r, RouteLds &l)
+template <bool TL = false>
+__device__ __forceinline__ void route_self(const RouteSelf &r, RouteLds &l, uint64_t *tl = nullptr,
+                                           int tl_cap = 0)
 {
     const UnionOut uo{l.u, l.off, l.sl, l.n, r.cap};
-    route_tokens<4, true>(r.scores, nullptr, 0, r.bias, r.T, r.E, r.k, r.top_p, l.ids, l.w, uo, 0);
+    route_tokens<4, true, TL>(r.scores, nullptr, 0, r.bias, r.T, r.E, r.k, r.top_p, l.ids, l.w, uo,
+                              0, tl, tl_cap);
     __syncthreads();
     if (blockIdx.x == 0) {
         const int i = threadIdx.x, nu = l.n[0], kept = l.off[nu];

@@ -31,6 +31,20 @@ __device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 constexpr uint32_t kOOB = 0x40000000u;
 
+// Timeline mark j (0..7) of the calling wave, compiled into the kernels'
+// TL variants only (the measurement entry point): the chip-wide 100 MHz
+// real-time counter at that point, written by lane 0 to tl[w * 8 + j] (w =
+// the wave's index in the grid, recorded while w < cap).
+template <bool TL>
+__device__ __forceinline__ void tl_mark(uint64_t *tl, int cap, int j)
+{
+    if constexpr (TL) {
+        const int w = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+        const uint64_t t = __builtin_amdgcn_s_memrealtime();
+        if ((threadIdx.x & 63) == 0 && w < cap) tl[(size_t)w * 8 + j] = t;
+    }
+}
+
 struct StageRsrc {
     __amdgpu_buffer_rsrc_t w, s, w0, s0;  // weights, scales, and their empty twins
 };

@@ -288,3 +288,18 @@ def test_route_forward_noalloc_argument_errors(L):
         assert coli.workspace_bytes(6144, 2048, 256, 8, t_max, mode) <= coli.NOALLOC_SCRATCH_BYTES
         assert rf(big, T=t_max + 1, mode=mode) == coli.COLI_E_SCRATCH
         assert rf(big, T=4096, mode=mode) == coli.COLI_E_SCRATCH
+
+
+def test_route_forward_timeline_argument_errors(L):
+    """The timeline entry point takes the self-routing fp32 cases only and a
+    buffer with at least one wave's record per kernel."""
+    def rft(T=1, mode=0, tl=FAKE, cap=1024, x=FAKE):
+        return L.coli_moe_route_forward_timeline(ctypes.byref(layer()), x, T, ctypes.c_float(1.0),
+                                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode, FAKE,
+                                                 FAKE, 1 << 30, tl, cap, None)
+    assert rft(tl=None) == coli.COLI_E_ARG
+    assert rft(cap=0) == coli.COLI_E_ARG
+    assert rft(tl=MIS) == coli.COLI_E_ARG           # 8-byte records
+    assert rft(T=5) == coli.COLI_E_UNSUPPORTED      # not self-routing
+    assert rft(mode=1) == coli.COLI_E_UNSUPPORTED   # the int8 family writes no timeline
+    assert rft(x=MIS) == coli.COLI_E_ALIGN
