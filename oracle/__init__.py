@@ -51,6 +51,7 @@ def _setup(L):
         "orc_expert_f32": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], None),
         "orc_expert_i8": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], None),
         "orc_down_acc_i8": ([i32, i32, vp, vp, vp], None),
+        "orc_down_i8": ([i32, i32, vp, vp, vp, vp, vp], None),
         "orc_token_forward": ([vp, vp, vp, vp, i32, vp], None),
         "orc_forward": ([vp, vp, i32, vp, vp, i32, vp], None),
         "orc_forward_rows": ([vp, vp, vp, vp, i32, i32, vp, vp], None),
@@ -200,6 +201,15 @@ class Oracle:
                             _p(np.ascontiguousarray(x, np.float32)), _p(acc13), _p(g), _p(u),
                             _p(h), _p(qh), _p(sh), _p(acc2), _p(o))
         return dict(acc13=acc13, g=g, u=u, h=h, qh=qh, sh=sh, acc2=acc2, o=o)
+
+    def down_i8(self, w2, s2, qh, sh):
+        """Down projection (double) from given int8 codes of h (natural order)
+        and their scales."""
+        H, I = w2.shape[0], w2.shape[1] * 2
+        o = np.empty(H, np.float64)
+        self.L.orc_down_i8(H, I, _p(w2), _p(s2), _p(np.ascontiguousarray(qh, np.int8)),
+                           _p(np.ascontiguousarray(sh, np.float32)), _p(o))
+        return o
 
     def down_acc_i8(self, w2, qh):
         H, I = w2.shape[0], w2.shape[1] * 2

@@ -333,6 +333,29 @@ void orc_down_acc_i8(int32_t H, int32_t I, const uint8_t *w2, const int8_t *qh, 
             acc2[(size_t)n * G + g] = group_dot(qh, w2 + (size_t)n * rb2, g);
 }
 
+/* Down projection of the integer family from given int8 codes of h (qh [I],
+ * natural order) and their scales (sh [I/64]):
+ *   o[n] = sum_g (double)acc2[n][g] * sh[g] * s2[n][g]   (double),
+ *   acc2[n][g] = group_dot(qh, w2 row n, g).
+ * The same down stage as orc_expert_i8, for operands that come from
+ * elsewhere: the accumulators are exact given the codes, while the codes of
+ * h themselves depend on how g and u were rounded (a code may differ by one
+ * at a rounding boundary), so a GPU down projection is compared with the
+ * oracle on the GPU's own codes. */
+void orc_down_i8(int32_t H, int32_t I, const uint8_t *w2, const uint16_t *s2, const int8_t *qh,
+                 const float *sh, double *o)
+{
+    const int64_t rb2 = I / 2, G2 = I / 64;
+    for (int32_t n = 0; n < H; ++n) {
+        const uint8_t *row = w2 + (size_t)n * rb2;
+        const uint16_t *srow = s2 + (size_t)n * G2;
+        double acc = 0.0;
+        for (int64_t gg = 0; gg < G2; ++gg)
+            acc += (double)group_dot(qh, row, gg) * (double)sh[gg] * (double)orc_f16_to_f32(srow[gg]);
+        o[n] = acc;
+    }
+}
+
 /* Integer family ([Guide] "詳細解説" step 3 and "コア技術のハイライト").
  *   qx, sx = quant(x);  acc13[r][g] = group_dot(qx, w13 row r, g);
  *   g/u[r] = fp32( sum_g (double)acc13[r][g] * sx[g] * s13[r][g] );

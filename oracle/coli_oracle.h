@@ -64,6 +64,8 @@ void orc_expert_i8(int32_t H, int32_t I, const uint8_t *w13, const uint16_t *s13
                    int32_t *acc13, float *g, float *u, float *h, int8_t *qh, float *sh,
                    int32_t *acc2, double *o);
 void orc_down_acc_i8(int32_t H, int32_t I, const uint8_t *w2, const int8_t *qh, int32_t *acc2);
+void orc_down_i8(int32_t H, int32_t I, const uint8_t *w2, const uint16_t *s2, const int8_t *qh,
+                 const float *sh, double *o);
 
 void orc_token_forward(const orc_layer *L, const float *x_t, const int32_t *ids_t,
                        const float *w_t, int32_t act_mode, float *y_t);

@@ -323,6 +323,17 @@ def pin_i8_expert(o):
         ex = sum(Fraction(int(acc2[n, g])) * Fraction(float(sh[g])) * Fraction(float(sc2[n, g]))
                  for g in range(I // 64))
         assert abs(Fraction(float(r["o"][n])) - ex) <= abs(ex) * Fraction(1, 10 ** 14)
+    # the down stage on given codes: the oracle's own codes reproduce its o,
+    # arbitrary codes and scales follow the exact rational sum
+    assert np.array_equal(o.down_i8(w2, s2, r["qh"], r["sh"]), r["o"])
+    qr = RNG.integers(-127, 128, I).astype(np.int8)
+    sr = (RNG.random(I // 64) * 0.05).astype(np.float32)
+    od = o.down_i8(w2, s2, qr, sr)
+    accr = (codes2 * qr.astype(np.int64).reshape(1, I // 64, 64)).sum(-1)
+    for n in range(H):
+        ex = sum(Fraction(int(accr[n, g])) * Fraction(float(sr[g])) * Fraction(float(sc2[n, g]))
+                 for g in range(I // 64))
+        assert abs(Fraction(float(od[n])) - ex) <= abs(ex) * Fraction(1, 10 ** 14)
     # extreme accumulator: all weight codes -8, all activation codes -127
     w13e = np.full_like(w13, 0x88)
     xe = np.full(H, -3.0, np.float32)
@@ -634,6 +645,8 @@ MUTANTS = [
      "for (int64_t kk = g * 64; kk < g * 64 + 63; ++kk)"),
     ("down scale", "acc += (double)a * (double)shv[gg] * (double)orc_f16_to_f32(srow[gg]);",
      "acc += (double)a * (double)shv[0] * (double)orc_f16_to_f32(srow[gg]);"),
+    ("down from codes scale", "acc += (double)group_dot(qh, row, gg) * (double)sh[gg] *",
+     "acc += (double)group_dot(qh, row, gg) * (double)sh[0] *"),
     ("shared dropped", "if (!L->n_shared) break;", "break;"),
     ("weight index", "wj = (double)w_t[j];", "wj = (double)w_t[0];"),
     ("rms divisor", "double inv = 1.0 / sqrt(ss / (double)H + 1e-6);",
