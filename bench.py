@@ -270,6 +270,27 @@ def oracle_baseline(w, host0, mode, topp, cpu_seconds):
                       f"pinned to one CPU)"}
 
 
+def expert_popularity(offsets, U, E):
+    """Realised popularity of the routed experts: per layer call, the slot
+    counts of the union entries sorted descending; their mean by rank over
+    the calls, and the least-squares slope of log(count) on log(rank) over
+    ranks 3..64 (the Zipf(1.1) bias aims at about -1.05 there)."""
+    by_rank = np.zeros(E)
+    for off, u in zip(offsets, U):
+        o = off[:u + 1].cpu().numpy().astype(np.int64)
+        c = np.sort(np.diff(o))[::-1]
+        by_rank[:len(c)] += c
+    by_rank /= len(offsets)
+    r = np.arange(3, min(64, int(U.min())) + 1)
+    c = by_rank[r - 1]
+    ok = c > 0
+    slope = float(np.polyfit(np.log(r[ok]), np.log(c[ok]), 1)[0]) if ok.sum() >= 2 else None
+    return {"mean_slots_by_rank_top16": [round(float(v), 1) for v in by_rank[:16]],
+            "mean_slots_rank_64_128_256": [round(float(by_rank[i - 1]), 2) for i in (64, 128, 256)],
+            "loglog_slope_ranks_3_64": round(slope, 3) if slope is not None else None,
+            "calls": len(offsets)}
+
+
 TL_CAP = 8192      # waves recorded per kernel by the timeline entry point
 TL_TICK_US = 0.01  # the real-time counter runs at 100 MHz
 
@@ -481,10 +502,15 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
     hip = Hip()
     names = coli.route_forward_kernel_names(mode, T) if one_call else coli.forward_kernel_names(mode, T)
     nk = len(names)
-    dom = next(j for j, nm in enumerate(names) if "gateup" in nm)
+    # the gate/up matmul: one launch, or the grouped GEMM's full-tile and
+    # partial-tile launches together
+    doms = [j for j, nm in enumerate(names) if "gateup" in nm]
+    dom = doms[0]
+    dom_label = names[dom] if len(doms) == 1 else names[dom].split(",")[0] + ">"
     if prof_steps is None:
         prof_steps = 8 if stacked else 64
     union_sizes = []
+    union_offsets = []
     ev = [[hip.event() for _ in range(2 * nk)] for _ in range(prof_steps * (w.layers if stacked else 1))]
     torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host enqueues
     i = 0
@@ -509,6 +535,8 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
                                       bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
                                       bufs.workspace, ev[i])
             union_sizes.append(bufs.n_union[:1].clone())
+            if w.bias_kind == "zipf":
+                union_offsets.append(bufs.offsets.clone())
             if stacked:
                 coli.add_inplace(resid, bufs.y, T * H)
             i += 1
@@ -521,7 +549,8 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
             hip.destroy(x_)
     per_kernel /= len(ev)
     U = np.array([int(u.item()) for u in union_sizes])
-    dur_s = per_kernel[dom] * 1e-3
+    popularity = expert_popularity(union_offsets, U, E) if union_offsets else None
+    dur_s = sum(per_kernel[j] for j in doms) * 1e-3
     n_exp = U.mean() + w.n_shared
     R = T * k + w.n_shared * T
     gateup_bytes = n_exp * (2 * I * (H // 2) + 2 * I * (H // 64) * 2)
@@ -548,13 +577,13 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath) and topp is None:
         with open(tpath) as fp:
-            rec = json.load(fp).get(f"{w.name}:{names[dom]}")
+            rec = json.load(fp).get(f"{w.name}:{dom_label}")
         if rec and rec.get("source_hash") == profiling.source_hash():
             roof["traffic"] = rec["hbm_bytes_per_launch"]
             roof["traffic_source"] = ("profiles/traffic.json (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                                       "copy-calibrated; same kernel sources)")
-    roof["kernel"] = names[dom]
-    roof["kernel_us"] = round(per_kernel[dom] * 1e3, 2)
+    roof["kernel"] = dom_label + (" (full- and partial-tile launches)" if len(doms) > 1 else "")
+    roof["kernel_us"] = round(dur_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(algo_bytes)
     roof["algorithmic_ops_per_launch"] = int(algo_ops)
     if mode == coli.ACT_I8:
@@ -582,7 +611,7 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
                      "'event us' is the kernel's dispatch-event duration from the same run.  "
                      "Marks (coli_moe_route_forward_timeline): self-routing gate/up 1 routing done, "
                      "2 activations staged, 3 first reduction batch written, 4 router keys loaded, "
-                     "5 top-k threshold found, 6 selection and union written; fused down + combine "
+                     "5 selection found, 6 selection and union written; fused down + combine "
                      "1 first entry's rows done, 2 / 3 before / after the workgroup barrier.\n\n")
             fp.write(table + "\n")
         log(table)
@@ -598,6 +627,7 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
                    "graph": use_graph, "union_size_mean": round(float(U.mean()), 2),
                    "union_size_minmax": [int(U.min()), int(U.max())],
                    "kernels_us": kernels_us},
+        **({"expert_popularity": popularity} if popularity else {}),
         # step time (us): warm = graph replays of the K timed steps (replay
         # time / K); cold = single-step graph replays, each after a 1 GiB read
         # of other memory (evicts L2 and Infinity Cache), graph launch included
@@ -694,6 +724,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic"}
     for key in ("config", "step_us", "roofline", "cpu_baseline"):
         out[key] = head[key]
+    if "expert_popularity" in head:
+        out["expert_popularity"] = head["expert_popularity"]
     if args.workload is None:
         # the other workloads of the metric, each with its own default steps
         extra = {}

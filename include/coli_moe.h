@@ -329,6 +329,24 @@ const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
 /* Size in bytes of the acc_dump buffer of coli_moe_forward (0 if invalid). */
 size_t coli_moe_acc_dump_bytes(int32_t H, int32_t I, int32_t k, int32_t T, int32_t n_shared);
 
+/* Where a coli_moe_forward call in the int8 family with T > 4 tokens (the
+ * grouped GEMM) leaves its intermediate results inside the workspace, for
+ * tests and diagnostics; they stay valid until the next call that uses the
+ * workspace.  R = T*k + n_shared*T rows.  out[0..2] receive byte offsets:
+ *   out[0]  o   fp32 [R][H]     expert outputs, row = slot t*k + j, or
+ *                               T*k + t for the shared expert;
+ *   out[1]  qh  int8 [R][I]     int8 codes of h, row = union position (the
+ *                               slot's index in the union's slot list, or
+ *                               T*k + t for the shared expert), inside
+ *                               every 8-element block in the element order
+ *                               [0,2,4,6,1,3,5,7];
+ *   out[2]  sh  fp32 [R][I/64]  the codes' scales, rows as qh.
+ * Returns COLI_OK; COLI_E_ARG (out NULL, n_shared not 0 or 1) or
+ * COLI_E_SHAPE (dimensions outside the limits, or T <= 4: the streaming
+ * kernels keep h in fp32 and quantise it in registers). */
+int coli_moe_i8_workspace_offsets(int32_t H, int32_t I, int32_t E, int32_t k, int32_t T,
+                                  int32_t n_shared, size_t *out);
+
 /* Human-readable name of a status code (static string). */
 const char *coli_moe_strerror(int status);
 

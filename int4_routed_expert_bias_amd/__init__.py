@@ -27,7 +27,8 @@ EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_route_forward_noalloc", "coli_moe_route_forward_timeline",
            "coli_moe_route_forward_kernel_count", "coli_moe_route_forward_kernel_name",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
-           "coli_moe_acc_dump_bytes", "coli_moe_strerror", "coli_moe_device_check",
+           "coli_moe_acc_dump_bytes", "coli_moe_i8_workspace_offsets", "coli_moe_strerror",
+           "coli_moe_device_check",
            "coli_rmsnorm", "coli_add_inplace", "coli_stream_read")
 # every symbol declared in include/coli_mla.h
 MLA_EXPORTS = ("coli_mla_workspace_bytes", "coli_mla_decode", "coli_mla_decode_profiled")
@@ -89,6 +90,7 @@ def lib():
             "coli_moe_forward_kernel_count": ([i32, i32], ctypes.c_int),
             "coli_moe_forward_kernel_name": ([i32, i32, i32], ctypes.c_char_p),
             "coli_moe_acc_dump_bytes": ([i32, i32, i32, i32, i32], sz),
+            "coli_moe_i8_workspace_offsets": ([i32, i32, i32, i32, i32, i32, vp], ctypes.c_int),
             "coli_moe_strerror": ([ctypes.c_int], ctypes.c_char_p),
             "coli_moe_device_check": ([], ctypes.c_int),
             "coli_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
@@ -149,6 +151,15 @@ def workspace_bytes(H, I, E, k, T, act_mode) -> int:
 
 def acc_dump_bytes(H, I, k, T, n_shared) -> int:
     return lib().coli_moe_acc_dump_bytes(H, I, k, T, n_shared)
+
+
+def i8_workspace_offsets(H, I, E, k, T, n_shared=1):
+    """Byte offsets of o, qh and sh inside an int8-family forward workspace
+    (T > 4; see coli_moe_i8_workspace_offsets)."""
+    out = (ctypes.c_size_t * 3)()
+    _check(lib().coli_moe_i8_workspace_offsets(H, I, E, k, T, n_shared, out),
+           "coli_moe_i8_workspace_offsets")
+    return {"o": out[0], "qh": out[1], "sh": out[2]}
 
 
 def device_check() -> int:

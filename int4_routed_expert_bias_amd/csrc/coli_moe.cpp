@@ -119,6 +119,18 @@ size_t coli_moe_acc_dump_bytes(int32_t H, int32_t I, int32_t k, int32_t T, int32
     return dump_layout(H, I, k, T, n_shared).total;
 }
 
+int coli_moe_i8_workspace_offsets(int32_t H, int32_t I, int32_t E, int32_t k, int32_t T,
+                                  int32_t n_shared, size_t *out)
+{
+    if (!out || (n_shared != 0 && n_shared != 1)) return COLI_E_ARG;
+    if (check_dims(H, I, E, k, T) != COLI_OK || T <= kI8StreamTMax) return COLI_E_SHAPE;
+    const Workspace w = workspace_layout(H, I, E, k, T, COLI_ACT_I8, n_shared);
+    out[0] = w.o;
+    out[1] = w.qh;
+    out[2] = w.sh;
+    return COLI_OK;
+}
+
 const char *coli_moe_strerror(int status)
 {
     switch (status) {
@@ -437,8 +449,9 @@ const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
     static const char *f32[] = {"gateup_f32_kernel", "down_f32_kernel", "combine_kernel"};
     static const char *i8_few[] = {"quant_rows_kernel", "gateup_i8v_kernel", "down_i8v_kernel",
                                    "combine_kernel"};
-    static const char *i8[] = {"quant_rows_kernel", "schedule_kernel", "ggemm_kernel<gateup>",
-                               "ggemm_kernel<down>", "combine_kernel"};
+    static const char *i8[] = {"quant_rows_kernel", "schedule_kernel", "ggemm_kernel<gateup,full>",
+                               "ggemm_kernel<gateup,partial>", "ggemm_kernel<down,full>",
+                               "ggemm_kernel<down,partial>", "combine_kernel"};
     if (i < 0 || i >= forward_kernel_count(act_mode, T)) return nullptr;
     if (act_mode == COLI_ACT_F32) return T == 1 ? f32_one[i] : T <= 4 ? f32_few[i] : f32[i];
     return T <= kI8StreamTMax ? i8_few[i] : i8[i];

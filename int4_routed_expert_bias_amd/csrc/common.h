@@ -58,6 +58,21 @@ __device__ __forceinline__ int perm8_pos(int kk)
     return (kk & ~7) | ((b & 1) << 2) | (b >> 1);
 }
 
+// The int8 family's fp32 epilogue forms each group term as acc * s from the
+// exact int32 group accumulator acc and the activation scale s rounded to 22
+// significant bits (to nearest, ties up; a relative change of at most
+// 2^-23): epi_act_scale(s).  Then kEpiM * s' is exact in fp32 (kEpiM = 3 *
+// 2^22), so the grouped GEMM forms the term as one FMA on the accumulator
+// offset by kEpiM inside the matrix core (as fp32, kEpiM + acc is exact for
+// |acc| < 2^22): fma(kEpiM + acc, s', -kEpiM * s') = round(acc * s'), bit
+// for bit float(acc) * s', which the streaming kernels compute.
+constexpr float kEpiM = 12582912.0f;         // 3 * 2^22 = 1.5 * 2^23
+constexpr int32_t kEpiMBits = 0x4B400000;    // its bit pattern (unit 1 in the last place)
+__device__ __forceinline__ float epi_act_scale(float s)
+{
+    return __uint_as_float((__float_as_uint(s) + 2u) & ~3u);
+}
+
 // ---------------------------------------------------------------------------
 // workspace layout (offsets in bytes, each region 256-byte aligned)
 
@@ -83,7 +98,7 @@ struct Workspace {
     int64_t max_tiles;
 };
 
-constexpr int kTileM = 64;  // token rows per integer-GEMM tile
+constexpr int kTileM = 128;  // token rows per integer-GEMM tile
 // Batches up to this size run the streaming kernels of the integer family
 // (and, for T >= 2, of the fp32 family).
 constexpr int kI8StreamTMax = 4;
@@ -274,11 +289,13 @@ struct ForwardIO {
 
 // Kernels one forward call launches (without acc_dump): fp32 family gate/up,
 // down, combine; integer family quant, [schedule,] gate/up, down, combine
-// (batches of at most kI8StreamTMax tokens stream without a tile schedule).
+// (batches of at most kI8StreamTMax tokens stream without a tile schedule;
+// larger ones run each grouped GEMM as two launches, full then partial
+// tiles).
 inline int forward_kernel_count(int act_mode, int T)
 {
     if (act_mode == 0) return T == 1 ? 2 : 3;  // T == 1: down and combine in one launch
-    if (act_mode == 1) return T <= kI8StreamTMax ? 4 : 5;
+    if (act_mode == 1) return T <= kI8StreamTMax ? 4 : 7;
     return 0;
 }
 

@@ -951,6 +951,8 @@ template <int P, int M, int DEPTH, int NTOK, int WPB, bool ROUTE, bool TL = fals
 __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
+    // route_self keeps one LDS record per wave of a 4-wave workgroup
+    static_assert(!ROUTE || WPB == 4, "self-routing needs exactly four waves");
     constexpr int V = next_pow2(2 * M * NTOK), N = reduced_count(V);
     static_assert(V <= 64, "at most 64 values per reduction");
     // x of the T tokens chunk-transposed (token t, piece q of chunk c at

@@ -6,8 +6,9 @@
 //  quant:    per token per 64-group, scale = amax / 127 (IEEE divide),
 //            q = clamp(rint(v / scale), -127, 127); codes are stored in the
 //            permuted order [0,2,4,6,1,3,5,7] inside every 8-element block.
-//  schedule: one thread per union expert turns its slot count into 64-row
-//            tiles (device side: the union size never leaves the GPU).
+//  schedule: one thread per union expert turns its slot count into 128-row
+//            tiles, longest entries first (device side: the union size
+//            never leaves the GPU).
 //  gemm:     v_mfma_i32_16x16x64_i8, one MFMA per 64-group, so the exact
 //            int32 group accumulator comes straight out of the matrix core.
 //            A = 16 token rows of int8 codes, B = 16 weight rows.  A packed
@@ -35,120 +36,179 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // --- activation quantisation ---------------------------------------------
 // rows [nrows][K] fp32 -> q [nrows][K] int8 (permuted), s [nrows][K/64];
 // dq / ds (tests only, else null): the same codes in natural order and the
-// scales
+// scales.  A wave quantises 4 groups: the 16 lanes of a DPP row hold one
+// group, 4 consecutive elements each (one 16-byte load), so the group's amax
+// is a 4-step butterfly inside the row; a lane pair (the two halves of an
+// 8-element block) swaps codes once and each lane stores 4 bytes of the
+// permuted block.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict__ x, int64_t ngroups,
                                                          int K, int8_t *__restrict__ q,
                                                          float *__restrict__ s, int8_t *dq,
                                                          float *ds)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (g >= ngroups) return;
+    const int lane = threadIdx.x & 63, l16 = lane & 15;
+    const int64_t g = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool ok = g < ngroups;
+    const int64_t gg = ok ? g : ngroups - 1;
     const int G = K / 64;
-    const int64_t row = g / G;
-    const int gi = (int)(g % G);
-    const float v = x[row * K + gi * 64 + lane];
-    const float amax = wave_max(fabsf(v));
-    int8_t code = 0;
+    const int64_t row = gg / G;
+    const int gi = (int)(gg % G);
+    const int64_t base = row * K + gi * 64;
+    const float4 v4 = *reinterpret_cast<const float4 *>(x + base + 4 * l16);
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     float sc = 0.f;
+    uint32_t nat = 0;  // the 4 codes, natural order
     if (amax > 0.f) {
         sc = amax / 127.0f;
-        float r = rintf(v / sc);
-        r = fminf(fmaxf(r, -127.f), 127.f);
-        code = (int8_t)r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float r = rintf(v[e] / sc);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            nat |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
+        }
     }
-    q[row * K + perm8_pos(gi * 64 + lane)] = code;
-    if (lane == 0) s[row * G + gi] = sc;
-    if (dq) {
-        dq[row * K + gi * 64 + lane] = code;
-        if (lane == 0) ds[row * G + gi] = sc;
+    // 8-element block b = l16 / 2: the even lane holds elements 0..3, the odd
+    // lane 4..7; permuted order [0,2,4,6 | 1,3,5,7]
+    const uint32_t other = (uint32_t)__shfl_xor((int)nat, 1, 64);
+    // v_perm bytes 0-3 select nat's bytes, 4-7 other's: even lane [n0 n2 o0 o2]
+    // = elements 0,2,4,6; odd lane [o1 o3 n1 n3] = elements 1,3,5,7
+    const uint32_t word = (l16 & 1) ? __builtin_amdgcn_perm(other, nat, 0x03010705u)
+                                    : __builtin_amdgcn_perm(other, nat, 0x06040200u);
+    if (ok) {
+        *reinterpret_cast<uint32_t *>(q + base + 4 * l16) = word;
+        if (l16 == 0) s[row * G + gi] = sc;
+        if (dq) {
+            *reinterpret_cast<uint32_t *>(dq + base + 4 * l16) = nat;
+            if (l16 == 0) ds[row * G + gi] = sc;
+        }
     }
 }
 
 // --- tile schedule ---------------------------------------------------------
-// tiles[i] = (entry, first row) for i < count; count stored at tiles[max].x
+// Two tile lists in tiles[]: every entry's full 128-row tiles first
+// (positions [0, nf)), then the entries' last, partial tiles (positions
+// [nf, nf + np)); tiles[max_tiles] = (nf, np).  A tile is (entry, first
+// row).  Full tiles are ordered by entry size, largest first (ties: lower
+// entry first), an entry's tiles consecutive, so the longest entries start
+// first and tiles that read the same weights run at the same time; partial
+// tiles are ordered by row count, largest first.  The order changes no
+// result (every tile writes its own rows).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ offsets,
                                                         const int32_t *__restrict__ n_union,
                                                         int cap, int T, int n_shared, int tile_m,
                                                         int2 *__restrict__ tiles, int max_tiles)
 {
-    __shared__ int32_t cnt[COLI_MAX_E_DEV + 1];
-    __shared__ int32_t scan[COLI_MAX_E_DEV + 2];  // entries cap + shared, plus the total
+    __shared__ int32_t cnt[COLI_MAX_E_DEV + 1];   // rows of live entry i (union entries, then shared)
+    __shared__ int32_t ordf[COLI_MAX_E_DEV + 1];  // live entry at each full-list position
+    __shared__ int32_t ordp[COLI_MAX_E_DEV + 1];  // live entry at each partial-list position
+    __shared__ int32_t scan[COLI_MAX_E_DEV + 2];  // first full tile of each position, then nf
+    __shared__ int32_t npart;
     const int tid = threadIdx.x;
     const int U = n_union[0];
-    const int nent = cap + n_shared;  // entry cap = the shared expert
-    for (int e = tid; e < nent; e += blockDim.x) {
-        int n = 0;
-        if (e < cap) {
-            if (e < U) n = offsets[e + 1] - offsets[e];
-        } else {
-            n = T;
+    const int nl = U + n_shared;
+    for (int i = tid; i < nl; i += blockDim.x) cnt[i] = i < U ? offsets[i + 1] - offsets[i] : T;
+    if (tid == 0) npart = 0;
+    __syncthreads();
+    // positions: entries with more rows (more full tiles; a longer partial
+    // tile), or as many and a lower index
+    for (int i = tid; i < nl; i += blockDim.x) {
+        const int c = cnt[i], cr = c % tile_m;
+        int rf = 0, rp = 0;
+        for (int j = 0; j < nl; ++j) {
+            const int cj = cnt[j], cjr = cj % tile_m;
+            rf += (cj > c) | ((cj == c) & (j < i));
+            rp += (cjr > cr) | ((cjr == cr) & (j < i));
         }
-        cnt[e] = (n + tile_m - 1) / tile_m;
+        ordf[rf] = i;
+        ordp[rp] = i;
+        if (cr) atomicAdd(&npart, 1);
     }
     __syncthreads();
     if (tid < 64) {
-        // single-wave exclusive scan over nent <= 1025 entries
+        // single-wave exclusive scan of the full-tile counts in list order
         int32_t carry = 0;
-        for (int base = 0; base < nent; base += 64) {
-            int e = base + tid;
-            int32_t v = e < nent ? cnt[e] : 0;
+        for (int base = 0; base < nl; base += 64) {
+            const int p = base + tid;
+            const int32_t v = p < nl ? cnt[ordf[p]] / tile_m : 0;
             int32_t incl = v;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                int32_t o = __shfl_up(incl, off, 64);
+                const int32_t o = __shfl_up(incl, off, 64);
                 if (tid >= off) incl += o;
             }
-            if (e < nent) scan[e] = carry + incl - v;
+            if (p < nl) scan[p] = carry + incl - v;
             carry += __shfl(incl, 63, 64);
         }
-        if (tid == 0) scan[nent] = carry;
+        if (tid == 0) scan[nl] = carry;
     }
     __syncthreads();
-    for (int e = tid; e < nent; e += blockDim.x) {
-        int32_t b = scan[e];
-        for (int m = 0; m < cnt[e] && b + m < max_tiles; ++m) tiles[b + m] = make_int2(e, m * tile_m);
+    const int nf = min(scan[nl], max_tiles);
+    const int np = min(npart, max_tiles - nf);
+    for (int p = tid; p < nl; p += blockDim.x) {
+        const int i = ordf[p];
+        const int e = i < U ? i : cap;  // entry cap = the shared expert
+        const int32_t b = scan[p];
+        for (int m = 0; m < cnt[i] / tile_m && b + m < nf; ++m) tiles[b + m] = make_int2(e, m * tile_m);
+        // partial tiles: entries with a remainder sort first in ordp
+        const int ip = ordp[p];
+        if (p < np && cnt[ip] % tile_m) {
+            const int ep = ip < U ? ip : cap;
+            tiles[nf + p] = make_int2(ep, cnt[ip] / tile_m * tile_m);
+        }
     }
-    if (tid == 0) tiles[max_tiles] = make_int2(min(scan[nent], max_tiles), 0);
+    if (tid == 0) tiles[max_tiles] = make_int2(nf, np);
 }
 
 // --- grouped GEMM ----------------------------------------------------------
-// One workgroup computes a BM x kBN output tile of one union entry: BM of
-// the entry's token rows (a tile from the schedule) against kBN weight rows
-// (gate/up: 64 gate rows i0.. and the 64 matching up rows I + i0..; down:
-// 128 output rows n0..).  The K loop walks kKG 64-groups per step through a
-// double-buffered LDS stage: the next step's activation codes, packed
-// weights and scales are loaded into registers while the current step
-// computes, then written to the other buffer.
+// One workgroup computes a 128 x 128 output tile of one union entry: up to
+// 128 of the entry's rows (a tile of the schedule) against 128 weight rows
+// (gate/up: 64 gate rows i0.. and the matching up rows I + i0..; down: 128
+// output rows n0..).  The K loop walks two 64-groups per step through a
+// double-buffered LDS stage: the next step's loads are issued before the
+// current step computes and written to the other buffer after it.
 //
-// Four waves as 2 (rows) x 2 (columns): wave (wm, wn) owns BM/2 rows
-// (MT = BM/32 m-tiles of 16) and 64 columns (4 n-tiles of 16): gate/up:
-// gate rows i0 + 32 wn.. and their up rows, so SwiGLU pairs sit in the same
-// lane and register; down: rows n0 + 64 wn...  Per 64-group an m-tile x
-// n-tile pair is one v_mfma_i32_16x16x64_i8 whose result is the exact group
-// accumulator (times 16, from the unpacked codes); the epilogue adds
-// acc * sx * (sw / 16) into fp32 (cvt, mul, fma: the 1/16 is folded into
-// the weight scale, exactly).  Each A fragment read from LDS feeds 4 MFMAs
-// and each B fragment MT, which keeps LDS traffic under its bandwidth.
-constexpr int kBN = 128;
+// Four waves as 2 (rows) x 2 (columns).  The 8 m-tiles of 16 rows are
+// interleaved over the row waves (wave wm owns m-tiles wm, wm + 2, wm + 4,
+// wm + 6), so a partial tile keeps both busy, and a wave skips its m-tiles
+// that hold no row.  Column wave wn owns 4 n-tiles of 16 weight rows:
+// gate/up: gate rows i0 + 32 wn.. and their up rows (a SwiGLU pair sits in
+// one lane and register); down: rows n0 + 64 wn...  Per 64-group an
+// (m-tile, n-tile) pair is one v_mfma_i32_16x16x64_i8 whose result is the
+// exact group accumulator times 16 (the int4 codes are unpacked to signed
+// bytes 16 x code); the epilogue adds acc * s' * (sw / 16) in fp32 (the
+// 1/16 folded into the weight scale, exactly).  The MFMA's accumulator input
+// is kEpiM for every element, so its result read as fp32 is kEpiM + 16 acc
+// exactly, and the term needs two FMAs per output: fma(that, s', -kEpiM s')
+// = round(16 acc * s') (see epi_act_scale), then fma(term, sw / 16, out).
+//
+// Issue cost per MFMA: the epilogue's 8 VALU instructions (4 outputs x 2)
+// are the floor of this arithmetic (an MFMA takes 16 cycles, 8 wave64 VALU
+// instructions 32, so the matrix cores can be at most half busy); the int4
+// unpack adds 1.5 (6 per B fragment, each fragment feeding 4 m-tiles) and
+// staging and addressing well under 1.
+constexpr int kGBM = kTileM;          // rows per tile
+constexpr int kGBN = 128;             // weight rows per tile
+constexpr int kGKG = 2;               // 64-groups per LDS stage
+constexpr int kGAS = kGKG * 64 + 32;  // LDS activation row stride (bytes)
+constexpr int kGBS = kGKG * 32 + 16;  // LDS packed-weight row stride
+static_assert(kGBM == 128 && kGBN == 128 && kGKG == 2, "the wave and staging layouts cover 128 x 128 tiles, two groups a step");
 
-// LDS of one workgroup: two stages of KG groups (row strides padded by 16
-// bytes, which keeps the fragment reads free of bank conflicts).
-template <int BM, int KG, bool UB>
 struct __attribute__((aligned(16))) GemmLds {
-    static constexpr int AS = KG * 64 + 16;             // activation row stride (bytes)
-    static constexpr int BS = UB ? KG * 64 + 16 : KG * 32 + 16;  // weight row stride
-    alignas(16) uint8_t a[2][BM * AS];
-    alignas(16) uint8_t b[2][kBN * BS];  // packed int4, or unpacked 16 x code (UB)
-    alignas(16) float sx[2][KG][BM];
-    alignas(16) float sw[2][KG][kBN];  // weight scale / 16
-    alignas(16) float amax[2][BM];
+    alignas(16) uint8_t a[2][kGBM * kGAS];  // activation codes
+    alignas(16) uint8_t b[2][kGBN * kGBS];  // packed int4 weight codes
+    alignas(16) float sx[2][kGKG][kGBM];    // activation scales s' (epi_act_scale)
+    alignas(16) float nm[2][kGKG][kGBM];    // -kEpiM * s'
+    alignas(16) float sw[2][kGKG][kGBN];    // weight scales / 16
+    alignas(16) float amax[2][kGBM];        // gate/up: |h| maxima per column wave
 };
 
 struct I8Args {
     const int8_t *qin;        // activation codes (permuted) [rows][K]
     const float *sin;         // activation scales [rows][K/64]
-    int in_by_slot;           // 0: input row = token, 1: input row = output row
+    int in_by_pos;            // 0: input row = token, 1: input row = position
     const uint8_t *w; const uint16_t *s;        // routed [E][N][K/2], [E][N][K/64]
     const uint8_t *sh_w; const uint16_t *sh_s;  // shared
     int N, K, I, H;
@@ -157,7 +217,7 @@ struct I8Args {
     int max_tiles;
     int T, k, cap;
     // outputs
-    int8_t *qh; float *sh;    // gate/up: quantised h (permuted) and scales
+    int8_t *qh; float *sh;    // gate/up: quantised h (permuted) and scales, by position
     float *o;                 // down: [R][H]
     int32_t *dump_acc;        // [R][N][K/64] or null
     int8_t *dump_qh; float *dump_sh;
@@ -186,14 +246,20 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 
 constexpr uint32_t kOOB8 = 0x80000000u;  // beyond any buffer: reads 0
 
-// Tile of the schedule: entry, first row and row count.
+// Tile of the schedule: entry, first row, row count and first position.
+// The positions of an entry's rows are consecutive: a routed entry's rows
+// are its slots in union order (positions offsets[e]..), the shared
+// expert's rows are the tokens (positions T*k + t); h travels between the
+// two GEMMs by position, so a down tile reads one contiguous block.
 struct TileInfo {
     int ue, m0, rows;
     bool routed;
     int o0;  // routed: first position in slots
+    int p0;  // position of the tile's first row
 };
 
-// Input and output rows of tile row m (rows past the tile repeat its last).
+// Token (or position) and output row of tile row m (rows past the tile
+// repeat its last).
 __device__ __forceinline__ void tile_row(const I8Args &a, const TileInfo &ti, int m, int &in_row,
                                          int &out_row)
 {
@@ -202,32 +268,35 @@ __device__ __forceinline__ void tile_row(const I8Args &a, const TileInfo &ti, in
     if (ti.routed) {
         const int sl = a.slots[ti.o0 + ti.m0 + mm];
         out_row = sl;
-        in_row = a.in_by_slot ? sl : sl / a.k;
+        in_row = a.in_by_pos ? ti.p0 + mm : sl / a.k;
     } else {
         const int t = ti.m0 + mm;
         out_row = TK + t;
-        in_row = a.in_by_slot ? TK + t : t;
+        in_row = a.in_by_pos ? ti.p0 + mm : t;
     }
 }
 
-// UB: the weight codes are unpacked once, when a stage is written to LDS,
-// instead of by each of the two waves that read a column block.  OCC: the
-// workgroups per CU the register budget is sized for.
-template <int BM, int KG, bool GATEUP, bool DUMP, bool UB = false, int OCC = 2>
-__global__ __launch_bounds__(256, OCC) void ggemm_kernel(I8Args a)
+// LIST: the tiles a launch covers -- kAllTiles (both lists; the dump
+// variant), kFullTiles (128 rows each: no row masks, the software-pipelined
+// step) or kPartialTiles (fewer rows: m-tiles without rows are skipped).
+// Full and partial tiles run as separate launches, so each variant gets its
+// own register allocation.
+constexpr int kAllTiles = 0, kFullTiles = 1, kPartialTiles = 2;
+
+template <bool GATEUP, bool DUMP, int LIST>
+__global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
 {
-    constexpr int MT = BM / 32;               // m-tiles per wave
-    constexpr int kKG = KG;
-    using Lds = GemmLds<BM, KG, UB>;
-    constexpr int kAS = Lds::AS, kBS = Lds::BS;
-    __shared__ Lds sm;
+    constexpr int BM = kGBM, BN = kGBN, KG = kGKG, AS = kGAS, BS = kGBS;
+    static_assert(!DUMP || LIST == kAllTiles, "the dump variant covers every tile");
+    __shared__ GemmLds sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int n = lane & 15, q = lane >> 4;
-    const int count = a.tiles[a.max_tiles].x;
+    const int2 counts = a.tiles[a.max_tiles];
+    const int count = LIST == kAllTiles ? counts.x + counts.y : LIST == kFullTiles ? counts.x : counts.y;
     if ((int)blockIdx.y >= count) return;
-    const int2 td = a.tiles[blockIdx.y];
+    const int2 td = a.tiles[blockIdx.y + (LIST == kPartialTiles ? counts.x : 0)];
     TileInfo ti;
     ti.ue = td.x;
     ti.m0 = td.y;
@@ -238,273 +307,388 @@ __global__ __launch_bounds__(256, OCC) void ggemm_kernel(I8Args a)
         const int e = a.union_ids[ti.ue];
         ti.o0 = a.offsets[ti.ue];
         ti.rows = min(BM, a.offsets[ti.ue + 1] - ti.o0 - ti.m0);
+        ti.p0 = ti.o0 + ti.m0;
         wb = a.w + (size_t)e * a.N * (a.K / 2);
         sb = a.s + (size_t)e * a.N * (a.K / 64);
     } else {
         ti.o0 = 0;
         ti.rows = min(BM, a.T - ti.m0);
+        ti.p0 = a.T * a.k + ti.m0;
         wb = a.sh_w;
         sb = a.sh_s;
     }
     const int K = a.K, G = K / 64, rb = K / 2;
-    const int nb0 = blockIdx.x * (GATEUP ? kBN / 2 : kBN);  // first unit / row of the block
-    // weight row of local LDS row r (-1: past the matrix)
+    const int nb0 = blockIdx.x * (GATEUP ? BN / 2 : BN);  // first unit / row of the block
+    // weight row of local row r (-1: past the matrix)
     auto wrow = [&](int r) -> int {
         int row, lim;
         if (GATEUP) {
-            row = (r < kBN / 2) ? nb0 + r : a.I + nb0 + (r - kBN / 2);
-            lim = (r < kBN / 2) ? a.I : 2 * a.I;
+            row = (r < BN / 2) ? nb0 + r : a.I + nb0 + (r - BN / 2);
+            lim = (r < BN / 2) ? a.I : 2 * a.I;
         } else {
             row = nb0 + r;
             lim = a.N;
         }
         return row < lim ? row : -1;
     };
+    // Buffers: the weights and scales of the entry; the activation codes and
+    // scales of the token matrix (gate/up) or of the tile's contiguous block
+    // of positions (down).  Every range holds 32-bit offsets (the host limits
+    // T * H and 128 rows * I); reads past a range return 0.
     const auto rB = rsrc_i8(wb, (uint32_t)((size_t)a.N * rb));
     const auto rS = rsrc_i8(sb, (uint32_t)((size_t)a.N * G * 2));
+    const int in0 = a.in_by_pos ? ti.p0 : 0;
+    const int in_rows = a.in_by_pos ? ti.rows : a.T;
+    const auto rA = rsrc_i8(a.qin + (size_t)in0 * K, (uint32_t)in_rows * K);
+    const auto rX = rsrc_i8(a.sin + (size_t)in0 * G, (uint32_t)in_rows * G * 4);
 
-    // staging assignment (fixed for the tile).  A step holds KG * 64 bytes of
-    // every activation row and KG * 32 bytes of every weight row; lanes are
-    // laid out so that one load instruction of a wave reads whole row
-    // segments (LA lanes x 16 B per activation row, LB per weight row).
-    constexpr int LA = 4 * KG, LB = 2 * KG;
-    constexpr int NA = BM * LA / 256;           // activation loads per thread
-    constexpr int NB = kBN * LB / 256;          // weight loads per thread
-    const int a_byte = (tid % LA) * 16;         // byte within the row segment
-    int a_in[NA];
-    bool a_ok[NA];
+    // Staging, fixed for the tile.  A step holds 128 bytes (two groups) of
+    // every activation row and 64 bytes of every packed weight row: thread
+    // tid loads 16 bytes at (tid & 7) * 16 of activation rows (tid >> 3) +
+    // 32 i and at (tid & 3) * 16 of weight rows (tid >> 2) + 64 i, so a
+    // wave's load instruction reads whole row segments.  Threads r < 128
+    // load row r's activation scales, threads 128 + r weight row r's.  Rows
+    // past the tile read the tile's last row (their results are not stored),
+    // weight rows past the matrix read 0, and the second group of the last
+    // step of an odd group count is never used.
+    const int a_byte = (tid & 7) * 16;
+    uint32_t a_off[4];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-        const int m = tid / LA + (256 / LA) * i;
-        int o_;
-        tile_row(a, ti, m, a_in[i], o_);
-        a_ok[i] = m < ti.rows;
+    for (int i = 0; i < 4; ++i) {
+        int ir, orow;
+        tile_row(a, ti, (tid >> 3) + 32 * i, ir, orow);
+        a_off[i] = (uint32_t)(ir - in0) * K + a_byte;
     }
-    const int b_byte = (tid % LB) * 16;
-    int b_row[NB];
+    // weight rows: a wave covers 16 rows per round, 4 lanes per row, and the
+    // 8 lanes of each LDS write pass hold rows r and r + 4 (disjoint banks at
+    // the 80-byte row stride)
+    const int b_byte = (tid & 3) * 16;
+    const int b_row = 16 * (tid >> 6) + ((tid >> 3) & 3) + 4 * ((tid >> 2) & 1) + 8 * ((tid >> 5) & 1);
+    uint32_t b_off[2];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) b_row[i] = wrow(tid / LB + (256 / LB) * i);
-    int x_in = 0, x_out;
-    if (tid < BM) tile_row(a, ti, tid, x_in, x_out);
-    const bool x_ok = tid < BM && tid < ti.rows;
-    const int s_row = tid < kBN ? wrow(tid) : -1;
+    for (int i = 0; i < 2; ++i) {
+        const int r = wrow(b_row + 64 * i);
+        b_off[i] = r >= 0 ? (uint32_t)r * rb + b_byte : kOOB8;
+    }
+    const bool x_thread = tid < BM;  // waves 0 and 1
+    uint32_t s_off;
+    if (x_thread) {
+        int ir, orow;
+        tile_row(a, ti, tid, ir, orow);
+        s_off = (uint32_t)(ir - in0) * G * 4;
+    } else {
+        const int r = wrow(tid - BM);
+        s_off = r >= 0 ? (uint32_t)r * G * 2 : kOOB8;
+    }
 
-    const int nsteps = (G + kKG - 1) / kKG;
-    // load_step only issues loads (raw values land in registers while the
-    // current step computes); store_step masks, converts and writes them to
-    // LDS after the compute, so no load is waited for before it is needed
-    uint4 ra[NA], rbw[NB];
-    float rx[kKG];
-    uint32_t rs_[kKG];
+    const int nsteps = (G + KG - 1) / KG;
+    uint4 ra[4], rbw[2];
+    uint32_t rs[KG];
+    // load_step only issues loads (their values land while the current step
+    // computes); store_step writes them to LDS after the compute
     auto load_step = [&](int ks) {
-        const int g0 = ks * kKG;
-        const int ga = g0 + a_byte / 64, gb = g0 + b_byte / 32;
-        // activation rows can exceed a 32-bit buffer range: 64-bit addresses;
-        // rows and groups past the tile read row 0 and are zeroed later
+        const int g0 = ks * KG;
+        if (g0 + KG <= G) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const bool ok = a_ok[i] && ga < G;
-            ra[i] = *reinterpret_cast<const uint4 *>(
-                a.qin + (ok ? (size_t)a_in[i] * K + g0 * 64 + a_byte : 0));
-        }
+            for (int i = 0; i < 4; ++i)
+                ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, a_off[i], g0 * 64, 0));
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const uint32_t off = (b_row[i] >= 0 && gb < G)
-                ? (uint32_t)((size_t)b_row[i] * rb + g0 * 32 + b_byte) : kOOB8;
-            rbw[i] = ld16(rB, off);
-        }
-        // scales: every thread issues the same loads (no branches around
-        // loads); threads without a row read an out-of-range offset
+            for (int i = 0; i < 2; ++i)
+                rbw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, b_off[i], g0 * 32, 0));
 #pragma unroll
-        for (int j = 0; j < kKG; ++j) {
-            const int g = g0 + j;
-            rx[j] = a.sin[(x_ok && g < G) ? (size_t)x_in * G + g : 0];
-            const uint32_t so = (s_row >= 0 && g < G) ? (uint32_t)((size_t)s_row * G + g) * 2 : kOOB8;
-            rs_[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, so, 0, 0);
+            for (int j = 0; j < KG; ++j) {
+                if (x_thread) rs[j] = __builtin_amdgcn_raw_buffer_load_b32(rX, s_off, (g0 + j) * 4, 0);
+                else rs[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, s_off, (g0 + j) * 2, 0);
+            }
+        } else {
+            // the last step of an odd group count: its second group lies past
+            // the rows, so those lanes read nothing (out-of-range offsets)
+            const bool a_in = g0 + (a_byte >> 6) < G, b_in = g0 + (b_byte >> 5) < G;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rA, a_in ? a_off[i] : kOOB8, g0 * 64, 0));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                rbw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rB, b_in ? b_off[i] : kOOB8, g0 * 32, 0));
+            if (x_thread) rs[0] = __builtin_amdgcn_raw_buffer_load_b32(rX, s_off, g0 * 4, 0);
+            else rs[0] = __builtin_amdgcn_raw_buffer_load_b16(rS, s_off, g0 * 2, 0);
+#pragma unroll
+            for (int j = 1; j < KG; ++j) rs[j] = 0;
         }
     };
-    auto store_step = [&](int buf, int ks) {
-        const int g0 = ks * kKG;
-        const int ga = g0 + a_byte / 64;
+    auto store_step = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            // zero by mask, component-wise (a select of whole vectors gets
-            // lowered through scratch memory)
-            const uint32_t m = (a_ok[i] && ga < G) ? 0xFFFFFFFFu : 0u;
-            const uint4 v = ra[i];
-            *reinterpret_cast<uint4 *>(sm.a[buf] + (tid / LA + (256 / LA) * i) * kAS + a_byte) =
-                make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-        }
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(sm.a[buf] + ((tid >> 3) + 32 * i) * AS + a_byte) = ra[i];
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            uint8_t *dst = sm.b[buf] + (tid / LB + (256 / LB) * i) * kBS;
-            if constexpr (UB) {
-                *reinterpret_cast<v4i *>(dst + 2 * b_byte) = unpack_b(make_uint2(rbw[i].x, rbw[i].y));
-                *reinterpret_cast<v4i *>(dst + 2 * b_byte + 16) = unpack_b(make_uint2(rbw[i].z, rbw[i].w));
+        for (int i = 0; i < 2; ++i)
+            *reinterpret_cast<uint4 *>(sm.b[buf] + (b_row + 64 * i) * BS + b_byte) = rbw[i];
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+            if (x_thread) {
+                const float sr = epi_act_scale(__uint_as_float(rs[j]));
+                sm.sx[buf][j][tid] = sr;
+                sm.nm[buf][j][tid] = -kEpiM * sr;
             } else {
-                *reinterpret_cast<uint4 *>(dst + b_byte) = rbw[i];
+                sm.sw[buf][j][tid - BM] = f16_to_f32((uint16_t)rs[j]) * 0.0625f;
             }
         }
-#pragma unroll
-        for (int j = 0; j < kKG; ++j) {
-            const int g = g0 + j;
-            if (tid < BM) sm.sx[buf][j][tid] = (x_ok && g < G) ? rx[j] : 0.f;
-            if (tid < kBN) sm.sw[buf][j][tid] = f16_to_f32((uint16_t)rs_[j]) * 0.0625f;
-        }
     };
 
-    // this wave's local rows: A rows wm * BM/2 + 16 mt + n, B rows lb[nt] + n
+    // this wave's B rows lb[nt] + n; its m-tile i covers rows 32 i + 16 wm ..
     int lb[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-        lb[nt] = GATEUP ? ((nt < 2) ? 32 * wn + 16 * nt : kBN / 2 + 32 * wn + 16 * (nt - 2))
+        lb[nt] = GATEUP ? ((nt < 2) ? 32 * wn + 16 * nt : BN / 2 + 32 * wn + 16 * (nt - 2))
                         : 64 * wn + 16 * nt;
-    const int arow0 = wm * (BM / 2);
-    // a wave whose half of the tile holds no row skips its MFMAs (one
-    // uniform branch per group keeps the MFMA/epilogue block in one piece)
-    const bool wave_live = arow0 < ti.rows;
-    float out[MT][4][4];
+    // m-tiles of this wave that hold a row of the tile (a prefix of i)
+    const int nlive = LIST == kFullTiles ? 4 : min(4, (ti.rows - 16 * wm + 31) >> 5);
+    float out[4][4][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[mt][nt][i] = 0.f;
+            for (int r = 0; r < 4; ++r) out[i][nt][r] = 0.f;
     // dump bookkeeping (tests only)
-    int d_out[MT][4], d_row[4];
+    int d_out[4][4], d_row[4];
     if constexpr (DUMP) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int r = 0; r < 4; ++r) {
                 int ir;
-                tile_row(a, ti, arow0 + mt * 16 + 4 * q + i, ir, d_out[mt][i]);
+                tile_row(a, ti, 32 * i + 16 * wm + 4 * q + r, ir, d_out[i][r]);
             }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) d_row[nt] = wrow(lb[nt] + n);
     }
 
-    load_step(0);
-    store_step(0, 0);
-    __syncthreads();
-    const v4i zero = {0, 0, 0, 0};
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nsteps) load_step(ks + 1);
+    // one K step on LDS buffer buf (a constant after unrolling, so every LDS
+    // address is a base register plus an immediate)
+    const v4i cmag = {kEpiMBits, kEpiMBits, kEpiMBits, kEpiMBits};
+    // A full step (every m-tile of the wave holds rows, both groups inside K;
+    // not the dump variant): the 8 (group, m-tile) units as one straight-line
+    // pipeline -- the MFMAs of unit u are issued next to the epilogue of unit
+    // u - 1, so one wave feeds the matrix core and the VALU together.  Each
+    // output still adds its group terms in ascending group order.
+    // A step of the full- and partial-tile launches (even group count): the
+    // 2 * NL (group, m-tile) units of a wave with NL live m-tiles, unit u =
+    // (u / NL, u % NL), as one straight-line pipeline -- the MFMAs of unit u
+    // are issued next to the epilogue of unit u - 1.  Each output still adds
+    // its group terms in ascending group order.
+    auto step_units = [&](const int buf, auto nl_c) {
+        constexpr int NL = decltype(nl_c)::value, NU = 2 * NL;
+        v4i pb[KG][4];
+        float psw[KG][4];
+        v4i pa[NU];
+        float psx[NU][4], pnm[NU][4];
+        v4i pc[NU][4];
+        auto read_b = [&](const int j) {
 #pragma unroll
-        for (int j = 0; j < kKG; ++j) {
-            const int g = ks * kKG + j;
-            if (wave_live && g < G) {
-                // fragments of the group, then all its MFMAs, then the epilogue
-                // (no MFMA result is consumed right after its issue)
-                v4i bv[4], av[MT];
-                float sw[4], sx[MT][4];
+            for (int nt = 0; nt < 4; ++nt) {
+                pb[j][nt] = unpack_b(*reinterpret_cast<const uint2 *>(
+                    sm.b[buf] + (lb[nt] + n) * BS + j * 32 + 8 * q));
+                psw[j][nt] = sm.sw[buf][j][lb[nt] + n];
+            }
+        };
+        auto read_a = [&](const int u) {
+            const int j = u / NL, r0 = 32 * (u % NL) + 16 * wm;
+            pa[u] = *reinterpret_cast<const v4i *>(sm.a[buf] + (r0 + n) * AS + j * 64 + 16 * q);
+            const float4 sx4 = *reinterpret_cast<const float4 *>(&sm.sx[buf][j][r0 + 4 * q]);
+            const float4 nm4 = *reinterpret_cast<const float4 *>(&sm.nm[buf][j][r0 + 4 * q]);
+            psx[u][0] = sx4.x; psx[u][1] = sx4.y; psx[u][2] = sx4.z; psx[u][3] = sx4.w;
+            pnm[u][0] = nm4.x; pnm[u][1] = nm4.y; pnm[u][2] = nm4.z; pnm[u][3] = nm4.w;
+        };
+        auto mfma = [&](const int u) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                pc[u][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[u], pb[u / NL][nt], cmag, 0, 0, 0);
+        };
+        auto epi = [&](const int u) {
+            const int i = u % NL, j = u / NL;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    out[i][nt][r] = fmaf(fmaf(__int_as_float(pc[u][nt][r]), psx[u][r], pnm[u][r]),
+                                         psw[j][nt], out[i][nt][r]);
+                // pin the unit's results here: the compiler would otherwise
+                // sink the epilogue below the step and keep every MFMA
+                // result alive until then
+                asm volatile("" : "+v"(out[i][nt][0]), "+v"(out[i][nt][1]), "+v"(out[i][nt][2]),
+                             "+v"(out[i][nt][3]));
+            }
+        };
+        // scheduling barriers keep the units in order (the compiler would
+        // otherwise hoist every unit's reads and MFMAs and run out of
+        // registers); inside a unit it interleaves the MFMAs with the
+        // previous unit's epilogue
+        read_b(0);
+        read_a(0);
+        read_a(1);
+        mfma(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 1; u < NU; ++u) {
+            if (u + 1 < NU) read_a(u + 1);
+            if (u == (NL > 1 ? NL - 1 : 1)) read_b(1);
+            mfma(u);
+            epi(u - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        epi(NU - 1);
+    };
+    // one K step of the general path (the dump variant and odd group
+    // counts): per group, the live m-tiles one after another
+    auto step_general = [&](const int ks, const int buf) {
+#pragma unroll
+        for (int j = 0; j < KG; ++j) {
+            const int g = ks * KG + j;
+            if (g < G && nlive > 0) {
+                v4i bv[4];
+                float sw[4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    if constexpr (UB)
-                        bv[nt] = *reinterpret_cast<const v4i *>(sm.b[buf] + (lb[nt] + n) * kBS + j * 64 + 16 * q);
-                    else
-                        bv[nt] = unpack_b(*reinterpret_cast<const uint2 *>(
-                            sm.b[buf] + (lb[nt] + n) * kBS + j * 32 + 8 * q));
+                    bv[nt] = unpack_b(*reinterpret_cast<const uint2 *>(
+                        sm.b[buf] + (lb[nt] + n) * BS + j * 32 + 8 * q));
                     sw[nt] = sm.sw[buf][j][lb[nt] + n];
                 }
-                // m-tiles in pairs: fewer MFMA results live at once
 #pragma unroll
-                for (int m2 = 0; m2 < MT; m2 += 2) {
+                for (int i = 0; i < 4; ++i) {
+                    if (i >= nlive) break;
+                    // the m-tile's A fragment and scales, 4 MFMAs, the epilogue
+                    const int r0 = 32 * i + 16 * wm;
+                    v4i av = *reinterpret_cast<const v4i *>(sm.a[buf] + (r0 + n) * AS + j * 64 + 16 * q);
+                    // keeps the MFMAs inside the m-tile's branch (hoisted, all
+                    // 16 results of a group would be alive at once)
+                    asm volatile("" : "+v"(av));
+                    const float4 sx4 = *reinterpret_cast<const float4 *>(&sm.sx[buf][j][r0 + 4 * q]);
+                    const float4 nm4 = *reinterpret_cast<const float4 *>(&sm.nm[buf][j][r0 + 4 * q]);
+                    const float sx[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
+                    const float nm[4] = {nm4.x, nm4.y, nm4.z, nm4.w};
+                    // c = kEpiM + 16 acc (as fp32 bits), so the group term
+                    // 16 acc * s' is one FMA and the weight scale a second
+                    v4i c[4];
 #pragma unroll
-                    for (int mt = m2; mt < m2 + 2; ++mt) {
-                        av[mt] = *reinterpret_cast<const v4i *>(
-                            sm.a[buf] + (arow0 + mt * 16 + n) * kAS + j * 64 + 16 * q);
-                        const float4 sx4 = *reinterpret_cast<const float4 *>(
-                            &sm.sx[buf][j][arow0 + mt * 16 + 4 * q]);
-                        sx[mt][0] = sx4.x; sx[mt][1] = sx4.y; sx[mt][2] = sx4.z; sx[mt][3] = sx4.w;
-                    }
-                    v4i c[2][4];
+                    for (int nt = 0; nt < 4; ++nt)
+                        c[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv[nt], cmag, 0, 0, 0);
 #pragma unroll
-                    for (int mm = 0; mm < 2; ++mm)
+                    for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            c[mm][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[m2 + mm], bv[nt], zero, 0, 0, 0);
+                        for (int r = 0; r < 4; ++r)
+                            out[i][nt][r] = fmaf(fmaf(__int_as_float(c[nt][r]), sx[r], nm[r]), sw[nt],
+                                                 out[i][nt][r]);
+                        if constexpr (DUMP) {
 #pragma unroll
-                    for (int mm = 0; mm < 2; ++mm) {
-                        const int mt = m2 + mm;
-#pragma unroll
-                        for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                out[mt][nt][i] = fmaf((float)c[mm][nt][i] * sx[mt][i], sw[nt], out[mt][nt][i]);
-                            if constexpr (DUMP) {
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    if (arow0 + mt * 16 + 4 * q + i < ti.rows && d_row[nt] >= 0)
-                                        a.dump_acc[((size_t)d_out[mt][i] * a.N + d_row[nt]) * G + g] =
-                                            c[mm][nt][i] >> 4;
-                            }
+                            for (int r = 0; r < 4; ++r)
+                                if (r0 + 4 * q + r < ti.rows && d_row[nt] >= 0)
+                                    a.dump_acc[((size_t)d_out[i][r] * a.N + d_row[nt]) * G + g] =
+                                        (c[nt][r] - kEpiMBits) >> 4;
                         }
                     }
                 }
             }
         }
-        if (ks + 1 < nsteps) store_step(buf ^ 1, ks + 1);
+    };
+    // the K loop: double-buffered stages, the next step's loads issued before
+    // the current step computes; NL live m-tiles (pipelined steps) or the
+    // general path (nl_c < 0)
+    auto kloop = [&](auto nl_c) {
+        constexpr int NL = decltype(nl_c)::value;
+        auto step = [&](const int ks, const int buf) {
+            if (ks + 1 < nsteps) load_step(ks + 1);
+            if constexpr (NL > 0) step_units(buf, nl_c);
+            else if constexpr (NL < 0) step_general(ks, buf);
+            if (ks + 1 < nsteps) store_step(buf ^ 1);
+            __syncthreads();
+        };
+        load_step(0);
+        store_step(0);
         __syncthreads();
+        for (int ks = 0; ks < nsteps; ks += 2) {
+            step(ks, 0);
+            if (ks + 1 < nsteps) step(ks + 1, 1);
+        }
+    };
+    if constexpr (LIST == kAllTiles) {
+        kloop(std::integral_constant<int, -1>{});
+    } else if constexpr (LIST == kFullTiles) {
+        kloop(std::integral_constant<int, 4>{});
+    } else {
+        // each live m-tile count its own loop (so each has its own register
+        // allocation); a wave without rows only stages and waits
+        switch (nlive) {
+        case 4: kloop(std::integral_constant<int, 4>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        default: kloop(std::integral_constant<int, 0>{}); break;
+        }
     }
 
     if constexpr (GATEUP) {
         // SwiGLU, then int8 quantisation of h per (row, 64-group [nb0, nb0 + 64)):
         // amax over the group's 64 columns = 16 lanes x 2 n-tiles x 2 waves (wn).
-        float h[MT][2][4];
+        float h[4][2][4];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int r = 0; r < 4; ++r) {
                 float m = 0.f;
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    const float gg = out[mt][nt][i], uu = out[mt][nt + 2][i];
-                    h[mt][nt][i] = gg / (1.0f + expf(-gg)) * uu;
-                    m = fmaxf(m, fabsf(h[mt][nt][i]));
+                    const float gg = out[i][nt][r], uu = out[i][nt + 2][r];
+                    h[i][nt][r] = gg / (1.0f + expf(-gg)) * uu;
+                    m = fmaxf(m, fabsf(h[i][nt][r]));
                 }
                 m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, true)));
                 m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, true)));
                 m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, true)));
                 m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x128, 0xF, 0xF, true)));
-                if (n == 0) sm.amax[wn][arow0 + mt * 16 + 4 * q + i] = m;
+                if (n == 0) sm.amax[wn][32 * i + 16 * wm + 4 * q + r] = m;
             }
         __syncthreads();
         const int G2 = a.I / 64;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = arow0 + mt * 16 + 4 * q + i;
+            for (int r = 0; r < 4; ++r) {
+                const int m = 32 * i + 16 * wm + 4 * q + r;
                 if (m >= ti.rows) continue;
                 const float amax = fmaxf(sm.amax[0][m], sm.amax[1][m]);
-                int ir, orow;
-                tile_row(a, ti, m, ir, orow);
+                const size_t pos = (size_t)ti.p0 + m;
+                int orow = 0;
+                if constexpr (DUMP) {
+                    int ir;
+                    tile_row(a, ti, m, ir, orow);
+                }
                 const float sc = amax > 0.f ? amax / 127.0f : 0.f;
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int col = nb0 + 32 * wn + 16 * nt + n;
                     int8_t code = 0;
                     if (amax > 0.f) {
-                        float r = rintf(h[mt][nt][i] / sc);
-                        r = fminf(fmaxf(r, -127.f), 127.f);
-                        code = (int8_t)r;
+                        float v = rintf(h[i][nt][r] / sc);
+                        v = fminf(fmaxf(v, -127.f), 127.f);
+                        code = (int8_t)v;
                     }
-                    a.qh[(size_t)orow * a.I + perm8_pos(col)] = code;
+                    a.qh[pos * a.I + perm8_pos(col)] = code;
                     if (DUMP) a.dump_qh[(size_t)orow * a.I + col] = code;
                 }
                 if (wn == 0 && n == 0) {
-                    a.sh[(size_t)orow * G2 + nb0 / 64] = sc;
+                    a.sh[pos * G2 + nb0 / 64] = sc;
                     if (DUMP) a.dump_sh[(size_t)orow * G2 + nb0 / 64] = sc;
                 }
             }
     } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = arow0 + mt * 16 + 4 * q + i;
+            for (int r = 0; r < 4; ++r) {
+                const int m = 32 * i + 16 * wm + 4 * q + r;
                 if (m >= ti.rows) continue;
                 int ir, orow;
                 tile_row(a, ti, m, ir, orow);
@@ -512,7 +696,7 @@ __global__ __launch_bounds__(256, OCC) void ggemm_kernel(I8Args a)
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     const int col = nb0 + lb[nt] + n;
-                    if (col < a.N) op[col] = out[mt][nt][i];
+                    if (col < a.N) op[col] = out[i][nt][r];
                 }
             }
     }
@@ -533,7 +717,7 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     const int64_t ng = (int64_t)T * (L.H / 64);
     int32_t *dump = io.acc_dump;
     uint8_t *dump_b = reinterpret_cast<uint8_t *>(dump);
-    launch(mk, quant_rows_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, st, io.x, ng,
+    launch(mk, quant_rows_kernel, dim3((unsigned)((ng + 15) / 16)), dim3(256), 0, st, io.x, ng,
            L.H, qx, sx, dump ? reinterpret_cast<int8_t *>(dump_b + io.dump.qx) : nullptr,
            dump ? reinterpret_cast<float *>(dump_b + io.dump.sx) : nullptr);
     hipError_t err = hipGetLastError();
@@ -543,13 +727,8 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     if (T <= kI8StreamTMax)
         return launch_forward_i8_small(L, io, qx, sx, reinterpret_cast<float *>(io.ws + lay.h), o,
                                        st, mk);
-    // 64-row tiles: measured on MI355X they beat 128-row tiles even for dense
-    // entries (three workgroups per CU instead of two) and waste fewer rows on
-    // the last, partial tile of each entry
-    constexpr int kTileRows = 64;
-    const int tile_m = kTileRows;
     launch(mk, schedule_kernel, dim3(1), dim3(1024), 0, st, io.offsets, io.n_union,
-                       (int)lay.cap, T, L.n_shared, tile_m, tiles, (int)lay.max_tiles);
+                       (int)lay.cap, T, L.n_shared, kTileM, tiles, (int)lay.max_tiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     I8Args a{};
@@ -557,29 +736,45 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.tiles = tiles; a.max_tiles = (int)lay.max_tiles;
     a.T = T; a.k = L.k; a.cap = (int)lay.cap; a.I = L.I; a.H = L.H;
     a.qh = qh; a.sh = sh; a.o = o;
-    a.qin = qx; a.sin = sx; a.in_by_slot = 0;
+    a.qin = qx; a.sin = sx; a.in_by_pos = 0;
     a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
     a.N = 2 * L.I; a.K = L.H;
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc13) : nullptr;
     a.dump_qh = dump ? reinterpret_cast<int8_t *>(dump_b + io.dump.qh) : nullptr;
     a.dump_sh = dump ? reinterpret_cast<float *>(dump_b + io.dump.sh) : nullptr;
+    // grid y: bounds of the two lists (full tiles: T*k/128 routed plus
+    // T/128 shared; partial tiles: one per entry)
+    const unsigned y_full = (unsigned)std::max<int64_t>(1, (T * L.k) / kTileM + L.n_shared * (T / kTileM));
+    const unsigned y_part = (unsigned)(lay.cap + L.n_shared);
 #define COLI_GG(GU_, GX_)                                                                      \
     {                                                                                          \
-        const dim3 grid(GX_, (unsigned)lay.max_tiles);                                         \
-        if (dump) launch(mk, (ggemm_kernel<kTileRows, 2, GU_, true>), grid, dim3(256), 0, st, a); \
-        else launch(mk, (ggemm_kernel<kTileRows, 2, GU_, false>), grid, dim3(256), 0, st, a);     \
+        if (dump || ((a.K / 64) & 1)) {                                                        \
+            /* the dump variant, and odd group counts: one launch over both lists */            \
+            if (dump)                                                                          \
+                launch(mk, (ggemm_kernel<GU_, true, kAllTiles>), dim3(GX_, (unsigned)lay.max_tiles), \
+                       dim3(256), 0, st, a);                                                   \
+            else                                                                               \
+                launch(mk, (ggemm_kernel<GU_, false, kAllTiles>), dim3(GX_, (unsigned)lay.max_tiles), \
+                       dim3(256), 0, st, a);                                                   \
+        } else {                                                                               \
+            launch(mk, (ggemm_kernel<GU_, false, kFullTiles>), dim3(GX_, y_full), dim3(256),     \
+                   0, st, a);                                                                  \
+            launch(mk, (ggemm_kernel<GU_, false, kPartialTiles>), dim3(GX_, y_part), dim3(256),  \
+                   0, st, a);                                                                  \
+        }                                                                                      \
         if ((err = hipGetLastError()) != hipSuccess) return err;                               \
     }
-    // gate/up: grid x = 64-unit column blocks (32 for I = 2048: a multiple of 8,
-    // so the m-tiles of one entry and column block land on one XCD's L2)
-    COLI_GG(true, L.I / (kBN / 2))
+    // gate/up: grid x = column blocks of 64 units (32 for I = 2048: a multiple
+    // of 8, so a column block runs on one XCD for every tile and the tiles of
+    // an entry share that XCD's L2 copy of its weight rows)
+    COLI_GG(true, L.I / (kGBN / 2))
     // down
-    a.qin = qh; a.sin = sh; a.in_by_slot = 1;
+    a.qin = qh; a.sin = sh; a.in_by_pos = 1;
     a.w = L.w2; a.s = L.s2; a.sh_w = L.sh_w2; a.sh_s = L.sh_s2;
     a.N = L.H; a.K = L.I;
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc2) : nullptr;
     a.dump_qh = nullptr; a.dump_sh = nullptr;
-    COLI_GG(false, (L.H + kBN - 1) / kBN)
+    COLI_GG(false, (L.H + kGBN - 1) / kGBN)
 #undef COLI_GG
     err = io.combine
         ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st, mk)

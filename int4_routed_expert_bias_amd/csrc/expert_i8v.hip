@@ -10,7 +10,9 @@
 //   acc_g  = exact int32 sum over the 64-group g of (int8 activation code) x
 //            (16 x int4 code), here from v_dot4_i32_i8 instead of the MFMA;
 //   out    = 0; for g ascending: out = fma(float(acc_g) * act_scale_g,
-//            w_scale_g / 16, out)    (fp32, one chain per output);
+//            w_scale_g / 16, out)    (fp32, one chain per output), the
+//            activation scale rounded to 22 significant bits
+//            (epi_act_scale);
 //   h      = g / (1 + exp(-g)) * u, quantised per 64-group of I with
 //            scale = amax / 127, code = clamp(rint(h / scale), +-127).
 // Only the work split differs: the weights are streamed once by persistent
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void gateup_i8v_kernel(I8vArgs a, RouteSelf r)
             const uint4 lo = src[0], hi = src[1];
             xq[j][p][0] = lo.x; xq[j][p][1] = lo.y; xq[j][p][2] = lo.z; xq[j][p][3] = lo.w;
             xq[j][p][4] = hi.x; xq[j][p][5] = hi.y; xq[j][p][6] = hi.z; xq[j][p][7] = hi.w;
-            xs[j][p] = a.sx[(size_t)tok * G + (c >> 1)];
+            xs[j][p] = epi_act_scale(a.sx[(size_t)tok * G + (c >> 1)]);
         }
     };
     if constexpr (ROUTE) load_x(0, 0);
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256) void down_i8v_kernel(I8vArgs a)
             for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
             amax = fmaxf(amax, pair_lane_f(amax));
             const float sc = amax > 0.f ? amax / 127.0f : 0.f;
-            xs[j][p] = sc;
+            xs[j][p] = epi_act_scale(sc);
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
                 uint32_t ev = 0, od = 0;

@@ -21,9 +21,9 @@ __device__ __forceinline__ float sigmoid_fp64(float l)
 }
 
 // --- top-k: one wave per token, 4 tokens per workgroup -------------------
-// Radix select: the k-th largest key is found two bits at a time with wave
-// ballots (16 rounds, no shuffles); keys equal to it are taken in expert order; the
-// k winners are then ordered by (key desc, expert asc) through LDS.
+// k rounds of a wave maximum: each round takes the largest key left, the
+// lowest expert among equal keys (a ballot), so the winners come out in
+// selection order (key desc, expert asc) without a ranking step.
 
 // Monotone map of an fp32 key to uint32 (larger float -> larger integer);
 // -0 is folded into +0 first so that equal keys compare equal.
@@ -31,6 +31,22 @@ __device__ __forceinline__ uint32_t order_bits(float z)
 {
     const uint32_t u = __float_as_uint(z + 0.0f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Largest v over the wave, in every lane: DPP steps inside the 16-lane rows
+// (neighbour, pair of neighbours, half-row mirror, row mirror), then the
+// four row maxima read out.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
 }
 
 // Logit of (t, e) for S >= 1: the fp64 partials of the S K-splits added in
@@ -64,7 +80,7 @@ struct UnionOut {
 // barriers, so every wave of the 256-thread workgroup must call this).
 // ids / w are indexed by token (t * k + rank); with UNION the workgroup's
 // tokens (T <= 4, t0 = 0) also form the batch union into uo.
-// TL: timeline marks 4 (keys loaded), 5 (threshold found), 6 (selection
+// TL: timeline marks 4 (keys loaded), 5 (selection found), 6 (selection
 // and union written) into tl (measurement variants only).
 template <int KPL, bool UNION, bool TL = false>
 __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
@@ -75,10 +91,6 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
                                              uint64_t *tl = nullptr, int tl_cap = 0)
 {
     __shared__ int32_t sid[64];  // the batch's selections (UNION)
-    __shared__ uint32_t sk[4][COLI_MAX_K_DEV];
-    __shared__ int32_t se[4][COLI_MAX_K_DEV];
-    __shared__ float ss[4][COLI_MAX_K_DEV];
-    __shared__ float sg[4][64 * KPL];  // each expert's sigmoid score, per wave
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int t = t0 + wv;
@@ -113,99 +125,66 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
     }
     tl_mark<TL>(tl, tl_cap, 4);
     uint32_t key[KPL];
+    float sgm[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        const float sgm = S == 0 ? lg[i] : sigmoid_fp64(lg[i]);
-        sg[wv][e] = sgm;
-        key[i] = (live && e < E) ? order_bits(sgm + bs[i]) : 0u;
+        sgm[i] = S == 0 ? lg[i] : sigmoid_fp64(lg[i]);
+        key[i] = (live && e < E) ? order_bits(sgm[i] + bs[i]) : 0u;
     }
-    // largest tau with #{key >= tau} >= k  (valid keys are >= 1), two bits
-    // per round: the counts of the three candidates of a round are
-    // independent (their ballots overlap, where one bit per round would wait
-    // for each count before the next compare)
-    uint32_t tau = 0;
-    for (int b = 30; b >= 0; b -= 2) {
-        const uint32_t c1 = tau | (1u << b), c2 = tau | (2u << b), c3 = tau | (3u << b);
-        int n1 = 0, n2 = 0, n3 = 0;
+    // The k winners in selection order: round j takes the largest key left
+    // (the lowest expert among equal keys) and removes it.  Lane j keeps
+    // winner j's expert and score; the scores add up in selection order.
+    int my_e = 0;
+    float my_s = 0.f, sum = 0.f;
+    if (live) {
+        for (int j = 0; j < k; ++j) {
+            uint32_t m = key[0];
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            n1 += __popcll(__ballot(key[i] >= c1));
-            n2 += __popcll(__ballot(key[i] >= c2));
-            n3 += __popcll(__ballot(key[i] >= c3));
+            for (int i = 1; i < KPL; ++i) m = max(m, key[i]);
+            m = wave_max_u32(m);
+            int e = -1;
+            float sc = 0.f;
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) {
+                if (e < 0) {
+                    const uint64_t b = __ballot(key[i] == m);
+                    if (b) {
+                        const int l = __builtin_ctzll(b);
+                        e = 64 * i + l;
+                        sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sgm[i]), l));
+                        if (lane == l) key[i] = 0u;
+                    }
+                }
+            }
+            if (lane == j) {
+                my_e = e;
+                my_s = sc;
+            }
+            sum += sc;  // fp32, selection order
         }
-        tau = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : tau;
     }
     tl_mark<TL>(tl, tl_cap, 5);
-    int gt = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) gt += __popcll(__ballot(key[i] > tau));
-    const int need = k - gt;  // keys equal to tau to take, lowest experts first
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int eq_before = 0, sel_before = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const uint64_t eqm = __ballot(key[i] == tau);
-        const bool is_eq = key[i] == tau;
-        const bool sel = key[i] > tau || (is_eq && eq_before + __popcll(eqm & lt_mask) < need);
-        const uint64_t selm = __ballot(sel);
-        if (sel && live && sel_before + __popcll(selm & lt_mask) < k) {
-            const int pos = sel_before + __popcll(selm & lt_mask);
-            sk[wv][pos] = key[i];
-            se[wv][pos] = lane + 64 * i;
-        }
-        eq_before += __popcll(eqm);
-        sel_before += __popcll(selm);
-    }
-    __syncthreads();
-    // lane j < k: rank of winner j among the winners, then its weight
-    uint32_t mk = 0;
-    int me = 0, rank = 0;
     if (live && lane < k) {
-        mk = sk[wv][lane];
-        me = se[wv][lane];
-        // all COLI_MAX_K_DEV entries read at once (one LDS round trip; the
-        // ones past k are not counted)
-#pragma unroll
-        for (int j = 0; j < COLI_MAX_K_DEV; ++j) {
-            const uint32_t ok = sk[wv][j];
-            const int oe = se[wv][j];
-            rank += (j < k && (ok > mk || (ok == mk && oe < me))) ? 1 : 0;
-        }
-    }
-    __syncthreads();
-    float sj = 0.f;
-    if (live && lane < k) {
-        sj = sg[wv][me];
-        ss[wv][rank] = sj;
-    }
-    __syncthreads();
-    if (live && lane < k) {
-        float sv[COLI_MAX_K_DEV];
-#pragma unroll
-        for (int j = 0; j < COLI_MAX_K_DEV; ++j) sv[j] = ss[wv][j];
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < COLI_MAX_K_DEV; ++j)
-            if (j < k) sum += sv[j];  // fp32, selection order
         // adaptive top-p: keep the shortest prefix of the selection whose
         // weights reach top_p (fp32, in order), renormalised over the kept
         int kp = k;
         if (top_p < 1.0f) {
             float c = 0.f;
             for (int m = 1; m <= k; ++m) {
-                c += ss[wv][m - 1] / sum;
+                c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), m - 1)) / sum;
                 if (c >= top_p) {
                     kp = m;
                     break;
                 }
             }
             sum = 0.f;
-            for (int j = 0; j < kp; ++j) sum += ss[wv][j];
+            for (int j = 0; j < kp; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
         }
-        ids[(size_t)t * k + rank] = rank < kp ? me : -1;
-        w[(size_t)t * k + rank] = rank < kp ? sj / sum : 0.f;
-        if constexpr (UNION) sid[t * k + rank] = rank < kp ? me : -1;
+        const int rank = lane;
+        ids[(size_t)t * k + rank] = rank < kp ? my_e : -1;
+        w[(size_t)t * k + rank] = rank < kp ? my_s / sum : 0.f;
+        if constexpr (UNION) sid[t * k + rank] = rank < kp ? my_e : -1;
     }
     if constexpr (UNION) {
         __syncthreads();

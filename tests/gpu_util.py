@@ -55,51 +55,82 @@ def check_route(gpu_ids, gpu_w, orc_ids, orc_w):
     assert_close(gpu_w, orc_w, "topk_w")
 
 
-def tile_rows(ids, union_ids, offsets, slots, n_union, T, k, n_shared, tile=64):
+def tile_rows(ids, union_ids, offsets, slots, n_union, T, k, n_shared, tile=128):
     """Rows of the expert outputs o to check so that the first and the last
-    tile of every union entry's row list hold a checked row (its first
-    row, the last row of its first full tile, its last row): a list of
+    tile of every union entry's row list hold a checked row (its first row,
+    the last rows of the first tile's two halves, its last row): a list of
     (o row, token, expert) with o row = slot t*k+j for a routed expert and
     T*k+t for the shared expert (expert -1)."""
     rows = []
     for u in range(n_union):
         a, b = int(offsets[u]), int(offsets[u + 1])
-        for p in sorted({a, min(a + tile - 1, b - 1), b - 1}):
+        for p in sorted({a, min(a + tile // 2 - 1, b - 1), min(a + tile - 1, b - 1), b - 1}):
             sl = int(slots[p])
             t, j = sl // k, sl % k
             assert ids[t, j] == union_ids[u]
             rows.append((sl, t, int(union_ids[u])))
     if n_shared:
-        for t in sorted({0, min(tile - 1, T - 1), T - 1}):
+        for t in sorted({0, min(tile // 2 - 1, T - 1), min(tile - 1, T - 1), T - 1}):
             rows.append((T * k + t, t, -1))
     return rows
 
 
-def workspace_o(bufs, R, H):
-    """The expert outputs o [R][H] fp32 that the forward leaves at offset 0
-    of its workspace (the library's workspace layout, both families)."""
+PERM8_INV = np.array([0, 4, 1, 5, 2, 6, 3, 7])  # natural element b sits at position PERM8_INV[b]
+
+
+def check_expert_rows_i8(orc, arrays, x, bufs, rows, T, k, n_shared, what):
+    """Int8 family, grouped GEMM (T > 4): for each listed (o row, token,
+    expert), the GPU's int8 codes of h and their scales (read from the
+    forward's workspace) against the oracle's -- every code within one of
+    the oracle's (a flip at a rounding boundary), flips rare overall -- and
+    the GPU's expert output against the oracle's down projection on the
+    GPU's own codes (the accumulators are exact given the operands).
+    Returns the fraction of flipped codes."""
+    H, I = arrays["H"], arrays["I"]
+    E = arrays["E"]
+    off = coli.i8_workspace_offsets(H, I, E, k, T, n_shared)
+    ws = bufs.workspace
+    R = T * k + n_shared * T
+    kept = int(bufs.offsets[int(bufs.n_union[0].item())].item())
+    slots = bufs.slots[:kept].cpu().numpy()
+    pos_of = np.full(T * k, -1, np.int64)
+    pos_of[slots] = np.arange(kept)
+    pos = np.array([pos_of[r[0]] if r[2] >= 0 else r[0] for r in rows])
+    assert (pos >= 0).all()
     import torch
-    return bufs.workspace[:R * H * 4].view(torch.float32).view(R, H)
+    G2 = I // 64
+    qh_all = ws[off["qh"]:off["qh"] + R * I].view(R, I)
+    sh_all = ws[off["sh"]:off["sh"] + R * G2 * 4].view(torch.float32).view(R, G2)
+    o_all = ws[off["o"]:off["o"] + R * H * 4].view(torch.float32).view(R, H)
+    pt = torch.tensor(pos, device=ws.device)
+    qh = qh_all[pt].cpu().numpy().view(np.int8).reshape(len(rows), -1, 8)[:, :, PERM8_INV]
+    qh = np.ascontiguousarray(qh.reshape(len(rows), I))
+    sh = sh_all[pt].cpu().numpy()
+    o = o_all[torch.tensor([r[0] for r in rows], device=ws.device)].cpu().numpy()
 
-
-def check_expert_rows(orc, arrays, x, o_rows, rows, mode, what):
-    """Each listed o row (o row, token, expert) against the oracle's output
-    of that expert for that token (the token's input row of x), within the
-    tolerance per row; rows run on a thread pool."""
-    import oracle as oracle_mod
-
-    def ref(r):
-        _, t, e = r
+    def weights(e):
         if e >= 0:
-            w = (arrays["w13"][e], arrays["s13"][e], arrays["w2"][e], arrays["s2"][e])
-        else:
-            w = (arrays["sh_w13"], arrays["sh_s13"], arrays["sh_w2"], arrays["sh_s2"])
-        f = orc.expert_i8 if mode == oracle_mod.ACT_I8 else orc.expert_f32
-        return f(*w, x[t])["o"]
+            return arrays["w13"][e], arrays["s13"][e], arrays["w2"][e], arrays["s2"][e]
+        return arrays["sh_w13"], arrays["sh_s13"], arrays["sh_w2"], arrays["sh_s2"]
 
-    refs = pool_map(ref, rows)
-    for i, (r, ro) in enumerate(zip(rows, refs)):
-        assert_close(o_rows[i], ro, f"{what}: o row {r[0]} (token {r[1]}, expert {r[2]})")
+    def ref(i):
+        _, t, e = rows[i]
+        w13, s13, w2, s2 = weights(e)
+        full = orc.expert_i8(w13, s13, w2, s2, x[t])
+        return full["qh"], full["sh"], orc.down_i8(w2, s2, qh[i], sh[i])
+
+    refs = pool_map(ref, range(len(rows)))
+    flips = 0
+    for i, (r, (qr, sr, og)) in enumerate(zip(rows, refs)):
+        tag = f"{what}: o row {r[0]} (token {r[1]}, expert {r[2]})"
+        d = np.abs(qh[i].astype(np.int32) - qr.astype(np.int32))
+        assert d.max() <= 1, f"{tag}: a code of h differs by {d.max()}"
+        flips += int((d > 0).sum())
+        assert_close(sh[i], sr, f"{tag}: scales of h")
+        assert_close(o[i], og, f"{tag}: down projection on the GPU's codes")
+    frac = flips / (len(rows) * I)
+    assert frac < 0.01, f"{what}: {frac:.2%} of the codes of h flipped"
+    return frac
 
 
 def orc_y_rows(orc, lay_orc, x_rows, ids_rows, w_rows, mode):

@@ -60,6 +60,20 @@ def test_workspace_bytes(L):
     assert coli.acc_dump_bytes(256, 128, 2, 4, 2) == 0
 
 
+def test_i8_workspace_offsets(L):
+    """The int8 family's intermediate regions lie inside the workspace, in
+    order, without overlap; batches of up to 4 tokens have none."""
+    H, I, E, k, T = 6144, 2048, 256, 8, 4096
+    off = coli.i8_workspace_offsets(H, I, E, k, T)
+    R = T * k + T
+    assert off["o"] + R * H * 4 <= off["qh"]
+    assert off["qh"] + R * I <= off["sh"]
+    assert off["sh"] + R * (I // 64) * 4 <= coli.workspace_bytes(H, I, E, k, T, coli.ACT_I8)
+    for bad in ((H, I, E, k, 4, 1), (H, I, E, k, T, 2), (6000, I, E, k, T, 1)):
+        with pytest.raises(coli.ColiError):
+            coli.i8_workspace_offsets(*bad)
+
+
 FAKE = 0x100000  # aligned, never dereferenced
 MIS = 0x100004   # 4-byte aligned only
 
