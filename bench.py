@@ -224,6 +224,31 @@ def stream_read_rate(hip, n_bufs=8, nbytes=188 << 20, reps=3):
             "kernel": "stream_read_kernel (coli_stream_read)"}
 
 
+def issue_sharing():
+    """Do the matrix core and the vector ALU of one SIMD issue in parallel?
+    coli_issue_probe's four modes on one workgroup per CU: MFMA only, FMA
+    only, one wave of each kind per SIMD, both in every wave (us per
+    workgroup, median over the workgroups)."""
+    import torch
+    import int4_routed_expert_bias_amd as coli
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ticks = torch.zeros((cus,), dtype=torch.int64, device="cuda")
+    sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    us = {}
+    for mode, name in enumerate(("mfma_only", "fma_only", "mfma_and_fma_waves", "mfma_and_fma_interleaved")):
+        for _ in range(2):
+            coli.issue_probe(mode, ticks, sink)
+        torch.cuda.synchronize()
+        us[name] = round(float(np.median(ticks.cpu().numpy())) / 100.0, 2)
+    # per SIMD: mode 2 runs half of mode 0's MFMAs and half of mode 1's FMAs
+    serial2 = (us["mfma_only"] + us["fma_only"]) / 2
+    return {"us_per_workgroup": us,
+            "mixed_waves_vs_serial_sum": round(us["mfma_and_fma_waves"] / serial2, 3),
+            "interleaved_vs_serial_sum": round(us["mfma_and_fma_interleaved"] /
+                                               (us["mfma_only"] + us["fma_only"]), 3),
+            "kernel": "issue_probe_kernel (coli_issue_probe)"}
+
+
 def percentiles(v):
     v = np.asarray(v, np.float64)
     return {"median": round(float(np.median(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
@@ -738,6 +763,7 @@ def main():
                 f"{r['roofline']['kernel_us']} us = {r['roofline']['frac']:.3f} of its roofline")
         out["workloads"] = extra
         out["hbm_read_ceiling"] = stream_read_rate(Hip())
+        out["simd_issue_sharing"] = issue_sharing()
     # clocks sampled every 20 ms while the headline workload ran on the GPU
     out["clocks_mhz"] = clk.summary()
     out["host"] = host_info()

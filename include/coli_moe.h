@@ -368,6 +368,19 @@ int coli_moe_device_check(void);
 int coli_stream_read(const void *buf, size_t bytes, uint32_t *out, int32_t n_groups,
                      void *hip_stream);
 
+/* For measurement only: whether one SIMD issues int8 MFMAs and fp32 vector
+ * FMAs in parallel (it sets the int8 GEMM's ceiling, whose epilogue is
+ * vector work).  n_groups workgroups of 8 waves (two per SIMD; 1..65536)
+ * run 2048 iterations of: mode 0, 4 independent v_mfma_i32_16x16x64_i8 per
+ * wave; mode 1, 16 independent fp32 FMAs per wave; mode 2, waves 0-3 the
+ * MFMAs of mode 0 and waves 4-7 the FMAs of mode 1; mode 3, every wave both,
+ * interleaved.  ticks[n_groups] (uint64) receives each workgroup's duration
+ * in wall-clock (100 MHz) ticks; sink (one int32) is written only to keep
+ * the work.  COLI_E_ARG for a bad mode, count or pointer, COLI_E_ALIGN for a
+ * misaligned one. */
+int coli_issue_probe(int32_t mode, int32_t n_groups, uint64_t *ticks, int32_t *sink,
+                     void *hip_stream);
+
 /* ---- Glue for stacking layers (outside the MoE layer itself) ------------
  * The pages do not describe the blocks around the MoE layer.  To run a
  * stack of synthetic layers without overflow, a unit-gain RMS pre-norm and

@@ -29,7 +29,7 @@ EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_i8_workspace_offsets", "coli_moe_strerror",
            "coli_moe_device_check",
-           "coli_rmsnorm", "coli_add_inplace", "coli_stream_read")
+           "coli_rmsnorm", "coli_add_inplace", "coli_stream_read", "coli_issue_probe")
 # every symbol declared in include/coli_mla.h
 MLA_EXPORTS = ("coli_mla_workspace_bytes", "coli_mla_decode", "coli_mla_decode_profiled")
 # every symbol declared in include/coli_place.h
@@ -96,6 +96,7 @@ def lib():
             "coli_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
             "coli_add_inplace": ([vp, vp, i64, vp], ctypes.c_int),
             "coli_stream_read": ([vp, sz, vp, i32, vp], ctypes.c_int),
+            "coli_issue_probe": ([i32, i32, vp, vp, vp], ctypes.c_int),
             "coli_moe_placer_create": ([i32, i32, i32, i32, i32, i32, i32, vp], ctypes.c_int),
             "coli_moe_placer_destroy": ([vp], None),
             "coli_moe_placer_reset": ([vp], ctypes.c_int),
@@ -297,6 +298,14 @@ def stream_read(buf, out, n_groups, nbytes=None, stream=None):
     nb = buf.numel() * buf.element_size() if nbytes is None else nbytes
     _check(lib().coli_stream_read(_ptr(buf), nb, _ptr(out), n_groups, _stream(stream)),
            "coli_stream_read")
+
+
+def issue_probe(mode, ticks, sink, n_groups=None, stream=None):
+    """coli_issue_probe (measurement only): MFMA-only, FMA-only and mixed
+    workloads on the SIMDs; each workgroup's ticks into ``ticks``."""
+    n = ticks.numel() if n_groups is None else n_groups
+    _check(lib().coli_issue_probe(mode, n, _ptr(ticks), _ptr(sink), _stream(stream)),
+           "coli_issue_probe")
 
 
 class DeviceLayer:

@@ -37,7 +37,6 @@
 #include "route_tokens.h"
 
 #include <algorithm>
-#include <atomic>
 
 namespace coli {
 
@@ -1293,21 +1292,6 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
 
 // Workgroups of NW waves of the fused down + combine kernel (variant P)
 // resident on one CU at once (at least 1), cached per device.
-static int resident_blocks(const void *kern, int P, int NW)
-{
-    static std::atomic<int> cache[8][4][16];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) dev = 0;
-    std::atomic<int> &c = cache[dev][P - 1][NW - 1];
-    int n = c.load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * NW, 0) != hipSuccess || n < 1)
-            n = 1;
-        c.store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // T == 1: the streaming kernels.  Launch shapes measured on MI355X with the
 // decode layer (H 6144, I 2048, 9 entries): gate/up runs one 4-wave
 // workgroup per CU (its register ring plus the x chunks allow two waves per
@@ -1354,16 +1338,15 @@ static hipError_t launch_f32_t1(const LayerDev &L, const ForwardIO &io, GemvArgs
             // 17.5 for 4 rows and 19.9 for 2 rows over 4 stages)
             constexpr int RD = 2, M = 2, DEPTH = 2;
             // fused with the combine: NW waves per workgroup cover the entries;
-            // as many workgroups as are resident at once (one round), each
-            // with at most kDownRowsMax rows
+            // one workgroup per CU (one round: the traces show one of these
+            // 9-wave workgroups resident per CU, and 256 workgroups beat 512),
+            // each with at most kDownRowsMax rows
             const int nblocks = L.H / RD, NW = std::min(entries, kDownT1cWaves);
             const dim3 block(64 * NW);
 #define COLI_DN1C(P_) \
             if (P == P_) { \
                 const auto kern = down_t1c_kernel<P_, RD, M, DEPTH>; \
-                const int per_cu = resident_blocks(reinterpret_cast<const void *>(kern), P_, NW); \
-                const int G = std::min(nblocks, std::max(per_cu * cus, \
-                                                         (nblocks * RD + kDownRowsMax - 1) / kDownRowsMax)); \
+                const int G = std::min(nblocks, std::max(cus, (nblocks * RD + kDownRowsMax - 1) / kDownRowsMax)); \
                 if (a.tl) launch(mk, (down_t1c_kernel<P_, RD, M, DEPTH, true>), dim3(G), block, 0, st, a, \
                                  io.ids, io.w, io.y); \
                 else launch(mk, kern, dim3(G), block, 0, st, a, io.ids, io.w, io.y); \

@@ -348,16 +348,17 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
     // 32 i and at (tid & 3) * 16 of weight rows (tid >> 2) + 64 i, so a
     // wave's load instruction reads whole row segments.  Threads r < 128
     // load row r's activation scales, threads 128 + r weight row r's.  Rows
-    // past the tile read the tile's last row (their results are not stored),
-    // weight rows past the matrix read 0, and the second group of the last
-    // step of an odd group count is never used.
+    // past the tile and weight rows past the matrix read 0 without touching
+    // memory (their results are not stored), and the second group of the
+    // last step of an odd group count is never used.
     const int a_byte = (tid & 7) * 16;
     uint32_t a_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const int m = (tid >> 3) + 32 * i;
         int ir, orow;
-        tile_row(a, ti, (tid >> 3) + 32 * i, ir, orow);
-        a_off[i] = (uint32_t)(ir - in0) * K + a_byte;
+        tile_row(a, ti, m, ir, orow);
+        a_off[i] = m < ti.rows ? (uint32_t)(ir - in0) * K + a_byte : kOOB8;
     }
     // weight rows: a wave covers 16 rows per round, 4 lanes per row, and the
     // 8 lanes of each LDS write pass hold rows r and r + 4 (disjoint banks at
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
     if (x_thread) {
         int ir, orow;
         tile_row(a, ti, tid, ir, orow);
-        s_off = (uint32_t)(ir - in0) * G * 4;
+        s_off = tid < ti.rows ? (uint32_t)(ir - in0) * G * 4 : kOOB8;
     } else {
         const int r = wrow(tid - BM);
         s_off = r >= 0 ? (uint32_t)r * G * 2 : kOOB8;

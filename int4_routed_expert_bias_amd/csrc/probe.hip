@@ -38,7 +38,92 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *__restr
     if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+// Issue sharing of one SIMD between the matrix core and the vector ALU,
+// the quantity that sets the int8 GEMM's ceiling: workgroups of 8 waves (two
+// per SIMD) run ITERS iterations of
+//   mode 0: 4 independent v_mfma_i32_16x16x64_i8 per wave,
+//   mode 1: 16 independent fp32 FMAs per wave,
+//   mode 2: waves 0-3 the MFMAs of mode 0, waves 4-7 the FMAs of mode 1
+//           (so each SIMD holds one wave of each kind),
+//   mode 3: every wave both, interleaved;
+// ticks[b] = workgroup b's duration in wall-clock (100 MHz) ticks.  If the
+// two units issued in parallel, modes 2 and 3 would take about as long as
+// the longer of modes 0 and 1 (halved for mode 2); serialised, as long as
+// their sum.
+constexpr int kIssueIters = 2048;
+typedef int v4i_p __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+__global__ __launch_bounds__(512) void issue_probe_kernel(uint64_t *__restrict__ ticks, int seed,
+                                                          int *__restrict__ sink)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const v4i_p a = {seed + lane, 1, 2, 3}, b = {3, seed, 1, lane};
+    v4i_p c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = (float)(lane + i) * 1e-3f;
+    const float m = 1.0001f + seed * 1e-9f, ad = 1e-7f;
+    const bool mfma = MODE == 0 || (MODE == 2 && wave < 4);
+    const bool valu = MODE == 1 || (MODE == 2 && wave >= 4);
+    __syncthreads();
+    const uint64_t t0 = wall_clock64();
+    if (MODE == 3) {
+        for (int it = 0; it < kIssueIters; ++it) {
+            c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = fmaf(f[i], m, ad);
+            c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c1, 0, 0, 0);
+#pragma unroll
+            for (int i = 4; i < 8; ++i) f[i] = fmaf(f[i], m, ad);
+            c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c2, 0, 0, 0);
+#pragma unroll
+            for (int i = 8; i < 12; ++i) f[i] = fmaf(f[i], m, ad);
+            c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c3, 0, 0, 0);
+#pragma unroll
+            for (int i = 12; i < 16; ++i) f[i] = fmaf(f[i], m, ad);
+        }
+    } else {
+        if (mfma)
+            for (int it = 0; it < kIssueIters; ++it) {
+                c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c3, 0, 0, 0);
+            }
+        if (valu)
+            for (int it = 0; it < kIssueIters; ++it) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) f[i] = fmaf(f[i], m, ad);
+            }
+    }
+    __syncthreads();
+    const uint64_t t1 = wall_clock64();
+    float fs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) fs += f[i];
+    if (c0[0] + c1[1] + c2[2] + c3[3] == 0x7fffffff || fs == 12345.f) sink[0] = 1;  // keeps the work
+    if (threadIdx.x == 0) ticks[blockIdx.x] = t1 - t0;
+}
+
 }  // namespace coli
+
+extern "C" int coli_issue_probe(int32_t mode, int32_t n_groups, uint64_t *ticks, int32_t *sink,
+                                void *hip_stream)
+{
+    if (!ticks || !sink || n_groups < 1 || n_groups > 65536) return COLI_E_ARG;
+    if (mode < 0 || mode > 3) return COLI_E_ARG;
+    if (((uintptr_t)ticks & 7u) || ((uintptr_t)sink & 3u)) return COLI_E_ALIGN;
+    if (int st = coli_moe_device_check()) return st;
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    switch (mode) {
+    case 0: hipLaunchKernelGGL(coli::issue_probe_kernel<0>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    case 1: hipLaunchKernelGGL(coli::issue_probe_kernel<1>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    case 2: hipLaunchKernelGGL(coli::issue_probe_kernel<2>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    default: hipLaunchKernelGGL(coli::issue_probe_kernel<3>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    }
+    return hipGetLastError() == hipSuccess ? COLI_OK : COLI_E_DEVICE;
+}
 
 extern "C" int coli_stream_read(const void *buf, size_t bytes, uint32_t *out, int32_t n_groups,
                                 void *hip_stream)
