@@ -603,7 +603,8 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
     if os.path.exists(tpath) and topp is None:
         with open(tpath) as fp:
             rec = json.load(fp).get(f"{w.name}:{dom_label}")
-        if rec and rec.get("source_hash") == profiling.source_hash():
+        if rec and rec.get("source_hash") == profiling.source_hash(
+                tuple(rec.get("sources", profiling.ALL_SOURCES))):
             roof["traffic"] = rec["hbm_bytes_per_launch"]
             roof["traffic_source"] = ("profiles/traffic.json (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                                       "copy-calibrated; same kernel sources)")

@@ -12,7 +12,7 @@ Used on the measurement side only (never by the compute path):
 
   python -m int4_routed_expert_bias_amd.profiling traffic \
       --fetch <pmc dir> --write <pmc dir> --copy-fetch <pmc dir> --copy-write <pmc dir> \
-      --kernel <label> --match <trace name substring> --workload <name> \
+      --kernel <label> --match <trace name substring> [--match ...] --workload <name> \
       --out profiles/traffic.json
       HBM bytes per launch of one kernel from the FETCH_SIZE and WRITE_SIZE
       counters (KiB per dispatch), each scaled by the factor that maps the
@@ -37,9 +37,24 @@ COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
 COPY_KERNEL = "copyBuffer"  # the runtime blit kernel behind a device-to-device tensor copy
 
 
-def source_hash(files=("expert_f32.hip", "expert_i8.hip", "expert_i8v.hip", "stream.h",
-                       "common.h", "route.hip", "route_tokens.h", "union_wave.h", "union.hip",
-                       "combine.hip")) -> str:
+ALL_SOURCES = ("expert_f32.hip", "expert_i8.hip", "expert_i8v.hip", "stream.h", "common.h",
+               "route.hip", "route_tokens.h", "union_wave.h", "union.hip", "combine.hip")
+
+
+def kernel_sources(kernel: str):
+    """The sources a kernel's traffic depends on (its translation unit and
+    the headers it includes), so that a traffic record stays valid while
+    only other kernels change."""
+    if kernel.startswith("ggemm") or kernel.startswith("quant_rows"):
+        return ("expert_i8.hip", "common.h")
+    if "i8v" in kernel:
+        return ("expert_i8v.hip", "stream.h", "route_tokens.h", "union_wave.h", "common.h")
+    if kernel.startswith(("gateup_", "down_")):
+        return ("expert_f32.hip", "stream.h", "route_tokens.h", "union_wave.h", "common.h")
+    return ALL_SOURCES
+
+
+def source_hash(files=ALL_SOURCES) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(HERE, "csrc", f), "rb") as fp:
@@ -141,8 +156,9 @@ def main(argv=None):
     cn.add_argument("--match", action="append", required=True)
     cn.add_argument("--command", action="append", default=[])
     tr = sub.add_parser("traffic")
-    for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "match", "workload", "out"):
+    for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "workload", "out"):
         tr.add_argument("--" + a.replace("_", "-"), required=True)
+    tr.add_argument("--match", action="append", required=True)
     tr.add_argument("--bytes-per-launch", type=float, default=None,
                     help="algorithmic bytes of one launch (for the ratio in the record)")
     args = ap.parse_args(argv)
@@ -156,15 +172,18 @@ def main(argv=None):
             print("Commands:\n\n```\n" + "\n".join(args.command) + "\n```\n")
         print(counter_table(args.dirs, args.match))
         return
-    f_kib = pmc_avg(args.fetch, "FETCH_SIZE", args.match)
-    w_kib = pmc_avg(args.write, "WRITE_SIZE", args.match)
+    # several --match: kernels launched together for one step (the grouped
+    # GEMM's full- and partial-tile launches), their per-launch means added
+    f_kib = sum(pmc_avg(args.fetch, "FETCH_SIZE", m) for m in args.match)
+    w_kib = sum(pmc_avg(args.write, "WRITE_SIZE", m) for m in args.match)
     cf_kib = pmc_avg(args.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
     cw_kib = pmc_avg(args.copy_write, "WRITE_SIZE", COPY_KERNEL)
     f_scale = COPY_BYTES / (cf_kib * 1024.0)
     w_scale = COPY_BYTES / (cw_kib * 1024.0)
     rec = {
         "kernel": args.kernel, "match": args.match, "workload": args.workload,
-        "source_hash": source_hash(),
+        "sources": list(kernel_sources(args.kernel)),
+        "source_hash": source_hash(kernel_sources(args.kernel)),
         "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
         "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
