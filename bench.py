@@ -608,7 +608,7 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
             roof["traffic"] = rec["hbm_bytes_per_launch"]
             roof["traffic_source"] = ("profiles/traffic.json (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                                       "copy-calibrated; same kernel sources)")
-    roof["kernel"] = dom_label + (" (full- and partial-tile launches)" if len(doms) > 1 else "")
+    roof["kernel"] = dom_label + (f" ({len(doms)} launches: the tile lists)" if len(doms) > 1 else "")
     roof["kernel_us"] = round(dur_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(algo_bytes)
     roof["algorithmic_ops_per_launch"] = int(algo_ops)

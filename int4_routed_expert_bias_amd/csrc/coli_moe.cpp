@@ -449,9 +449,11 @@ const char *coli_moe_forward_kernel_name(int32_t act_mode, int32_t T, int32_t i)
     static const char *f32[] = {"gateup_f32_kernel", "down_f32_kernel", "combine_kernel"};
     static const char *i8_few[] = {"quant_rows_kernel", "gateup_i8v_kernel", "down_i8v_kernel",
                                    "combine_kernel"};
-    static const char *i8[] = {"quant_rows_kernel", "schedule_kernel", "ggemm_kernel<gateup,full>",
-                               "ggemm_kernel<gateup,partial>", "ggemm_kernel<down,full>",
-                               "ggemm_kernel<down,partial>", "combine_kernel"};
+    static const char *i8[] = {"quant_rows_kernel",           "schedule_kernel",
+                               "ggemm_kernel<gateup,full>",   "ggemm_kernel<gateup,partial>",
+                               "ggemm_kernel<gateup,small>",  "ggemm_kernel<down,full>",
+                               "ggemm_kernel<down,partial>",  "ggemm_kernel<down,small>",
+                               "combine_kernel"};
     if (i < 0 || i >= forward_kernel_count(act_mode, T)) return nullptr;
     if (act_mode == COLI_ACT_F32) return T == 1 ? f32_one[i] : T <= 4 ? f32_few[i] : f32[i];
     return T <= kI8StreamTMax ? i8_few[i] : i8[i];

@@ -86,7 +86,7 @@ struct Workspace {
     // int8 family
     size_t qx, sx;   // [T][H] i8 (permuted), [T][H/64] f32
     size_t qh, sh;   // [R][I] i8 (permuted), [R][I/64] f32
-    size_t tiles;    // [max_tiles] int2 (entry, first row) + [1] count
+    size_t tiles;    // [max_tiles] int2 (entry, first row) + [2] list sizes
     size_t forward_end;
     // route + forward in one call (one token): the scores stay readable
     // while gate/up writes h, so they sit past the forward buffers
@@ -154,7 +154,7 @@ inline Workspace workspace_layout(int64_t H, int64_t I, int64_t E, int64_t k, in
         w.sx = p; p = align256(p + (size_t)T * (H / 64) * 4);
         w.qh = p; p = align256(p + (size_t)w.R * I);
         w.sh = p; p = align256(p + (size_t)w.R * (I / 64) * 4);
-        w.tiles = p; p = align256(p + (size_t)(w.max_tiles + 1) * 8);
+        w.tiles = p; p = align256(p + (size_t)(w.max_tiles + 2) * 8);
         if (T <= kI8StreamTMax) {  // the small-batch kernels pass h in fp32
             w.h = p; p = align256(p + (size_t)w.R * I * 4);
         }
@@ -295,7 +295,7 @@ struct ForwardIO {
 inline int forward_kernel_count(int act_mode, int T)
 {
     if (act_mode == 0) return T == 1 ? 2 : 3;  // T == 1: down and combine in one launch
-    if (act_mode == 1) return T <= kI8StreamTMax ? 4 : 7;
+    if (act_mode == 1) return T <= kI8StreamTMax ? 4 : 9;
     return 0;
 }
 

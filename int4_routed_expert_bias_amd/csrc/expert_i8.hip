@@ -7,8 +7,9 @@
 //            q = clamp(rint(v / scale), -127, 127); codes are stored in the
 //            permuted order [0,2,4,6,1,3,5,7] inside every 8-element block.
 //  schedule: one thread per union expert turns its slot count into 128-row
-//            tiles, longest entries first (device side: the union size
-//            never leaves the GPU).
+//            tiles, longest entries first, and its remainder into a last
+//            tile of the 128-row or the 64-row shape (device side: the union
+//            size never leaves the GPU).
 //  gemm:     v_mfma_i32_16x16x64_i8, one MFMA per 64-group, so the exact
 //            int32 group accumulator comes straight out of the matrix core.
 //            A = 16 token rows of int8 codes, B = 16 weight rows.  A packed
@@ -16,13 +17,12 @@
 //            and w & 0xF0F0F0F0 (odd elements): signed bytes equal to 16 x
 //            the code, so the MFMA yields 16 x acc exactly (|16 acc| < 2^21)
 //            and the activation layout above matches that byte order.
-//            Epilogue per group: out += float(acc) * act_scale * w_scale.
-//            The epilogue's three VALU ops per output and group (convert,
-//            multiply, FMA) cost more issue cycles than the MFMA itself, so
-//            the kernel is built to keep the VALU fed: whole-row coalesced
-//            staging loads that are only waited for after the compute, an
-//            LDS double buffer, and each group's MFMAs issued before its
-//            epilogue.
+//            Epilogue per group: out += acc * act_scale * w_scale in two FMAs
+//            per output (below).  The epilogue costs more issue cycles than
+//            the MFMA itself, so the kernel is built to keep the VALU fed:
+//            whole-row coalesced staging loads that are only waited for
+//            after the compute, an LDS double buffer, and each unit's MFMAs
+//            issued next to the previous unit's epilogue.
 //  gate/up:  the SwiGLU pairs (gate row i, up row I + i) sit in the same
 //            lane and register, and the int8 quantisation of h (per 64-group
 //            of i) finishes in the epilogue; the down GEMM reads the
@@ -88,29 +88,32 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict
 }
 
 // --- tile schedule ---------------------------------------------------------
-// Two tile lists in tiles[]: every entry's full 128-row tiles first
-// (positions [0, nf)), then the entries' last, partial tiles (positions
-// [nf, nf + np)); tiles[max_tiles] = (nf, np).  A tile is (entry, first
-// row).  Full tiles are ordered by entry size, largest first (ties: lower
-// entry first), an entry's tiles consecutive, so the longest entries start
-// first and tiles that read the same weights run at the same time; partial
-// tiles are ordered by row count, largest first.  The order changes no
-// result (every tile writes its own rows).
+// Three tile lists in tiles[]: every entry's full 128-row tiles first
+// (positions [0, nf)), then the entries' last tiles of more than small_m
+// rows (positions [nf, nf + np)), then those of at most small_m rows
+// (positions [nf + np, nf + np + ns)); tiles[max_tiles] = (nf, np),
+// tiles[max_tiles + 1] = (ns, 0).  A tile is (entry, first row).  Full
+// tiles are ordered by entry size, largest first (ties: lower entry first),
+// an entry's tiles consecutive, so the longest entries start first and
+// tiles that read the same weights run at the same time; last tiles are
+// ordered by row count, largest first.  The order changes no result (every
+// tile writes its own rows).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ offsets,
                                                         const int32_t *__restrict__ n_union,
                                                         int cap, int T, int n_shared, int tile_m,
-                                                        int2 *__restrict__ tiles, int max_tiles)
+                                                        int small_m, int2 *__restrict__ tiles,
+                                                        int max_tiles)
 {
     __shared__ int32_t cnt[COLI_MAX_E_DEV + 1];   // rows of live entry i (union entries, then shared)
     __shared__ int32_t ordf[COLI_MAX_E_DEV + 1];  // live entry at each full-list position
     __shared__ int32_t ordp[COLI_MAX_E_DEV + 1];  // live entry at each partial-list position
     __shared__ int32_t scan[COLI_MAX_E_DEV + 2];  // first full tile of each position, then nf
-    __shared__ int32_t npart;
+    __shared__ int32_t npart, nbig;
     const int tid = threadIdx.x;
     const int U = n_union[0];
     const int nl = U + n_shared;
     for (int i = tid; i < nl; i += blockDim.x) cnt[i] = i < U ? offsets[i + 1] - offsets[i] : T;
-    if (tid == 0) npart = 0;
+    if (tid == 0) npart = nbig = 0;
     __syncthreads();
     // positions: entries with more rows (more full tiles; a longer partial
     // tile), or as many and a lower index
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
         ordf[rf] = i;
         ordp[rp] = i;
         if (cr) atomicAdd(&npart, 1);
+        if (cr > small_m) atomicAdd(&nbig, 1);
     }
     __syncthreads();
     if (tid < 64) {
@@ -159,21 +163,25 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
             tiles[nf + p] = make_int2(ep, cnt[ip] / tile_m * tile_m);
         }
     }
-    if (tid == 0) tiles[max_tiles] = make_int2(nf, np);
+    if (tid == 0) {
+        const int nb = min(nbig, np);
+        tiles[max_tiles] = make_int2(nf, nb);
+        tiles[max_tiles + 1] = make_int2(np - nb, 0);
+    }
 }
 
 // --- grouped GEMM ----------------------------------------------------------
-// One workgroup computes a 128 x 128 output tile of one union entry: up to
-// 128 of the entry's rows (a tile of the schedule) against 128 weight rows
+// One workgroup computes a BM x 128 output tile of one union entry: up to
+// BM of the entry's rows (a tile of the schedule) against 128 weight rows
 // (gate/up: 64 gate rows i0.. and the matching up rows I + i0..; down: 128
-// output rows n0..).  The K loop walks two 64-groups per step through a
+// output rows n0..).  The K loop walks KG 64-groups per step through a
 // double-buffered LDS stage: the next step's loads are issued before the
 // current step computes and written to the other buffer after it.
 //
-// Four waves as 2 (rows) x 2 (columns).  The 8 m-tiles of 16 rows are
-// interleaved over the row waves (wave wm owns m-tiles wm, wm + 2, wm + 4,
-// wm + 6), so a partial tile keeps both busy, and a wave skips its m-tiles
-// that hold no row.  Column wave wn owns 4 n-tiles of 16 weight rows:
+// Four waves as 2 (rows) x 2 (columns).  The BM / 16 m-tiles of 16 rows are
+// interleaved over the row waves (wave wm owns m-tiles wm, wm + 2, ...), so
+// a partial tile keeps both busy, and a wave skips its m-tiles that hold no
+// row.  Column wave wn owns 4 n-tiles of 16 weight rows:
 // gate/up: gate rows i0 + 32 wn.. and their up rows (a SwiGLU pair sits in
 // one lane and register); down: rows n0 + 64 wn...  Per 64-group an
 // (m-tile, n-tile) pair is one v_mfma_i32_16x16x64_i8 whose result is the
@@ -185,25 +193,41 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
 // = round(16 acc * s') (see epi_act_scale), then fma(term, sw / 16, out).
 //
 // Issue cost per MFMA: the epilogue's 8 VALU instructions (4 outputs x 2)
-// are the floor of this arithmetic (an MFMA takes 16 cycles, 8 wave64 VALU
-// instructions 32, so the matrix cores can be at most half busy); the int4
-// unpack adds 1.5 (6 per B fragment, each fragment feeding 4 m-tiles) and
-// staging and addressing well under 1.
-constexpr int kGBM = kTileM;          // rows per tile
-constexpr int kGBN = 128;             // weight rows per tile
-constexpr int kGKG = 2;               // 64-groups per LDS stage
-constexpr int kGAS = kGKG * 64 + 32;  // LDS activation row stride (bytes)
-constexpr int kGBS = kGKG * 32 + 16;  // LDS packed-weight row stride
-static_assert(kGBM == 128 && kGBN == 128 && kGKG == 2, "the wave and staging layouts cover 128 x 128 tiles, two groups a step");
+// are the floor of this arithmetic, and a SIMD does not issue them while it
+// issues MFMAs; the int4 unpack adds 1.5 (6 per B fragment, each fragment
+// feeding the wave's 4 m-tiles; 3 in the 64-row shape) and staging and
+// addressing well under 1.
+//
+// Two tile shapes share this code: 128 rows with two 64-groups per K step
+// (the full tiles and the entries' last tiles of more than 64 rows), and
+// 64 rows with four groups per step (the last tiles of at most 64 rows,
+// most of an entry's rows at T = 512: per step a wave does the same MFMA
+// work as in a full 128-row tile, and the workgroup has twice the bytes in
+// flight, in half the steps).
+constexpr int kGBN = 128;  // weight rows per tile
+constexpr int kSmallBM = 64, kSmallKG = 4;
+static_assert(kTileM == 128, "the schedule's tiles are 128 rows");
 
-struct __attribute__((aligned(16))) GemmLds {
-    alignas(16) uint8_t a[2][kGBM * kGAS];  // activation codes
-    alignas(16) uint8_t b[2][kGBN * kGBS];  // packed int4 weight codes
-    alignas(16) float sx[2][kGKG][kGBM];    // activation scales s' (epi_act_scale)
-    alignas(16) float nm[2][kGKG][kGBM];    // -kEpiM * s'
-    alignas(16) float sw[2][kGKG][kGBN];    // weight scales / 16
-    alignas(16) float amax[2][kGBM];        // gate/up: |h| maxima per column wave
+template <int BM, int KG>
+struct GemmShape {
+    static_assert((BM == 128 && KG == 2) || (BM == kSmallBM && KG == kSmallKG), "two tile shapes");
+    static constexpr int AS = KG * 64 + (KG == 2 ? 32 : 16);  // LDS activation row stride (bytes; conflict-free fragment reads)
+    static constexpr int BS = KG * 32 + 16;                   // LDS packed-weight row stride
+    static constexpr int MT = BM / 32;                        // m-tiles per row wave
+    static constexpr int RA = 64 / KG;                        // activation rows per staging pass
 };
+
+template <int BM, int KG>
+struct __attribute__((aligned(16))) GemmLds {
+    using S = GemmShape<BM, KG>;
+    alignas(16) uint8_t a[2][BM * S::AS];   // activation codes
+    alignas(16) uint8_t b[2][kGBN * S::BS]; // packed int4 weight codes
+    alignas(16) float sx[2][KG][BM];        // activation scales s' (epi_act_scale)
+    alignas(16) float nm[2][KG][BM];        // -kEpiM * s'
+    alignas(16) float sw[2][KG][kGBN];      // weight scales / 16
+    alignas(16) float amax[2][BM];          // gate/up: |h| maxima per column wave
+};
+static_assert(2 * sizeof(GemmLds<kSmallBM, kSmallKG>) <= 160 * 1024, "two small-tile workgroups per CU");
 
 struct I8Args {
     const int8_t *qin;        // activation codes (permuted) [rows][K]
@@ -215,6 +239,7 @@ struct I8Args {
     const int32_t *union_ids, *offsets, *slots;
     const int2 *tiles;
     int max_tiles;
+    int small_list;           // 1: the small-tile launch runs the list of last tiles of <= 64 rows
     int T, k, cap;
     // outputs
     int8_t *qh; float *sh;    // gate/up: quantised h (permuted) and scales, by position
@@ -276,27 +301,35 @@ __device__ __forceinline__ void tile_row(const I8Args &a, const TileInfo &ti, in
     }
 }
 
-// LIST: the tiles a launch covers -- kAllTiles (both lists; the dump
-// variant), kFullTiles (128 rows each: no row masks, the software-pipelined
-// step) or kPartialTiles (fewer rows: m-tiles without rows are skipped).
-// Full and partial tiles run as separate launches, so each variant gets its
-// own register allocation.
-constexpr int kAllTiles = 0, kFullTiles = 1, kPartialTiles = 2;
+// LIST: the tiles a launch covers -- kAllTiles (every list, 128-row tiles:
+// odd group counts), kFullTiles (128 rows each: no row masks), kPartialTiles
+// (last tiles of more than 64 rows, or of any count when small_list is 0)
+// or kSmallTiles (last tiles of at most 64 rows, the 64-row shape).  Each
+// list runs as a launch of its own, so each variant gets its own register
+// allocation.  DUMP (tests only): the plain step, with the int32 group sums
+// written out.
+constexpr int kAllTiles = 0, kFullTiles = 1, kPartialTiles = 2, kSmallTiles = 3;
 
-template <bool GATEUP, bool DUMP, int LIST>
+template <bool GATEUP, bool DUMP, int LIST, int BM = 128, int KG = 2>
 __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
 {
-    constexpr int BM = kGBM, BN = kGBN, KG = kGKG, AS = kGAS, BS = kGBS;
-    static_assert(!DUMP || LIST == kAllTiles, "the dump variant covers every tile");
-    __shared__ GemmLds sm;
+    using Sh = GemmShape<BM, KG>;
+    constexpr int BN = kGBN, AS = Sh::AS, BS = Sh::BS, MT = Sh::MT, RA = Sh::RA;
+    static_assert((LIST == kSmallTiles) == (BM == kSmallBM), "the small list runs the 64-row shape");
+    __shared__ GemmLds<BM, KG> sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int n = lane & 15, q = lane >> 4;
     const int2 counts = a.tiles[a.max_tiles];
-    const int count = LIST == kAllTiles ? counts.x + counts.y : LIST == kFullTiles ? counts.x : counts.y;
+    const int nsmall = a.tiles[a.max_tiles + 1].x;
+    const int count = LIST == kAllTiles ? counts.x + counts.y + nsmall
+                      : LIST == kFullTiles ? counts.x
+                      : LIST == kPartialTiles ? counts.y + (a.small_list ? 0 : nsmall)
+                      : nsmall;
     if ((int)blockIdx.y >= count) return;
-    const int2 td = a.tiles[blockIdx.y + (LIST == kPartialTiles ? counts.x : 0)];
+    const int first = LIST == kPartialTiles ? counts.x : LIST == kSmallTiles ? counts.x + counts.y : 0;
+    const int2 td = a.tiles[blockIdx.y + first];
     TileInfo ti;
     ti.ue = td.x;
     ti.m0 = td.y;
@@ -342,48 +375,49 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
     const auto rA = rsrc_i8(a.qin + (size_t)in0 * K, (uint32_t)in_rows * K);
     const auto rX = rsrc_i8(a.sin + (size_t)in0 * G, (uint32_t)in_rows * G * 4);
 
-    // Staging, fixed for the tile.  A step holds 128 bytes (two groups) of
-    // every activation row and 64 bytes of every packed weight row: thread
-    // tid loads 16 bytes at (tid & 7) * 16 of activation rows (tid >> 3) +
-    // 32 i and at (tid & 3) * 16 of weight rows (tid >> 2) + 64 i, so a
-    // wave's load instruction reads whole row segments.  Threads r < 128
-    // load row r's activation scales, threads 128 + r weight row r's.  Rows
-    // past the tile and weight rows past the matrix read 0 without touching
-    // memory (their results are not stored), and the second group of the
-    // last step of an odd group count is never used.
-    const int a_byte = (tid & 7) * 16;
+    // Staging, fixed for the tile.  A step holds KG * 64 bytes of every
+    // activation row and KG * 32 bytes of every packed weight row: thread
+    // tid loads 16 bytes of activation rows tid / (4 KG) + (64 / KG) i and
+    // of weight rows (128-row tiles: 4 lanes a row, rows r and r + 4 in each
+    // 8-lane LDS write pass, disjoint banks at the 80-byte stride; 64-row
+    // tiles: 8 lanes a row, one row per pass), so a wave's load instruction
+    // reads whole row segments.  Threads r < BM load row r's activation
+    // scales, threads 128 + r weight row r's.  Rows past the tile, weight
+    // rows past the matrix and groups past K read 0 without touching memory
+    // (rows: their results are not stored; groups: their terms are exact
+    // zeros, or never used on the plain step).
+    const int a_byte = (tid & (4 * KG - 1)) * 16;
     uint32_t a_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int m = (tid >> 3) + 32 * i;
+        const int m = tid / (4 * KG) + RA * i;
         int ir, orow;
         tile_row(a, ti, m, ir, orow);
         a_off[i] = m < ti.rows ? (uint32_t)(ir - in0) * K + a_byte : kOOB8;
     }
-    // weight rows: a wave covers 16 rows per round, 4 lanes per row, and the
-    // 8 lanes of each LDS write pass hold rows r and r + 4 (disjoint banks at
-    // the 80-byte row stride)
-    const int b_byte = (tid & 3) * 16;
-    const int b_row = 16 * (tid >> 6) + ((tid >> 3) & 3) + 4 * ((tid >> 2) & 1) + 8 * ((tid >> 5) & 1);
-    uint32_t b_off[2];
+    const int b_byte = KG == 2 ? (tid & 3) * 16 : (tid & 7) * 16;
+    const int b_row = KG == 2 ? 16 * (tid >> 6) + ((tid >> 3) & 3) + 4 * ((tid >> 2) & 1) + 8 * ((tid >> 5) & 1)
+                              : tid >> 3;
+    constexpr int BROWS = 128 / KG;  // weight rows per staging pass
+    uint32_t b_off[KG];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = wrow(b_row + 64 * i);
+    for (int i = 0; i < KG; ++i) {
+        const int r = wrow(b_row + BROWS * i);
         b_off[i] = r >= 0 ? (uint32_t)r * rb + b_byte : kOOB8;
     }
-    const bool x_thread = tid < BM;  // waves 0 and 1
-    uint32_t s_off;
+    const bool x_thread = tid < BM, w_thread = tid >= 128;
+    uint32_t s_off = kOOB8;
     if (x_thread) {
         int ir, orow;
         tile_row(a, ti, tid, ir, orow);
         s_off = tid < ti.rows ? (uint32_t)(ir - in0) * G * 4 : kOOB8;
-    } else {
-        const int r = wrow(tid - BM);
+    } else if (w_thread) {
+        const int r = wrow(tid - 128);
         s_off = r >= 0 ? (uint32_t)r * G * 2 : kOOB8;
     }
 
     const int nsteps = (G + KG - 1) / KG;
-    uint4 ra[4], rbw[2];
+    uint4 ra[4], rbw[KG];
     uint32_t rs[KG];
     // load_step only issues loads (their values land while the current step
     // computes); store_step writes them to LDS after the compute
@@ -394,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
             for (int i = 0; i < 4; ++i)
                 ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, a_off[i], g0 * 64, 0));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < KG; ++i)
                 rbw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, b_off[i], g0 * 32, 0));
 #pragma unroll
             for (int j = 0; j < KG; ++j) {
@@ -402,38 +436,40 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
                 else rs[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, s_off, (g0 + j) * 2, 0);
             }
         } else {
-            // the last step of an odd group count: its second group lies past
-            // the rows, so those lanes read nothing (out-of-range offsets)
+            // the last step when KG does not divide the group count: its
+            // groups past K are read by no lane (out-of-range offsets)
             const bool a_in = g0 + (a_byte >> 6) < G, b_in = g0 + (b_byte >> 5) < G;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                     rA, a_in ? a_off[i] : kOOB8, g0 * 64, 0));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < KG; ++i)
                 rbw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                     rB, b_in ? b_off[i] : kOOB8, g0 * 32, 0));
-            if (x_thread) rs[0] = __builtin_amdgcn_raw_buffer_load_b32(rX, s_off, g0 * 4, 0);
-            else rs[0] = __builtin_amdgcn_raw_buffer_load_b16(rS, s_off, g0 * 2, 0);
 #pragma unroll
-            for (int j = 1; j < KG; ++j) rs[j] = 0;
+            for (int j = 0; j < KG; ++j) {
+                const uint32_t so = g0 + j < G ? s_off : kOOB8;
+                if (x_thread) rs[j] = __builtin_amdgcn_raw_buffer_load_b32(rX, so, (g0 + j) * 4, 0);
+                else rs[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, so, (g0 + j) * 2, 0);
+            }
         }
     };
     auto store_step = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4 *>(sm.a[buf] + ((tid >> 3) + 32 * i) * AS + a_byte) = ra[i];
+            *reinterpret_cast<uint4 *>(sm.a[buf] + (tid / (4 * KG) + RA * i) * AS + a_byte) = ra[i];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            *reinterpret_cast<uint4 *>(sm.b[buf] + (b_row + 64 * i) * BS + b_byte) = rbw[i];
+        for (int i = 0; i < KG; ++i)
+            *reinterpret_cast<uint4 *>(sm.b[buf] + (b_row + BROWS * i) * BS + b_byte) = rbw[i];
 #pragma unroll
         for (int j = 0; j < KG; ++j) {
             if (x_thread) {
                 const float sr = epi_act_scale(__uint_as_float(rs[j]));
                 sm.sx[buf][j][tid] = sr;
                 sm.nm[buf][j][tid] = -kEpiM * sr;
-            } else {
-                sm.sw[buf][j][tid - BM] = f16_to_f32((uint16_t)rs[j]) * 0.0625f;
+            } else if (w_thread) {
+                sm.sw[buf][j][tid - 128] = f16_to_f32((uint16_t)rs[j]) * 0.0625f;
             }
         }
     };
@@ -445,19 +481,19 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
         lb[nt] = GATEUP ? ((nt < 2) ? 32 * wn + 16 * nt : BN / 2 + 32 * wn + 16 * (nt - 2))
                         : 64 * wn + 16 * nt;
     // m-tiles of this wave that hold a row of the tile (a prefix of i)
-    const int nlive = LIST == kFullTiles ? 4 : min(4, (ti.rows - 16 * wm + 31) >> 5);
-    float out[4][4][4];
+    const int nlive = LIST == kFullTiles ? MT : min(MT, (ti.rows - 16 * wm + 31) >> 5);
+    float out[MT][4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[i][nt][r] = 0.f;
     // dump bookkeeping (tests only)
-    int d_out[4][4], d_row[4];
+    int d_out[MT][4], d_row[4];
     if constexpr (DUMP) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 int ir;
@@ -481,18 +517,21 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
     // are issued next to the epilogue of unit u - 1.  Each output still adds
     // its group terms in ascending group order.
     auto step_units = [&](const int buf, auto nl_c) {
-        constexpr int NL = decltype(nl_c)::value, NU = 2 * NL;
-        v4i pb[KG][4];
-        float psw[KG][4];
+        constexpr int NL = decltype(nl_c)::value, NU = KG * NL;
+        // B fragments and weight scales of two groups at a time (group j in
+        // slot j & 1: a slot is refilled only after the last unit of the
+        // group before has used it)
+        v4i pb[2][4];
+        float psw[2][4];
         v4i pa[NU];
         float psx[NU][4], pnm[NU][4];
         v4i pc[NU][4];
         auto read_b = [&](const int j) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                pb[j][nt] = unpack_b(*reinterpret_cast<const uint2 *>(
+                pb[j & 1][nt] = unpack_b(*reinterpret_cast<const uint2 *>(
                     sm.b[buf] + (lb[nt] + n) * BS + j * 32 + 8 * q));
-                psw[j][nt] = sm.sw[buf][j][lb[nt] + n];
+                psw[j & 1][nt] = sm.sw[buf][j][lb[nt] + n];
             }
         };
         auto read_a = [&](const int u) {
@@ -506,7 +545,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
         auto mfma = [&](const int u) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-                pc[u][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[u], pb[u / NL][nt], cmag, 0, 0, 0);
+                pc[u][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[u], pb[(u / NL) & 1][nt], cmag, 0, 0, 0);
         };
         auto epi = [&](const int u) {
             const int i = u % NL, j = u / NL;
@@ -515,7 +554,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     out[i][nt][r] = fmaf(fmaf(__int_as_float(pc[u][nt][r]), psx[u][r], pnm[u][r]),
-                                         psw[j][nt], out[i][nt][r]);
+                                         psw[j & 1][nt], out[i][nt][r]);
                 // pin the unit's results here: the compiler would otherwise
                 // sink the epilogue below the step and keep every MFMA
                 // result alive until then
@@ -535,7 +574,13 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
 #pragma unroll
         for (int u = 1; u < NU; ++u) {
             if (u + 1 < NU) read_a(u + 1);
-            if (u == (NL > 1 ? NL - 1 : 1)) read_b(1);
+            // the next group's B: during the group's last unit (one unit ahead),
+            // or, one m-tile a group, just before its own unit
+            if constexpr (NL > 1) {
+                if (u % NL == NL - 1 && u / NL + 1 < KG) read_b(u / NL + 1);
+            } else {
+                read_b(u);
+            }
             mfma(u);
             epi(u - 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -558,7 +603,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
                     sw[nt] = sm.sw[buf][j][lb[nt] + n];
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < MT; ++i) {
                     if (i >= nlive) break;
                     // the m-tile's A fragment and scales, 4 MFMAs, the epilogue
                     const int r0 = 32 * i + 16 * wm;
@@ -614,16 +659,16 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
             if (ks + 1 < nsteps) step(ks + 1, 1);
         }
     };
-    if constexpr (LIST == kAllTiles) {
+    if constexpr (DUMP || LIST == kAllTiles) {
         kloop(std::integral_constant<int, -1>{});
     } else if constexpr (LIST == kFullTiles) {
-        kloop(std::integral_constant<int, 4>{});
+        kloop(std::integral_constant<int, MT>{});
     } else {
         // each live m-tile count its own loop (so each has its own register
         // allocation); a wave without rows only stages and waits
         switch (nlive) {
-        case 4: kloop(std::integral_constant<int, 4>{}); break;
-        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        case 4: if constexpr (MT >= 4) kloop(std::integral_constant<int, 4>{}); break;
+        case 3: if constexpr (MT >= 3) kloop(std::integral_constant<int, 3>{}); break;
         case 2: kloop(std::integral_constant<int, 2>{}); break;
         case 1: kloop(std::integral_constant<int, 1>{}); break;
         default: kloop(std::integral_constant<int, 0>{}); break;
@@ -633,9 +678,9 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
     if constexpr (GATEUP) {
         // SwiGLU, then int8 quantisation of h per (row, 64-group [nb0, nb0 + 64)):
         // amax over the group's 64 columns = 16 lanes x 2 n-tiles x 2 waves (wn).
-        float h[4][2][4];
+        float h[MT][2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float m = 0.f;
@@ -654,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
         __syncthreads();
         const int G2 = a.I / 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 32 * i + 16 * wm + 4 * q + r;
@@ -686,7 +731,7 @@ __global__ __launch_bounds__(256, 2) void ggemm_kernel(I8Args a)
             }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 32 * i + 16 * wm + 4 * q + r;
@@ -729,12 +774,12 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
         return launch_forward_i8_small(L, io, qx, sx, reinterpret_cast<float *>(io.ws + lay.h), o,
                                        st, mk);
     launch(mk, schedule_kernel, dim3(1), dim3(1024), 0, st, io.offsets, io.n_union,
-                       (int)lay.cap, T, L.n_shared, kTileM, tiles, (int)lay.max_tiles);
+                       (int)lay.cap, T, L.n_shared, kTileM, kSmallBM, tiles, (int)lay.max_tiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     I8Args a{};
     a.union_ids = io.union_ids; a.offsets = io.offsets; a.slots = io.slots;
-    a.tiles = tiles; a.max_tiles = (int)lay.max_tiles;
+    a.tiles = tiles; a.max_tiles = (int)lay.max_tiles; a.small_list = 1;
     a.T = T; a.k = L.k; a.cap = (int)lay.cap; a.I = L.I; a.H = L.H;
     a.qh = qh; a.sh = sh; a.o = o;
     a.qin = qx; a.sin = sx; a.in_by_pos = 0;
@@ -743,25 +788,31 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.dump_acc = dump ? reinterpret_cast<int32_t *>(dump_b + io.dump.acc13) : nullptr;
     a.dump_qh = dump ? reinterpret_cast<int8_t *>(dump_b + io.dump.qh) : nullptr;
     a.dump_sh = dump ? reinterpret_cast<float *>(dump_b + io.dump.sh) : nullptr;
-    // grid y: bounds of the two lists (full tiles: T*k/128 routed plus
-    // T/128 shared; partial tiles: one per entry)
+    // grid y: bounds of the lists (full tiles: T*k/128 routed plus T/128
+    // shared; last tiles: one per entry)
     const unsigned y_full = (unsigned)std::max<int64_t>(1, (T * L.k) / kTileM + L.n_shared * (T / kTileM));
     const unsigned y_part = (unsigned)(lay.cap + L.n_shared);
+#define COLI_GG_LISTS(GU_, DU_, GX_)                                                            \
+    {                                                                                          \
+        launch(mk, (ggemm_kernel<GU_, DU_, kFullTiles>), dim3(GX_, y_full), dim3(256), 0, st, a); \
+        launch(mk, (ggemm_kernel<GU_, DU_, kPartialTiles>), dim3(GX_, y_part), dim3(256), 0, st, a); \
+        launch(mk, (ggemm_kernel<GU_, DU_, kSmallTiles, kSmallBM, kSmallKG>), dim3(GX_, y_part),  \
+               dim3(256), 0, st, a);                                                           \
+    }
 #define COLI_GG(GU_, GX_)                                                                      \
     {                                                                                          \
-        if (dump || ((a.K / 64) & 1)) {                                                        \
-            /* the dump variant, and odd group counts: one launch over both lists */            \
+        if ((a.K / 64) & 1) {                                                                  \
+            /* odd group counts: one launch over every list (128-row tiles) */                 \
             if (dump)                                                                          \
                 launch(mk, (ggemm_kernel<GU_, true, kAllTiles>), dim3(GX_, (unsigned)lay.max_tiles), \
                        dim3(256), 0, st, a);                                                   \
             else                                                                               \
                 launch(mk, (ggemm_kernel<GU_, false, kAllTiles>), dim3(GX_, (unsigned)lay.max_tiles), \
                        dim3(256), 0, st, a);                                                   \
+        } else if (dump) {                                                                     \
+            COLI_GG_LISTS(GU_, true, GX_)                                                      \
         } else {                                                                               \
-            launch(mk, (ggemm_kernel<GU_, false, kFullTiles>), dim3(GX_, y_full), dim3(256),     \
-                   0, st, a);                                                                  \
-            launch(mk, (ggemm_kernel<GU_, false, kPartialTiles>), dim3(GX_, y_part), dim3(256),  \
-                   0, st, a);                                                                  \
+            COLI_GG_LISTS(GU_, false, GX_)                                                     \
         }                                                                                      \
         if ((err = hipGetLastError()) != hipSuccess) return err;                               \
     }
@@ -777,6 +828,7 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     a.dump_qh = nullptr; a.dump_sh = nullptr;
     COLI_GG(false, (L.H + kGBN - 1) / kGBN)
 #undef COLI_GG
+#undef COLI_GG_LISTS
     err = io.combine
         ? launch_combine(o, io.ids, io.w, T, L.k, L.H, L.n_shared, io.y, st, mk)
         : hipSuccess;

@@ -173,7 +173,7 @@ def main(argv=None):
         print(counter_table(args.dirs, args.match))
         return
     # several --match: kernels launched together for one step (the grouped
-    # GEMM's full- and partial-tile launches), their per-launch means added
+    # GEMM's launches over its tile lists), their per-launch means added
     f_kib = sum(pmc_avg(args.fetch, "FETCH_SIZE", m) for m in args.match)
     w_kib = sum(pmc_avg(args.write, "WRITE_SIZE", m) for m in args.match)
     cf_kib = pmc_avg(args.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
@@ -190,6 +190,7 @@ def main(argv=None):
         "hbm_bytes_per_launch": round(f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale),
     }
     if args.bytes_per_launch:
+        rec["algorithmic_bytes_per_launch"] = round(args.bytes_per_launch)
         rec["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / args.bytes_per_launch, 3)
     db = {}
     if os.path.exists(args.out):
