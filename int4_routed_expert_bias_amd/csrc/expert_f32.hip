@@ -946,13 +946,21 @@ __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, i
 
 // ROUTE: the tokens route themselves first (route_self, as the
 // single-token kernel), and the union is read from LDS.
+// WPB = 8: wave pairs.  Waves w and w + 4 of a workgroup (one SIMD) stream
+// the same row blocks of the same entry and split its tokens (w the even
+// ones, w + 4 the odd ones, NTOK / 2 each): the number of DRAM streams is
+// that of four waves, while two waves per SIMD share the VALU work (a
+// wave alone issues a VALU instruction only about every other slot); the
+// second wave's weight loads are served by the cache.
 template <int P, int M, int DEPTH, int NTOK, int WPB, bool ROUTE, bool TL = false>
 __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
-    // route_self keeps one LDS record per wave of a 4-wave workgroup
-    static_assert(!ROUTE || WPB == 4, "self-routing needs exactly four waves");
-    constexpr int V = next_pow2(2 * M * NTOK), N = reduced_count(V);
+    // route_self: one token per wave of the first four (T <= 4)
+    static_assert(WPB == 4 || (WPB == 8 && NTOK % 2 == 0), "four waves, or four pairs");
+    constexpr bool PAIRS = WPB == 8;
+    constexpr int NW = PAIRS ? NTOK / 2 : NTOK;  // tokens per wave
+    constexpr int V = next_pow2(2 * M * NW), N = reduced_count(V);
     static_assert(V <= 64, "at most 64 values per reduction");
     // x of the T tokens chunk-transposed (token t, piece q of chunk c at
     // float4 (8 t + q) C + c: the lanes of a wave read consecutive float4s,
@@ -975,7 +983,8 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
         U = a.n_union[0];
     }
     tl_mark<TL>(a.tl, a.tl_cap, 1);
-    const T1Split sp = mt_split<ROUTE>(a, blockIdx.x * WPB + wave, gridDim.x * WPB, U, a.I);
+    const int hh = PAIRS ? (wave >> 2) : 0;  // wave pair half: its tokens hh, hh + 2, ...
+    const T1Split sp = mt_split<ROUTE>(a, blockIdx.x * 4 + (wave & 3), gridDim.x * 4, U, a.I);
     const int nsteps = sp.nsteps;
     const uint8_t *wb;
     const uint16_t *sb;
@@ -1031,15 +1040,17 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
         __syncthreads();
     }
     tl_mark<TL>(a.tl, a.tl_cap, 2);
-    if (nsteps == 0 || cnt <= 0) {
+    // this wave's tokens: entry tokens hh + 2 j (pairs) or j
+    const int cntw = PAIRS ? (cnt - hh + 1) / 2 : cnt;
+    if (nsteps == 0 || cntw <= 0) {
         tl_mark<TL>(a.tl, a.tl_cap, 7);
         return;
     }
-    int tok[NTOK], orow[NTOK];
+    int tok[NW], orow[NW];
 #pragma unroll
-    for (int j = 0; j < NTOK; ++j) {
+    for (int j = 0; j < NW; ++j) {
         int in_row = 0, out_row = 0;
-        if (j < cnt) token_rows(a, list, j, in_row, out_row);
+        if (j < cntw) token_rows(a, list, PAIRS ? hh + 2 * j : j, in_row, out_row);
         tok[j] = in_row;
         orow[j] = out_row;
     }
@@ -1055,10 +1066,10 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
                 // per-lane sums over the P chunks (p ascending) for every token
                 auto stage = [&](auto cnt_c) {
                     constexpr int CNT = decltype(cnt_c)::value;
-                    float acc[2][NTOK];
+                    float acc[2][NW];
 #pragma unroll
                     for (int j = 0; j < CNT; ++j) acc[0][j] = acc[1][j] = 0.f;
-                    if constexpr (CNT == 1) {
+                    if constexpr (CNT == 1 && NW == 1) {
                         // one token: all P chunks at once, 2 * P interleaved chains
                         float xl[P][32], kl[P], dots[2][P];
 #pragma unroll
@@ -1077,15 +1088,15 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
 #pragma unroll
                     for (int p = 0; p < P; ++p) {
                         const int c = min(lane + 64 * p, C - 1);  // dead lanes: scale 0
-                        float xl[NTOK][32], kl[NTOK];
+                        float xl[NW][32], kl[NW];
 #pragma unroll
                         for (int j = 0; j < CNT; ++j) {
                             kl[j] = ks[tok[j] * C + c];
                             load_chunk32(xt + 8 * tok[j] * C + c, C, xl[j]);
                         }
                         const uint4 wl[2] = {wv[d][0][p], wv[d][1][p]};
-                        float dl[2][NTOK];
-                        chunk_dots_tok<2, CNT, NTOK, true>(wl, xl, kl, dl);
+                        float dl[2][NW];
+                        chunk_dots_tok<2, CNT, NW, true>(wl, xl, kl, dl);
                         const float s0 = wscale<true>(sv[d][0][p]), s1 = wscale<true>(sv[d][1][p]);
 #pragma unroll
                         for (int j = 0; j < CNT; ++j) {
@@ -1100,7 +1111,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
                         racc[V / 2 + j * M + m] = acc[1][j];
                     }
                 };
-                dispatch_count<NTOK>(cnt, stage);
+                dispatch_count<NW>(cntw, stage);
             }
             issue(d, g0 + m + DEPTH);
         }
@@ -1111,7 +1122,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
             const int vi = reduced_value<V>(jj, lane);
             const int j = vi / M, m = vi % M;
             const int i = sp.part + (g0 + m) * sp.wpe;
-            if (value_writer<V>(jj, lane) && vi < NTOK * M && j < cnt && g0 + m < nsteps)
+            if (value_writer<V>(jj, lane) && vi < NW * M && j < cntw && g0 + m < nsteps)
                 a.out[(size_t)orow[j] * a.out_ld + ht_pos(i, CI)] = swiglu(racc[jj], up);
         }
         if (g0 == 0) tl_mark<TL>(a.tl, a.tl_cap, 3);
@@ -1241,17 +1252,18 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
     a.tl_cap = mk ? mk->tl_cap : 0;
     {
         a.tl = mk ? mk->tl_next() : nullptr;
-        // one 4-wave workgroup per CU (eight waves measured slower: more
-        // concurrent streams lose DRAM locality); reductions over M = 2
-        // stages (M = 4 measured 6% slower: twice the code per token count
-        // and more live registers)
-        constexpr int M = 2, DEPTH = 2, WPB = 4;
+        // one workgroup per CU: four streams (eight streaming waves measured
+        // slower: more concurrent streams lose DRAM locality), each run by
+        // a wave pair that splits the tokens; reductions over M = 2 stages
+        // (M = 4 measured 6% slower: twice the code per token count and
+        // more live registers)
+        constexpr int M = 2, DEPTH = 2, WPB = 8;
         a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
         a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
         a.in = io.x; a.in_by_slot = 0;
         a.out = h; a.out_ld = L.I;
         const int P = (L.H / 32 + 63) / 64;
-        const dim3 grid(std::max(cus, (entries + WPB - 1) / WPB)), block(WPB * 64);
+        const dim3 grid(std::max(cus, (entries + 3) / 4)), block(WPB * 64);
         const size_t lds = (size_t)io.T * (L.H + L.H / 32) * 4;
 #define COLI_GUM(P_) \
         if (P == P_) { \
