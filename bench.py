@@ -226,16 +226,19 @@ def stream_read_rate(hip, n_bufs=8, nbytes=188 << 20, reps=3):
 
 def issue_sharing():
     """Do the matrix core and the vector ALU of one SIMD issue in parallel?
-    coli_issue_probe's four modes on one workgroup per CU: MFMA only, FMA
-    only, one wave of each kind per SIMD, both in every wave (us per
-    workgroup, median over the workgroups)."""
+    coli_issue_probe's modes on one workgroup per CU: MFMA only, FMA only,
+    one wave of each kind per SIMD, both in every wave; and the vector
+    issue rate itself: the FMAs of one wave per SIMD instead of two, and
+    three-VGPR-source FMAs (us per workgroup, median over the workgroups;
+    ns per wave64 instruction per SIMD)."""
     import torch
     import int4_routed_expert_bias_amd as coli
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     ticks = torch.zeros((cus,), dtype=torch.int64, device="cuda")
     sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
     us = {}
-    for mode, name in enumerate(("mfma_only", "fma_only", "mfma_and_fma_waves", "mfma_and_fma_interleaved")):
+    for mode, name in enumerate(("mfma_only", "fma_only", "mfma_and_fma_waves", "mfma_and_fma_interleaved",
+                                 "fma_one_wave_per_simd", "fma_three_vgpr_sources")):
         for _ in range(2):
             coli.issue_probe(mode, ticks, sink)
         torch.cuda.synchronize()
@@ -246,6 +249,11 @@ def issue_sharing():
             "mixed_waves_vs_serial_sum": round(us["mfma_and_fma_waves"] / serial2, 3),
             "interleaved_vs_serial_sum": round(us["mfma_and_fma_interleaved"] /
                                                (us["mfma_only"] + us["fma_only"]), 3),
+            # 2048 iterations x 16 FMAs per wave; 2 waves per SIMD (1 in mode 4)
+            "ns_per_valu_instr_per_simd": {
+                "two_waves": round(us["fma_only"] * 1e3 / (2 * 2048 * 16), 3),
+                "one_wave": round(us["fma_one_wave_per_simd"] * 1e3 / (2048 * 16), 3),
+                "two_waves_three_vgpr_sources": round(us["fma_three_vgpr_sources"] * 1e3 / (2 * 2048 * 16), 3)},
             "kernel": "issue_probe_kernel (coli_issue_probe)"}
 
 

@@ -374,7 +374,9 @@ int coli_stream_read(const void *buf, size_t bytes, uint32_t *out, int32_t n_gro
  * run 2048 iterations of: mode 0, 4 independent v_mfma_i32_16x16x64_i8 per
  * wave; mode 1, 16 independent fp32 FMAs per wave; mode 2, waves 0-3 the
  * MFMAs of mode 0 and waves 4-7 the FMAs of mode 1; mode 3, every wave both,
- * interleaved.  ticks[n_groups] (uint64) receives each workgroup's duration
+ * interleaved; mode 4, the FMAs of mode 1 in waves 0-3 only (one wave per
+ * SIMD); mode 5, 16 independent fp32 FMAs per wave whose three sources are
+ * distinct VGPRs (the VOP3 form).  ticks[n_groups] (uint64) receives each workgroup's duration
  * in wall-clock (100 MHz) ticks; sink (one int32) is written only to keep
  * the work.  COLI_E_ARG for a bad mode, count or pointer, COLI_E_ALIGN for a
  * misaligned one. */

@@ -970,6 +970,19 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int K = a.K, rb = K / 2, sbs = K / 64, C = K / 32, CI = a.I / 32;
     tl_mark<TL>(a.tl, a.tl_cap, 0);
+    // x of the batch: every load issued at once, before the selection (its
+    // latency overlaps the selection's); staged to LDS after it
+    constexpr int XPRE = (NTOK * (COLI_MAX_H_DEV / 4) + WPB * 64 - 1) / (WPB * 64);
+    uint4 xpre[XPRE];
+    {
+        const int nx = a.T * (K / 4);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.in, (uint32_t)nx * 16);
+#pragma unroll
+        for (int j = 0; j < XPRE; ++j) {
+            const int i = (int)threadIdx.x + WPB * 64 * j;
+            xpre[j] = load16(rx, i < nx ? (uint32_t)i * 16 : kOOB);
+        }
+    }
     int U;
     if constexpr (ROUTE) {
         __shared__ RouteLds rl;
@@ -1024,11 +1037,15 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
     float *ks = xs + a.T * K;
     const float4 *xt = reinterpret_cast<const float4 *>(xs);
     {
-        const float4 *src = reinterpret_cast<const float4 *>(a.in);
         float4 *dst = reinterpret_cast<float4 *>(xs);
-        for (int i = threadIdx.x; i < a.T * (K / 4); i += blockDim.x) {
-            const int t = i / (K / 4), r = i - t * (K / 4), c = r >> 3, q = r & 7;
-            dst[(8 * t + q) * C + c] = src[i];
+#pragma unroll
+        for (int j = 0; j < XPRE; ++j) {
+            const int i = (int)threadIdx.x + WPB * 64 * j;
+            if (i < a.T * (K / 4)) {
+                const int t = i / (K / 4), r = i - t * (K / 4), c = r >> 3, q = r & 7;
+                dst[(8 * t + q) * C + c] = make_float4(__uint_as_float(xpre[j].x), __uint_as_float(xpre[j].y),
+                                                       __uint_as_float(xpre[j].z), __uint_as_float(xpre[j].w));
+            }
         }
         __syncthreads();
         for (int tc = threadIdx.x; tc < a.T * C; tc += blockDim.x) {
@@ -1243,6 +1260,15 @@ __global__ __launch_bounds__(256) void down_mt_kernel(GemvArgs a)
     tl_mark<TL>(a.tl, a.tl_cap, 7);
 }
 
+// Workgroups of a kernel resident on one CU at once (at least 1).
+template <typename Kern>
+static int resident_per_cu(Kern kernel, int block)
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+}
+
 template <int NTOK>
 static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs a, float *h,
                                 float *o, hipStream_t st, Marks *mk, const RouteSelf *rt = nullptr)
@@ -1285,9 +1311,13 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         a.in = h; a.in_by_slot = 1;
         a.out = o; a.out_ld = L.H;
         const int P = (L.I / 32 + 63) / 64;
-        const dim3 grid(std::max(4 * cus, (entries + 3) / 4)), block(256);
+        // as many workgroups as the CUs hold at once (its registers allow
+        // two per CU at the benchmark's shape): a second round of
+        // workgroups would start only as the first ones finish
 #define COLI_DNM(P_) \
         if (P == P_) { \
+            static const int occ = resident_per_cu(down_mt_kernel<P_, RD, M, DEPTH, NTOK>, 256); \
+            const dim3 grid(std::max(occ * cus, (entries + 3) / 4)), block(256); \
             if (a.tl) launch(mk, (down_mt_kernel<P_, RD, M, DEPTH, NTOK, true>), grid, block, 0, st, a); \
             else launch(mk, (down_mt_kernel<P_, RD, M, DEPTH, NTOK>), grid, block, 0, st, a); \
         }

@@ -46,6 +46,11 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *__restr
 //   mode 2: waves 0-3 the MFMAs of mode 0, waves 4-7 the FMAs of mode 1
 //           (so each SIMD holds one wave of each kind),
 //   mode 3: every wave both, interleaved;
+//   mode 4: the FMAs of mode 1 in waves 0-3 only (one wave per SIMD: the
+//           rate of a single wave's VALU issue);
+//   mode 5: 16 independent three-source fp32 FMAs per wave, every source a
+//           distinct VGPR (v_fma_f32 in its VOP3 form, as in the int8 GEMM's
+//           epilogue; mode 1's compile to the two-source-plus-constant form);
 // ticks[b] = workgroup b's duration in wall-clock (100 MHz) ticks.  If the
 // two units issued in parallel, modes 2 and 3 would take about as long as
 // the longer of modes 0 and 1 (halved for mode 2); serialised, as long as
@@ -65,10 +70,22 @@ __global__ __launch_bounds__(512) void issue_probe_kernel(uint64_t *__restrict__
     for (int i = 0; i < 16; ++i) f[i] = (float)(lane + i) * 1e-3f;
     const float m = 1.0001f + seed * 1e-9f, ad = 1e-7f;
     const bool mfma = MODE == 0 || (MODE == 2 && wave < 4);
-    const bool valu = MODE == 1 || (MODE == 2 && wave >= 4);
+    const bool valu = MODE == 1 || (MODE == 2 && wave >= 4) || (MODE == 4 && wave < 4);
+    float g[16], h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        g[i] = (float)(lane - i) * 1e-3f;
+        h[i] = (float)(i + 1) * 1e-4f;
+    }
     __syncthreads();
     const uint64_t t0 = wall_clock64();
-    if (MODE == 3) {
+    if (MODE == 5) {
+        for (int it = 0; it < kIssueIters; ++it) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)  // f = g * h + f, all three in VGPRs, f not the destination
+                asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(g[i]) : "v"(g[i]), "v"(h[i]), "v"(f[i]));
+        }
+    } else if (MODE == 3) {
         for (int it = 0; it < kIssueIters; ++it) {
             c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c0, 0, 0, 0);
 #pragma unroll
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(512) void issue_probe_kernel(uint64_t *__restrict__
     const uint64_t t1 = wall_clock64();
     float fs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) fs += f[i];
+    for (int i = 0; i < 16; ++i) fs += f[i] + g[i];
     if (c0[0] + c1[1] + c2[2] + c3[3] == 0x7fffffff || fs == 12345.f) sink[0] = 1;  // keeps the work
     if (threadIdx.x == 0) ticks[blockIdx.x] = t1 - t0;
 }
@@ -112,7 +129,7 @@ extern "C" int coli_issue_probe(int32_t mode, int32_t n_groups, uint64_t *ticks,
                                 void *hip_stream)
 {
     if (!ticks || !sink || n_groups < 1 || n_groups > 65536) return COLI_E_ARG;
-    if (mode < 0 || mode > 3) return COLI_E_ARG;
+    if (mode < 0 || mode > 5) return COLI_E_ARG;
     if (((uintptr_t)ticks & 7u) || ((uintptr_t)sink & 3u)) return COLI_E_ALIGN;
     if (int st = coli_moe_device_check()) return st;
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -120,7 +137,9 @@ extern "C" int coli_issue_probe(int32_t mode, int32_t n_groups, uint64_t *ticks,
     case 0: hipLaunchKernelGGL(coli::issue_probe_kernel<0>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
     case 1: hipLaunchKernelGGL(coli::issue_probe_kernel<1>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
     case 2: hipLaunchKernelGGL(coli::issue_probe_kernel<2>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
-    default: hipLaunchKernelGGL(coli::issue_probe_kernel<3>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    case 3: hipLaunchKernelGGL(coli::issue_probe_kernel<3>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    case 4: hipLaunchKernelGGL(coli::issue_probe_kernel<4>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
+    default: hipLaunchKernelGGL(coli::issue_probe_kernel<5>, dim3(n_groups), dim3(512), 0, s, ticks, 1, sink); break;
     }
     return hipGetLastError() == hipSuccess ? COLI_OK : COLI_E_DEVICE;
 }

@@ -60,6 +60,17 @@ def test_workspace_bytes(L):
     assert coli.acc_dump_bytes(256, 128, 2, 4, 2) == 0
 
 
+def test_issue_probe_argument_errors(L):
+    """The measurement probe rejects modes outside 0..5, group counts
+    outside 1..65536 and null or misaligned pointers before any device
+    work."""
+    fake = ctypes.c_void_p(FAKE)
+    for mode, n in ((-1, 1), (6, 1), (0, 0), (5, 65537)):
+        assert L.coli_issue_probe(mode, n, fake, fake, None) == coli.COLI_E_ARG, (mode, n)
+    assert L.coli_issue_probe(0, 1, None, fake, None) == coli.COLI_E_ARG
+    assert L.coli_issue_probe(0, 1, ctypes.c_void_p(FAKE + 4), fake, None) == coli.COLI_E_ALIGN
+
+
 def test_i8_workspace_offsets(L):
     """The int8 family's intermediate regions lie inside the workspace, in
     order, without overlap; batches of up to 4 tokens have none."""
