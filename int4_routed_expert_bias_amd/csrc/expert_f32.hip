@@ -925,21 +925,37 @@ __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, i
     T1Split s{0, 0, 0, 0};
     const int ne = U + a.n_shared;
     if (ne <= 0 || GW < ne) return s;
-    const int total = rd_union<UL>(a.offsets, U) + a.n_shared * a.T + ne;
-    const long spare = GW - ne;
+    // one entry per lane (64 at a time): its cost, the exclusive prefix of
+    // the costs by a wave scan, its wave range; the wave's entry is the
+    // lane whose range holds gw (32-bit: spare * total stays far below 2^31)
+    const int lane = threadIdx.x & 63;
+    const uint32_t total = (uint32_t)(rd_union<UL>(a.offsets, U) + a.n_shared * a.T + ne);
+    const uint32_t spare = (uint32_t)(GW - ne);
     int before = 0;
-    for (int e = 0; e < ne; ++e) {
-        const int cnt = 1 + (e < U ? rd_union<UL>(a.offsets, e + 1) - rd_union<UL>(a.offsets, e) : a.T);
-        const int b0 = e + (int)(spare * before / total);
-        const int b1 = e + 1 + (int)(spare * (before + cnt) / total);
-        if (gw >= b0 && gw < b1) {
-            s.ue = e;
-            s.part = gw - b0;
-            s.wpe = b1 - b0;
+    for (int base = 0; base < ne; base += 64) {
+        const int e = base + lane;
+        int cnt = 0;
+        if (e < ne) cnt = 1 + (e < U ? a.offsets[e + 1] - a.offsets[e] : a.T);
+        int inc = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += o;
+        }
+        const uint32_t bef = (uint32_t)(before + inc - cnt);
+        const int b0 = e + (int)(spare * bef / total);
+        const int b1 = e + 1 + (int)(spare * (bef + (uint32_t)cnt) / total);
+        const uint64_t hit = __ballot(e < ne && gw >= b0 && gw < b1);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            const int b0l = __builtin_amdgcn_readlane(b0, l), b1l = __builtin_amdgcn_readlane(b1, l);
+            s.ue = base + l;
+            s.part = gw - b0l;
+            s.wpe = b1l - b0l;
             s.nsteps = s.part < nblocks ? (nblocks - s.part + s.wpe - 1) / s.wpe : 0;
             return s;
         }
-        before += cnt;
+        before += __builtin_amdgcn_readlane(inc, 63);
     }
     return s;
 }
