@@ -71,7 +71,10 @@ def test_tiny_workload(mode):
 
 @pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
 @pytest.mark.parametrize("shape", [(512, 256, 32, 4, 37), (256, 128, 16, 2, 1),
-                                   (320, 192, 10, 3, 67), (64, 64, 5, 5, 9)])
+                                   (320, 192, 10, 3, 67), (64, 64, 5, 5, 9),
+                                   # H / 64 = 6: the 64-row tiles' four-group K steps end
+                                   # on a step with two groups past K
+                                   (384, 256, 12, 3, 29)])
 def test_ragged_shapes(mode, shape):
     H, I, E, k, T = shape
     lay = make_layer(H, I, E, k, wid=50 + H % 97)
