@@ -918,7 +918,16 @@ __device__ __forceinline__ int rd_union(const int32_t *p, int i)
     return p[i];
 }
 
-template <bool UL = false>
+// Stage cost of an entry with tok tokens, in units of a quarter of a
+// single-token stage: one wave up to two tokens, a wave pair (tokens split
+// two and one or two and two) from three.  Measured on the 4-token verify
+// layer: 1.2, ~1.8, ~2.2 and 2.56 us per stage for 1-4 tokens.
+__device__ __forceinline__ int pair_stage_cost(int tok)
+{
+    return tok <= 1 ? 4 : tok == 2 ? 6 : tok == 3 ? 7 : 9;
+}
+
+template <bool UL = false, bool PAIRS = false>
 __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, int U,
                                             int nblocks)
 {
@@ -929,13 +938,22 @@ __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, i
     // the costs by a wave scan, its wave range; the wave's entry is the
     // lane whose range holds gw (32-bit: spare * total stays far below 2^31)
     const int lane = threadIdx.x & 63;
-    const uint32_t total = (uint32_t)(rd_union<UL>(a.offsets, U) + a.n_shared * a.T + ne);
     const uint32_t spare = (uint32_t)(GW - ne);
+    auto cost = [&](int e) {
+        const int tok = e < U ? a.offsets[e + 1] - a.offsets[e] : a.T;
+        return PAIRS ? pair_stage_cost(tok) : 1 + tok;
+    };
+    uint32_t total = 0;
+    for (int base = 0; base < ne; base += 64) {
+        int c = base + lane < ne ? cost(base + lane) : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+        total += (uint32_t)c;
+    }
     int before = 0;
     for (int base = 0; base < ne; base += 64) {
         const int e = base + lane;
-        int cnt = 0;
-        if (e < ne) cnt = 1 + (e < U ? a.offsets[e + 1] - a.offsets[e] : a.T);
+        const int cnt = e < ne ? cost(e) : 0;
         int inc = cnt;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -963,17 +981,19 @@ __device__ __forceinline__ T1Split mt_split(const GemvArgs &a, int gw, int GW, i
 // ROUTE: the tokens route themselves first (route_self, as the
 // single-token kernel), and the union is read from LDS.
 // WPB = 8: wave pairs.  Waves w and w + 4 of a workgroup (one SIMD) stream
-// the same row blocks of the same entry and split its tokens (w the even
-// ones, w + 4 the odd ones, NTOK / 2 each): the number of DRAM streams is
-// that of four waves, while two waves per SIMD share the VALU work (a
-// wave alone issues a VALU instruction only about every other slot); the
-// second wave's weight loads are served by the cache.
+// the same row blocks of the same entry; an entry of three or four tokens
+// splits them (w the even ones, w + 4 the odd ones), so the number of DRAM
+// streams is that of four waves while two waves per SIMD share the VALU
+// work (a wave alone issues a VALU instruction only about every other
+// slot; the second wave's weight loads mostly hit the cache).  Entries of
+// one or two tokens run on wave w alone (a pair was measured slower there:
+// 2.17 us a stage against ~1.8).
 template <int P, int M, int DEPTH, int NTOK, int WPB, bool ROUTE, bool TL = false>
 __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSelf r)
 {
     static_assert(M % DEPTH == 0, "stage ring must divide the reduction batch");
     // route_self: one token per wave of the first four (T <= 4)
-    static_assert(WPB == 4 || (WPB == 8 && NTOK % 2 == 0), "four waves, or four pairs");
+    static_assert(WPB == 4 || (WPB == 8 && NTOK == 4), "four waves, or four pairs of up to two tokens each");
     constexpr bool PAIRS = WPB == 8;
     constexpr int NW = PAIRS ? NTOK / 2 : NTOK;  // tokens per wave
     constexpr int V = next_pow2(2 * M * NW), N = reduced_count(V);
@@ -1013,7 +1033,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
     }
     tl_mark<TL>(a.tl, a.tl_cap, 1);
     const int hh = PAIRS ? (wave >> 2) : 0;  // wave pair half: its tokens hh, hh + 2, ...
-    const T1Split sp = mt_split<ROUTE>(a, blockIdx.x * 4 + (wave & 3), gridDim.x * 4, U, a.I);
+    const T1Split sp = mt_split<ROUTE, PAIRS>(a, blockIdx.x * 4 + (wave & 3), gridDim.x * 4, U, a.I);
     const int nsteps = sp.nsteps;
     const uint8_t *wb;
     const uint16_t *sb;
@@ -1073,8 +1093,10 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
         __syncthreads();
     }
     tl_mark<TL>(a.tl, a.tl_cap, 2);
-    // this wave's tokens: entry tokens hh + 2 j (pairs) or j
-    const int cntw = PAIRS ? (cnt - hh + 1) / 2 : cnt;
+    // this wave's tokens: entry tokens hh + 2 j (a pair splitting three or
+    // four) or j
+    const bool split = PAIRS && cnt > 2;
+    const int cntw = split ? (cnt - hh + 1) / 2 : hh == 0 ? cnt : 0;
     if (nsteps == 0 || cntw <= 0) {
         tl_mark<TL>(a.tl, a.tl_cap, 7);
         return;
@@ -1083,7 +1105,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
         int in_row = 0, out_row = 0;
-        if (j < cntw) token_rows(a, list, PAIRS ? hh + 2 * j : j, in_row, out_row);
+        if (j < cntw) token_rows(a, list, split ? hh + 2 * j : j, in_row, out_row);
         tok[j] = in_row;
         orow[j] = out_row;
     }
@@ -1102,7 +1124,7 @@ __global__ __launch_bounds__(WPB * 64) void gateup_mt_kernel(GemvArgs a, RouteSe
                     float acc[2][NW];
 #pragma unroll
                     for (int j = 0; j < CNT; ++j) acc[0][j] = acc[1][j] = 0.f;
-                    if constexpr (CNT == 1 && NW == 1) {
+                    if constexpr (CNT == 1 && !PAIRS) {
                         // one token: all P chunks at once, 2 * P interleaved chains
                         float xl[P][32], kl[P], dots[2][P];
 #pragma unroll
@@ -1299,7 +1321,7 @@ static hipError_t launch_f32_mt(const LayerDev &L, const ForwardIO &io, GemvArgs
         // a wave pair that splits the tokens; reductions over M = 2 stages
         // (M = 4 measured 6% slower: twice the code per token count and
         // more live registers)
-        constexpr int M = 2, DEPTH = 2, WPB = 8;
+        constexpr int M = 2, DEPTH = 2, WPB = NTOK == 4 ? 8 : 4;
         a.w = L.w13; a.s = L.s13; a.sh_w = L.sh_w13; a.sh_s = L.sh_s13;
         a.N = 2 * L.I; a.K = L.H; a.upe = L.I;
         a.in = io.x; a.in_by_slot = 0;
