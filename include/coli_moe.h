@@ -31,7 +31,11 @@
  *    calls (coli_moe_route_forward_noalloc's static scratch array aside) and
  *    never synchronises.  Work is enqueued on `hip_stream` (a
  *    hipStream_t; NULL = the null stream) and buffers must stay valid until
- *    the caller synchronises that stream.  The layer descriptor itself is
+ *    the caller synchronises that stream.  (The int8 grouped GEMM of 5 to
+ *    1,024 tokens also runs on two side streams of the library, created once
+ *    per device with the default priority; they wait for the caller's
+ *    stream and the caller's stream waits for them, so ordering is that of
+ *    one stream, under HIP graph capture as well.)  The layer descriptor itself is
  *    host memory and may be reused or freed when the call returns.
  *  - Layouts are row-major.  int4 codes are two's complement in [-8, 7];
  *    byte b of a packed row holds element 2b in its low nibble and element

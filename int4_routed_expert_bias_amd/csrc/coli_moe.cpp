@@ -1,7 +1,9 @@
 // coli_moe.cpp -- host entry points of libcoli_moe.so (C ABI declared in
 // include/coli_moe.h).  Every argument, shape and alignment check runs on
 // the host before the first HIP call; kernels are enqueued on the caller's
-// stream; nothing is allocated, freed or synchronised here.
+// stream (the grouped GEMM of up to 1,024 tokens also on two side streams
+// forked from it and joined back, created once per device); nothing is
+// allocated, freed or synchronised here.
 #include "../../include/coli_moe.h"
 
 #include <hip/hip_runtime.h>
@@ -9,6 +11,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 
@@ -82,6 +85,59 @@ int coli::device_cu_count()
         g_dev_cus[dev].store(n, std::memory_order_relaxed);
     }
     return n;
+}
+
+namespace {
+
+struct SideSlot {
+    std::once_flag once;
+    std::mutex mu;
+    bool ok = false;
+    SideSet set{};
+};
+SideSlot g_side[64];
+
+void side_create(SideSlot &sl)
+{
+    SideSet &q = sl.set;
+    bool ok = hipEventCreateWithFlags(&q.fork, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; i < 2 && ok; ++i)
+        ok = hipStreamCreateWithFlags(&q.s[i], hipStreamNonBlocking) == hipSuccess &&
+             hipEventCreateWithFlags(&q.join[i], hipEventDisableTiming) == hipSuccess;
+    sl.ok = ok;
+}
+
+}  // namespace
+
+SideSet *coli::side_fork(hipStream_t st, int n)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || n < 1 || n > 2) return nullptr;
+    SideSlot &sl = g_side[dev];
+    std::call_once(sl.once, side_create, std::ref(sl));
+    if (!sl.ok) return nullptr;
+    sl.mu.lock();
+    SideSet *q = &sl.set;
+    bool ok = hipEventRecord(q->fork, st) == hipSuccess;
+    for (int i = 0; i < n && ok; ++i) ok = hipStreamWaitEvent(q->s[i], q->fork, 0) == hipSuccess;
+    if (!ok) {
+        sl.mu.unlock();
+        return nullptr;
+    }
+    return q;
+}
+
+hipError_t coli::side_join(SideSet *q, hipStream_t st, int n)
+{
+    hipError_t err = hipSuccess;
+    for (int i = 0; i < n; ++i) {
+        if (err == hipSuccess) err = hipEventRecord(q->join[i], q->s[i]);
+        if (err == hipSuccess) err = hipStreamWaitEvent(st, q->join[i], 0);
+    }
+    // the lock of the device whose set this is
+    for (auto &sl : g_side)
+        if (&sl.set == q) sl.mu.unlock();
+    return err;
 }
 
 namespace {

@@ -318,6 +318,21 @@ int route_forward_scratch(const coli_moe_layer *L, const float *x, int32_t T, fl
                           int32_t *topk_ids, float *topk_w, int32_t *union_ids, int32_t *offsets,
                           int32_t *slots, int32_t *n_union, int32_t act_mode, float *y,
                           void *hip_stream, ScratchFn scratch);
+// Side streams of one device for launches of a call that may run
+// concurrently with the caller's stream (created once per device with the
+// default priority, non-blocking, kept until the process ends).  Between
+// side_fork and side_join the enqueueing thread holds the device's lock, so
+// concurrent calls on one device cannot interleave their fork and join
+// events.  side_fork makes side streams 0..n-1 wait for everything enqueued
+// on st so far and returns them (null: none available -- the caller then
+// enqueues on st); side_join makes st wait for everything enqueued on them
+// since, and releases the lock.
+struct SideSet {
+    hipStream_t s[2];
+    hipEvent_t fork, join[2];
+};
+SideSet *side_fork(hipStream_t st, int n);
+hipError_t side_join(SideSet *ss, hipStream_t st, int n);
 hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, int32_t T, int32_t k,
                           int32_t H, int32_t n_shared, float *y, hipStream_t st,
                           Marks *mk = nullptr);

@@ -205,6 +205,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
 // work as in a full 128-row tile, and the workgroup has twice the bytes in
 // flight, in half the steps).
 constexpr int kGBN = 128;  // weight rows per tile
+constexpr int kSideTMax = 1024;  // tile lists on side streams up to this many tokens
 constexpr int kSmallBM = 64, kSmallKG = 4;
 static_assert(kTileM == 128, "the schedule's tiles are 128 rows");
 
@@ -792,12 +793,22 @@ hipError_t launch_forward_i8(const LayerDev &L, const ForwardIO &io, hipStream_t
     // shared; last tiles: one per entry)
     const unsigned y_full = (unsigned)std::max<int64_t>(1, (T * L.k) / kTileM + L.n_shared * (T / kTileM));
     const unsigned y_part = (unsigned)(lay.cap + L.n_shared);
+    // Up to kSideTMax tokens the three tile lists run concurrently: the
+    // partial- and small-tile launches on two side streams forked from st
+    // and joined back before the next launch, so the lists' launches overlap
+    // their fill and tail (each list is a few rounds of workgroups there).
+    // At 4,096 tokens the full-tile list alone is 18 rounds and the overlap
+    // gains nothing (measured); the lists then run in order on st.
+    const int nside = T <= kSideTMax ? 2 : 0;
 #define COLI_GG_LISTS(GU_, DU_, GX_)                                                            \
     {                                                                                          \
+        SideSet *ss = nside ? side_fork(st, nside) : nullptr;                                  \
+        hipStream_t s_part = ss ? ss->s[0] : st, s_small = ss ? ss->s[nside - 1] : st;          \
         launch(mk, (ggemm_kernel<GU_, DU_, kFullTiles>), dim3(GX_, y_full), dim3(256), 0, st, a); \
-        launch(mk, (ggemm_kernel<GU_, DU_, kPartialTiles>), dim3(GX_, y_part), dim3(256), 0, st, a); \
+        launch(mk, (ggemm_kernel<GU_, DU_, kPartialTiles>), dim3(GX_, y_part), dim3(256), 0, s_part, a); \
         launch(mk, (ggemm_kernel<GU_, DU_, kSmallTiles, kSmallBM, kSmallKG>), dim3(GX_, y_part),  \
-               dim3(256), 0, st, a);                                                           \
+               dim3(256), 0, s_small, a);                                                      \
+        if (ss && (err = side_join(ss, st, nside)) != hipSuccess) return err;                  \
     }
 #define COLI_GG(GU_, GX_)                                                                      \
     {                                                                                          \
