@@ -383,6 +383,37 @@ def test_union_sizes(T, k, E):
     assert np.array_equal(sl.cpu().numpy(), rsl)
 
 
+@pytest.mark.parametrize("T,k,E,drop", [(2049, 1, 256, 0.0), (4096, 8, 256, 0.1), (4096, 8, 256, 1.0),
+                                         (65536, 16, 64, 0.05), (700, 16, 1024, 0.0)])
+def test_union_multi_workgroup(T, k, E, drop):
+    """Batches of more than 2,048 slots: the union split over several
+    workgroups (one chunk of slots each) must equal the oracle's exactly,
+    also with dropped slots (id -1, as top-p leaves them), with every slot
+    dropped, and at the largest slot count (65,536 tokens x 16)."""
+    import torch
+    rng = np.random.default_rng(T + 7 * k + E)
+    # k distinct experts per token, Zipf-like popularity (Gumbel top-k)
+    logp = -1.1 * np.log(np.arange(1, E + 1, dtype=np.float64))
+    keys = logp[None, :] + rng.gumbel(size=(T, E))
+    ids = np.argpartition(-keys, k - 1, axis=1)[:, :k].astype(np.int32)
+    ids[rng.random((T, k)) < drop] = -1
+    cap = min(E, T * k)
+    d_ids = torch.from_numpy(ids).cuda()
+    u = torch.empty(cap, dtype=torch.int32, device="cuda")
+    off = torch.empty(cap + 1, dtype=torch.int32, device="cuda")
+    sl = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    nu = torch.empty(4, dtype=torch.int32, device="cuda")
+    coli.union(d_ids, T, k, E, u, off, sl, nu)
+    torch.cuda.synchronize()
+    ru, roff, rsl, rnu = orc().union(ids, E)
+    kept = int(roff[-1])
+    assert int(nu[0]) == rnu
+    assert np.array_equal(u.cpu().numpy(), ru)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    # slots past the kept ones are not written by either side
+    assert np.array_equal(sl.cpu().numpy()[:kept], rsl[:kept])
+
+
 @pytest.mark.parametrize("mode", [coli.ACT_F32, coli.ACT_I8])
 def test_determinism_and_batch_invariance(mode):
     lay = make_layer(512, 256, 16, 4, wid=63)
