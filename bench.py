@@ -449,11 +449,16 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
 
     def step(s):
         if stacked:
+            # pre-norm of layer 0; between layers the residual add and the
+            # next pre-norm in one pass (coli_add_rmsnorm)
             resid.copy_(xs[0])
-            for lay in devl:
-                coli.rmsnorm(resid, xhat, T, H, 1e-6)
+            coli.rmsnorm(resid, xhat, T, H, 1e-6)
+            for li, lay in enumerate(devl):
                 coli.run_layer(lay, xhat, bufs, top_p=topp)
-                coli.add_inplace(resid, bufs.y, T * H)
+                if li + 1 < len(devl):
+                    coli.add_rmsnorm(resid, bufs.y, xhat, T, H, 1e-6)
+                else:
+                    coli.add_inplace(resid, bufs.y, T * H)
         else:
             coli.run_layer(devl[s % NL], xs[s], bufs, top_p=topp,
                            fused="step" if one_call else True)
@@ -553,10 +558,10 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
             lays = devl
         else:
             lays = [devl[(W + s) % NL]]
-        for lay in lays:
+        if stacked:
+            coli.rmsnorm(resid, xhat, T, H, 1e-6)
+        for li, lay in enumerate(lays):
             x_in = xs[(W + s) % len(xs)] if not stacked else xhat
-            if stacked:
-                coli.rmsnorm(resid, xhat, T, H, 1e-6)
             if one_call:
                 coli.route_forward_profiled(lay, x_in, T, bufs.ids, bufs.w, bufs.union_ids,
                                             bufs.offsets, bufs.slots, bufs.n_union, mode, bufs.y,
@@ -570,7 +575,9 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
             union_sizes.append(bufs.n_union[:1].clone())
             if w.bias_kind == "zipf":
                 union_offsets.append(bufs.offsets.clone())
-            if stacked:
+            if stacked and li + 1 < len(lays):
+                coli.add_rmsnorm(resid, bufs.y, xhat, T, H, 1e-6)
+            elif stacked:
                 coli.add_inplace(resid, bufs.y, T * H)
             i += 1
     torch.cuda.synchronize()

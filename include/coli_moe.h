@@ -399,6 +399,14 @@ int coli_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
 /* x[i] += y[i] for i < n (fp32). */
 int coli_add_inplace(float *x, const float *y, int64_t n, void *hip_stream);
 
+/* Both of the above in one pass, as they meet between stacked layers:
+ * x[t][h] += y[t][h], then xhat = rmsnorm(x) of the updated x; x and xhat
+ * are bitwise those of coli_add_inplace(x, y, T*H) followed by
+ * coli_rmsnorm(x, xhat, T, H, eps).  x, y, xhat [T][H] fp32, distinct
+ * buffers; same limits and errors as coli_rmsnorm. */
+int coli_add_rmsnorm(float *x, const float *y, float *xhat, int32_t T, int32_t H, float eps,
+                     void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

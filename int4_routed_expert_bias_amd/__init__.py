@@ -29,7 +29,7 @@ EXPORTS = ("coli_moe_abi_version", "coli_moe_workspace_bytes", "coli_moe_route",
            "coli_moe_forward_kernel_count", "coli_moe_forward_kernel_name",
            "coli_moe_acc_dump_bytes", "coli_moe_i8_workspace_offsets", "coli_moe_strerror",
            "coli_moe_device_check",
-           "coli_rmsnorm", "coli_add_inplace", "coli_stream_read", "coli_issue_probe")
+           "coli_rmsnorm", "coli_add_inplace", "coli_add_rmsnorm", "coli_stream_read", "coli_issue_probe")
 # every symbol declared in include/coli_mla.h
 MLA_EXPORTS = ("coli_mla_workspace_bytes", "coli_mla_decode", "coli_mla_decode_profiled")
 # every symbol declared in include/coli_place.h
@@ -95,6 +95,7 @@ def lib():
             "coli_moe_device_check": ([], ctypes.c_int),
             "coli_rmsnorm": ([vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
             "coli_add_inplace": ([vp, vp, i64, vp], ctypes.c_int),
+            "coli_add_rmsnorm": ([vp, vp, vp, i32, i32, ctypes.c_float, vp], ctypes.c_int),
             "coli_stream_read": ([vp, sz, vp, i32, vp], ctypes.c_int),
             "coli_issue_probe": ([i32, i32, vp, vp, vp], ctypes.c_int),
             "coli_moe_placer_create": ([i32, i32, i32, i32, i32, i32, i32, vp], ctypes.c_int),
@@ -290,6 +291,12 @@ def rmsnorm(x, xhat, T, H, eps=1e-6, stream=None):
 
 def add_inplace(x, y, n, stream=None):
     _check(lib().coli_add_inplace(_ptr(x), _ptr(y), n, _stream(stream)), "coli_add_inplace")
+
+
+def add_rmsnorm(x, y, xhat, T, H, eps=1e-6, stream=None):
+    """x += y, then xhat = rmsnorm(x), in one pass (coli_add_rmsnorm)."""
+    _check(lib().coli_add_rmsnorm(_ptr(x), _ptr(y), _ptr(xhat), T, H, eps, _stream(stream)),
+           "coli_add_rmsnorm")
 
 
 def stream_read(buf, out, n_groups, nbytes=None, stream=None):

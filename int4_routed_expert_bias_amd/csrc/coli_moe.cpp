@@ -536,4 +536,16 @@ int coli_add_inplace(float *x, const float *y, int64_t n, void *hip_stream)
     return status_of(launch_add(x, y, n, static_cast<hipStream_t>(hip_stream)));
 }
 
+int coli_add_rmsnorm(float *x, const float *y, float *xhat, int32_t T, int32_t H, float eps,
+                     void *hip_stream)
+{
+    if (T < 0 || T > COLI_MAX_T || H < 64 || H > COLI_MAX_H || H % 64) return COLI_E_SHAPE;
+    if (!(eps >= 0.0f)) return COLI_E_ARG;
+    if (T == 0) return COLI_OK;
+    if (!x || !y || !xhat) return COLI_E_ARG;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(xhat)) return COLI_E_ALIGN;
+    if (int st = device_check()) return st;
+    return status_of(launch_add_rmsnorm(x, y, xhat, T, H, eps, static_cast<hipStream_t>(hip_stream)));
+}
+
 }  // extern "C"

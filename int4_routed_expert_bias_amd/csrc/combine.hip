@@ -62,6 +62,55 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
         xhat[(size_t)blockIdx.x * H + i] = (float)((double)r[i] * inv);
 }
 
+// x += y, then xhat = rmsnorm(x), one row per workgroup: every element of
+// the sum is formed once (fp32 add), written back and kept in registers for
+// the norm, whose sum of squares runs over the same elements in the same
+// order as rmsnorm_kernel's -- so x and xhat are bitwise those of add_kernel
+// followed by rmsnorm_kernel, with one pass over x fewer.
+constexpr int kNormPer = COLI_MAX_H_DEV / 256;  // elements per thread, at most
+
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(float *__restrict__ x,
+                                                          const float *__restrict__ y,
+                                                          float *__restrict__ xhat, int H, float eps)
+{
+    __shared__ double part[4];
+    float *r = x + (size_t)blockIdx.x * H;
+    const float *d = y + (size_t)blockIdx.x * H;
+    float v[kNormPer];
+#pragma unroll
+    for (int c = 0; c < kNormPer; ++c) {
+        const int i = threadIdx.x + 256 * c;
+        v[c] = i < H ? r[i] + d[i] : 0.f;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < kNormPer; ++c) {
+        const int i = threadIdx.x + 256 * c;
+        if (i < H) {
+            r[i] = v[c];
+            ss = fma((double)v[c], (double)v[c], ss);
+        }
+    }
+    ss = wave_sum_f64(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const double tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const double inv = 1.0 / sqrt(tot / (double)H + (double)eps);
+#pragma unroll
+    for (int c = 0; c < kNormPer; ++c) {
+        const int i = threadIdx.x + 256 * c;
+        if (i < H) xhat[(size_t)blockIdx.x * H + i] = (float)((double)v[c] * inv);
+    }
+}
+
+hipError_t launch_add_rmsnorm(float *x, const float *y, float *xhat, int32_t T, int32_t H,
+                              float eps, hipStream_t st)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(T), dim3(256), 0, st, x, y, xhat, H, eps);
+    return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
                           hipStream_t st)
 {

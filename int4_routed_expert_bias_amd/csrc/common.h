@@ -339,5 +339,7 @@ hipError_t launch_combine(const float *o, const int32_t *ids, const float *w, in
 hipError_t launch_rmsnorm(const float *x, float *xhat, int32_t T, int32_t H, float eps,
                           hipStream_t st);
 hipError_t launch_add(float *x, const float *y, int64_t n, hipStream_t st);
+hipError_t launch_add_rmsnorm(float *x, const float *y, float *xhat, int32_t T, int32_t H,
+                              float eps, hipStream_t st);
 
 }  // namespace coli

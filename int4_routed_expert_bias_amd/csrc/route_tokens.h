@@ -76,8 +76,9 @@ struct UnionOut {
     int cap;
 };
 
-// Tokens t0 .. t0 + 3 (one per wave; waves past T only take part in the
-// barriers, so every wave of the 256-thread workgroup must call this).
+// Tokens t0 .. t0 + 3 (one per wave of the first four; later waves, and
+// waves past T, only take part in the barriers, so every wave of the
+// workgroup must call this).
 // ids / w are indexed by token (t * k + rank); with UNION the workgroup's
 // tokens (T <= 4, t0 = 0) also form the batch union into uo.
 // TL: timeline marks 4 (keys loaded), 5 (selection found), 6 (selection
@@ -231,7 +232,7 @@ struct RouteLds {
 };
 
 // The tokens (r.T <= 4, one per wave) select their top k and form their
-// union into l (every thread of the 256-thread workgroup calls this);
+// union into l (every thread of the workgroup calls this: 4 or 8 waves);
 // workgroup 0 also writes the global contents the top-k kernel leaves
 // (slots past the kept ones untouched).
 template <bool TL = false>

@@ -181,6 +181,11 @@ def test_glue_argument_errors(L):
     assert L.coli_rmsnorm(MIS, FAKE, 4, 128, ctypes.c_float(1e-6), None) == coli.COLI_E_ALIGN
     assert L.coli_add_inplace(FAKE, None, 8, None) == coli.COLI_E_ARG
     assert L.coli_add_inplace(FAKE, FAKE, -1, None) == coli.COLI_E_ARG
+    assert L.coli_add_rmsnorm(FAKE, FAKE, FAKE, 4, 100, ctypes.c_float(1e-6), None) == coli.COLI_E_SHAPE
+    assert L.coli_add_rmsnorm(FAKE, FAKE, FAKE, 4, 128, ctypes.c_float(-1.0), None) == coli.COLI_E_ARG
+    assert L.coli_add_rmsnorm(FAKE, None, FAKE, 4, 128, ctypes.c_float(1e-6), None) == coli.COLI_E_ARG
+    assert L.coli_add_rmsnorm(FAKE, MIS, FAKE, 4, 128, ctypes.c_float(1e-6), None) == coli.COLI_E_ALIGN
+    assert L.coli_add_rmsnorm(FAKE, FAKE, FAKE, 0, 128, ctypes.c_float(1e-6), None) == coli.COLI_OK
 
 
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path of a GPU-less host")

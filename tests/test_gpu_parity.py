@@ -511,6 +511,30 @@ def test_rmsnorm_and_add():
     assert np.array_equal(xd.cpu().numpy(), x + np.float32(1.0))
 
 
+@pytest.mark.parametrize("T,H", [(33, 640), (3, 8192), (5, 64)])
+def test_add_rmsnorm_fused(T, H):
+    """The fused residual add + pre-norm equals the two calls bitwise, and
+    its xhat is within one ulp of the oracle's norm of the updated x."""
+    import torch
+    rng = np.random.default_rng(T + H)
+    x = (rng.standard_normal((T, H)) * 7).astype(np.float32)
+    y = (rng.standard_normal((T, H)) * 3).astype(np.float32)
+    a = torch.from_numpy(x).cuda()
+    b = a.clone()
+    yd = torch.from_numpy(y).cuda()
+    xa, xb = torch.empty_like(a), torch.empty_like(a)
+    coli.add_inplace(a, yd, T * H)
+    coli.rmsnorm(a, xa, T, H, 1e-6)
+    coli.add_rmsnorm(b, yd, xb, T, H, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.int32), b.cpu().numpy().view(np.int32))
+    assert np.array_equal(xa.cpu().numpy().view(np.int32), xb.cpu().numpy().view(np.int32))
+    assert np.array_equal(b.cpu().numpy(), x + y)
+    ref = orc().rmsnorm(x + y)
+    d = np.abs(xb.cpu().numpy().view(np.int32).astype(np.int64) - ref.view(np.int32))
+    assert d.max() <= 1
+
+
 @pytest.mark.parametrize("E,k,T", [(64, 8, 3), (65, 1, 5), (256, 8, 33), (256, 16, 9),
                                    (1000, 7, 11), (1024, 16, 70), (2, 2, 4)])
 def test_route_expert_counts(E, k, T):
