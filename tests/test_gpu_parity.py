@@ -383,10 +383,11 @@ def test_union_sizes(T, k, E):
     assert np.array_equal(sl.cpu().numpy(), rsl)
 
 
-@pytest.mark.parametrize("T,k,E,drop", [(2049, 1, 256, 0.0), (4096, 8, 256, 0.1), (4096, 8, 256, 1.0),
+@pytest.mark.parametrize("T,k,E,drop", [(2049, 1, 256, 0.0), (8192, 1, 256, 0.0), (8193, 1, 256, 0.0),
+                                         (4096, 8, 256, 0.1), (4096, 8, 256, 1.0),
                                          (65536, 16, 64, 0.05), (700, 16, 1024, 0.0)])
 def test_union_multi_workgroup(T, k, E, drop):
-    """Batches of more than 2,048 slots: the union split over several
+    """Batches of more than 8,192 slots: the union split over several
     workgroups (one chunk of slots each) must equal the oracle's exactly,
     also with dropped slots (id -1, as top-p leaves them), with every slot
     dropped, and at the largest slot count (65,536 tokens x 16)."""
