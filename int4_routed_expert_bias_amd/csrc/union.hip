@@ -284,7 +284,7 @@ hipError_t launch_union(const int32_t *ids, int32_t T, int32_t k, int32_t E, int
     }
     // more than kUnionMultiMin slots: one workgroup per chunk of kUnionChunk
     // slots (at most kUnionBlocks, the chunks growing beyond that).  Below,
-    // the single workgroup is as fast (4,096 slots: 17.1 us against 18.7
+    // the single workgroup is as fast (4,096 slots: 17-18 us against 18.7
     // with two chunks; 32,768: 62.4 against 27.2)
     if (n > kUnionMultiMin) {
         const int B = std::min(kUnionBlocks, (n + kUnionChunk - 1) / kUnionChunk);
