@@ -587,9 +587,9 @@ def bench_resident(name, K, W, *, act_mode=None, topp=None, layers=None, use_gra
         for j in range(nk):
             per_kernel[j] += hip.elapsed_ms(e[2 * j], e[2 * j + 1])
         if len(doms) > 1:
-            # times from the end of the launch before them (or the first
-            # one's start), earliest start to latest end
-            ref = e[2 * doms[0] - 1] if doms[0] > 0 else e[2 * doms[0]]
+            # times from the start of the call's first launch, earliest
+            # start to latest end
+            ref = e[0]
             span_ms += (max(hip.elapsed_ms(ref, e[2 * j + 1]) for j in doms)
                         - min(hip.elapsed_ms(ref, e[2 * j]) for j in doms))
         for x_ in e:
